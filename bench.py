@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the deformable sampling core on one MI355X.
+
+Headline: DCN core forward effective GB/s (input + offset + mask + output
+bytes per launch / launch time), as a fraction of the 8 TB/s HBM3E peak, and
+Gsamples/s, on the FlashInternImage-T stage-1 shape (DCNv4, fp16 with fp32
+accumulation, N=64, 56x56, C=64, G=4, K=3).  One step = one forward launch
+over the whole batch.  Beside it, in the same JSON line: the bf16 sweep over
+the four FlashInternImage-T stage shapes, the DCNv3 large-channel stage at
+stride 1 and 2, the fp32 forward + backward, and the CPU oracle timed on the
+host cores.
+
+Inputs are seeded synthetic tensors (no dataset, no weights).  Timing uses
+R rotating copies of every tensor (R * bytes > 512 MB, twice the 256 MB
+Infinity Cache) so each launch reads its inputs from HBM, and the K timed
+launches are captured in one HIP graph replayed between two events on the
+stream the kernels run on, so host launch overhead does not pad the small
+kernels.  Eager-launch timing is reported too.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import deformable_convolution_core_amd as dcn  # noqa: E402
+from deformable_convolution_core_amd import inputs  # noqa: E402
+
+METRIC = "DCN core fwd effective GB/s (% HBM roofline) + Gsamples/s, FlashInternImage-T"
+HBM_PEAK_GBPS = 8000.0
+ROTATE_BYTES = 600e6
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "deformable_convolution_core_amd", "csrc", f)
+                  for f in ("dcn_kernels.hpp", "dcn_core.hip")]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cfg(w):
+    return dict(kernel_size=w.K, stride=w.stride, pad=w.pad, dilation=w.dilation,
+                offset_scale=w.offset_scale, softmax=w.softmax, group=w.G)
+
+
+def rotating_sets(w, backward=False):
+    """R device copies of the workload's tensors (+ outputs)."""
+    per = w.min_bytes_backward() if backward else w.min_bytes_forward()
+    R = max(2, math.ceil(ROTATE_BYTES / per))
+    host = inputs.make(w, with_grad=backward)
+    sets = []
+    for _ in range(R):
+        d = {k: v.to("cuda") for k, v in host.items()}
+        if backward:
+            d["gi"] = torch.empty_like(d["input"])
+            d["goff"] = torch.empty_like(d["offset"])
+            d["gm"] = torch.empty_like(d["mask"])
+        else:
+            d["out"] = torch.empty(w.shapes()["output"], dtype=d["input"].dtype, device="cuda")
+        sets.append(d)
+    return sets
+
+
+def launcher(w, backward=False):
+    lib = dcn.load_library()
+    c = cfg(w)
+    dt = {"f32": 0, "f16": 1, "bf16": 2}[w.dtype]
+    import ctypes
+    vp = ctypes.c_void_p
+
+    def fwd(d, stream):
+        rc = lib.dcn_core_forward(vp(d["input"].data_ptr()), vp(d["offset"].data_ptr()),
+                                  vp(d["mask"].data_ptr()), vp(d["out"].data_ptr()),
+                                  w.N, w.H, w.W, w.G, w.Cg, w.K, w.stride, w.pad, w.dilation,
+                                  float(w.offset_scale), int(w.softmax), dt, vp(stream))
+        if rc:
+            raise dcn.DCNError(rc, lib.dcn_status_string(rc).decode())
+
+    def bwd(d, stream):
+        rc = lib.dcn_core_backward(vp(d["input"].data_ptr()), vp(d["offset"].data_ptr()),
+                                   vp(d["mask"].data_ptr()), vp(d["grad_out"].data_ptr()),
+                                   vp(d["gi"].data_ptr()), vp(d["goff"].data_ptr()),
+                                   vp(d["gm"].data_ptr()),
+                                   w.N, w.H, w.W, w.G, w.Cg, w.K, w.stride, w.pad, w.dilation,
+                                   float(w.offset_scale), int(w.softmax), dt, vp(stream))
+        if rc:
+            raise dcn.DCNError(rc, lib.dcn_status_string(rc).decode())
+
+    return bwd if backward else fwd
+
+
+def time_launches(w, steps, warmup, backward=False):
+    """Mean per-launch time (ms) of `steps` launches over rotating buffers:
+    graph-replayed (primary) and eager."""
+    sets = rotating_sets(w, backward)
+    R = len(sets)
+    launch = launcher(w, backward)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        h = stream.cuda_stream
+        for i in range(warmup):
+            launch(sets[i % R], h)
+        torch.cuda.synchronize()
+        # eager
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            launch(sets[i % R], h)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager_ms = e0.elapsed_time(e1) / steps
+    # graph of exactly `steps` launches
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(steps):
+            launch(sets[i % R], h)
+    torch.cuda.synchronize()
+    g.replay()                      # warm replay
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / steps
+    del g, sets
+    torch.cuda.empty_cache()
+    return graph_ms, eager_ms, R
+
+
+def forward_record(w, steps, warmup):
+    ms, eager_ms, R = time_launches(w, steps, warmup)
+    gbps = w.min_bytes_forward() / (ms * 1e-3) / 1e9
+    return dict(workload=w.name, dtype=w.dtype, softmax=bool(w.softmax),
+                shape=dict(N=w.N, H=w.H, W=w.W, C=w.C, G=w.G, Cg=w.Cg, K=w.K, stride=w.stride,
+                           Ho=w.Ho, Wo=w.Wo),
+                us=round(ms * 1e3, 3), eager_us=round(eager_ms * 1e3, 3),
+                min_bytes=w.min_bytes_forward(), GBps=round(gbps, 1),
+                frac_hbm=round(gbps / HBM_PEAK_GBPS, 4),
+                Gsamples_s=round(w.samples() / (ms * 1e-3) / 1e9, 3), rotating_sets=R)
+
+
+def cpu_baseline(w):
+    """The oracle as it stands, on the host cores, over whole batches of the
+    headline workload, repeated until at least ~3 s of wall time."""
+    import oracle   # test infrastructure, used here only for this timing leg
+    t = inputs.make(w, with_grad=False)
+    x, o, m = (inputs.to_f64(t[k]) for k in ("input", "offset", "mask"))
+    kw = dict(K=w.K, stride=w.stride, pad=w.pad, dilation=w.dilation, offset_scale=w.offset_scale,
+              softmax=w.softmax, group=w.G, with_absum=False)
+    oracle.forward(x, o, m, **kw)           # warm (page-in, thread start)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(x, o, m, **kw)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= 3.0 or reps >= 200:
+            break
+    per = el / reps
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    return dict(value=round(w.min_bytes_forward() / per / 1e9, 3), unit="GB/s", cores=cores,
+                kind="oracle",
+                sample=f"{reps} full batches of {w.name} (N={w.N}), binary64 C loops with OpenMP, "
+                       f"{per * 1e3:.1f} ms per batch")
+
+
+def traffic_record(name, min_bytes):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counters, if they were taken on the current kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except ValueError:
+        return None
+    if d.get("kernel_hash") != kernel_hash():
+        return None
+    e = d.get("workloads", {}).get(name)
+    return None if e is None else e.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=inputs.HEADLINE, choices=list(inputs.WORKLOADS))
+    ap.add_argument("--quick", action="store_true", help="headline only (no sweep, no CPU leg)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the sampling core needs no communication and this "
+              "build runs on a single MI355X; rerun with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dcn.load_library()
+    torch.cuda.set_device(0)
+
+    w = inputs.WORKLOADS[args.workload]
+    log(f"headline {w.name}: steps={args.steps} warmup={args.warmup}")
+    head = forward_record(w, args.steps, args.warmup)
+    log(f"headline {head['us']} us, {head['GBps']} GB/s")
+
+    extra = {}
+    if not args.quick:
+        sweep = []
+        for name in inputs.BF16_SWEEP:
+            r = forward_record(inputs.WORKLOADS[name], args.steps, args.warmup)
+            log(f"{name}: {r['us']} us, {r['GBps']} GB/s")
+            sweep.append(r)
+        tot_bytes = sum(r["min_bytes"] for r in sweep)
+        tot_us = sum(r["us"] for r in sweep)
+        extra["bf16_sweep"] = sweep
+        extra["bf16_sweep_aggregate"] = dict(
+            min_bytes=tot_bytes, us=round(tot_us, 3), GBps=round(tot_bytes / tot_us / 1e3, 1),
+            frac_hbm=round(tot_bytes / tot_us / 1e3 / HBM_PEAK_GBPS, 4))
+        others = []
+        for name in ("c4s1_dcnv3_bf16_128", "c4s2_dcnv3_bf16_128", "c5_dcnv4_f32_56_fwdbwd"):
+            r = forward_record(inputs.WORKLOADS[name], args.steps, args.warmup)
+            log(f"{name}: {r['us']} us, {r['GBps']} GB/s")
+            others.append(r)
+        extra["other_forward"] = others
+        w5 = inputs.WORKLOADS["c5_dcnv4_f32_56_fwdbwd"]
+        bms, beager, R = time_launches(w5, max(20, args.steps // 4), min(args.warmup, 10), backward=True)
+        extra["backward"] = dict(workload=w5.name, us=round(bms * 1e3, 3), eager_us=round(beager * 1e3, 3),
+                                 min_bytes=w5.min_bytes_backward(),
+                                 GBps=round(w5.min_bytes_backward() / (bms * 1e-3) / 1e9, 1),
+                                 frac_hbm=round(w5.min_bytes_backward() / (bms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4))
+        log(f"backward c5: {extra['backward']['us']} us")
+
+    cpu = None
+    if not args.quick and not args.no_cpu_baseline:
+        cpu = cpu_baseline(w)
+        log(f"cpu oracle {cpu['value']} GB/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": head["GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["us"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: DCNv4 core forward, fp16 in/out with fp32 accumulation, "
+                               f"N={w.N}, {w.H}x{w.W}, C={w.C}, G={w.G} (Cg={w.Cg}), K={w.K}, "
+                               f"stride {w.stride}, pad {w.pad}, raw mask",
+                   "global_batch": w.N, "parallelism": "single GPU"},
+        "Gsamples_s": head["Gsamples_s"],
+        "frac_hbm_peak": head["frac_hbm"],
+        "eager_ms_per_step": round(head["eager_us"] / 1e3, 6),
+        "roofline": {"bound": "hbm", "achieved": head["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": head["frac_hbm"],
+                     "traffic": traffic_record(w.name, head["min_bytes"])},
+        "cpu_baseline": cpu,
+        "kernel_hash": kernel_hash(),
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

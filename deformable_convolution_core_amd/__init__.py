@@ -1,0 +1,177 @@
+"""MI355X (gfx950) deformable sampling core of DCNv3 / DCNv4.
+
+A thin ctypes binding over the C ABI of ``libdcn_core.so`` (declared in
+``include/dcn_core.h``): it checks tensor shapes, dtypes and devices, allocates
+outputs with torch, and passes raw device pointers plus torch's current HIP
+stream.  Every step of the computation runs in the library's HIP kernels;
+there is no other implementation behind these functions, and they raise if
+the library is not built.
+
+The operation (pages: "没有CUDA内核也能跑：InternImage-G的DCNv3纯PyTorch回退实现逐行解读",
+trdm.cn, section 4 steps 1-5; "DCNv4高效实践指南", seekfood.cn, core-architecture
+section): for every output pixel and channel group, sample the group's
+channels bilinearly (zero outside the map) at K*K offset positions around the
+pixel and sum them weighted by the per-point mask, softmax-normalised for
+DCNv3 and raw for DCNv4.  Tensors are channels-last:
+input (N,H,W,G*Cg), offset (N,Ho,Wo,G*K*K*2) as (dx,dy) pixel pairs,
+mask (N,Ho,Wo,G*K*K), output (N,Ho,Wo,G*Cg).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["forward", "backward", "out_size", "dcn_core", "DCNCoreFunction", "DCNError",
+           "library_path", "load_library"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libdcn_core.so")
+_lib = None
+
+DCN_F32, DCN_F16, DCN_BF16 = 0, 1, 2
+_DTYPE = {torch.float32: DCN_F32, torch.float16: DCN_F16, torch.bfloat16: DCN_BF16}
+EXPORTED = ("dcn_core_out_size", "dcn_core_forward", "dcn_core_backward", "dcn_status_string")
+
+
+class DCNError(RuntimeError):
+    """A dcn_core call returned a non-OK status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def load_library(path: str | None = None):
+    """Load libdcn_core.so (once) and declare its C signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or library_path
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"HIP library not built: {p} is missing; build it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'` at the repository root")
+    lib = ctypes.CDLL(p)
+    i, f, vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    lib.dcn_core_out_size.argtypes = [i] * 5
+    lib.dcn_core_out_size.restype = i
+    lib.dcn_core_forward.argtypes = [vp] * 4 + [i] * 9 + [f, i, i, vp]
+    lib.dcn_core_forward.restype = i
+    lib.dcn_core_backward.argtypes = [vp] * 7 + [i] * 9 + [f, i, i, vp]
+    lib.dcn_core_backward.restype = i
+    lib.dcn_status_string.argtypes = [i]
+    lib.dcn_status_string.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = load_library().dcn_status_string(rc).decode()
+        raise DCNError(rc, f"{what}: {msg}")
+
+
+def out_size(n: int, kernel_size: int, stride: int, pad: int, dilation: int) -> int:
+    """Output extent along one axis (<= 0 if invalid), from the library."""
+    return int(load_library().dcn_core_out_size(n, kernel_size, stride, pad, dilation))
+
+
+def _ptr(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() else ctypes.c_void_p(0)
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _geometry(input, offset, mask, kernel_size, stride, pad, dilation, group):
+    if input.dim() != 4:
+        raise ValueError("input must be (N, H, W, G*Cg)")
+    N, H, W, C = input.shape
+    if group < 1 or C % group:
+        raise ValueError(f"channels {C} not divisible by group {group}")
+    Ho = out_size(H, kernel_size, stride, pad, dilation)
+    Wo = out_size(W, kernel_size, stride, pad, dilation)
+    if Ho <= 0 or Wo <= 0:
+        raise ValueError("empty output grid for this geometry")
+    P = kernel_size * kernel_size
+    if tuple(offset.shape) != (N, Ho, Wo, group * P * 2):
+        raise ValueError(f"offset must be {(N, Ho, Wo, group * P * 2)}, got {tuple(offset.shape)}")
+    if tuple(mask.shape) != (N, Ho, Wo, group * P):
+        raise ValueError(f"mask must be {(N, Ho, Wo, group * P)}, got {tuple(mask.shape)}")
+    for name, t in (("input", input), ("offset", offset), ("mask", mask)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (channels-last NHWC)")
+        if t.dtype != input.dtype or t.device != input.device:
+            raise ValueError(f"{name} must share input's dtype and device")
+    if input.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {input.dtype}")
+    return N, H, W, C, C // group, Ho, Wo
+
+
+def forward(input, offset, mask, *, kernel_size=3, stride=1, pad=1, dilation=1,
+            offset_scale=1.0, softmax=False, group=1, out=None) -> torch.Tensor:
+    """Forward sampling core on input.device, on torch's current stream."""
+    N, H, W, C, Cg, Ho, Wo = _geometry(input, offset, mask, kernel_size, stride, pad, dilation, group)
+    if out is None:
+        out = torch.empty((N, Ho, Wo, C), dtype=input.dtype, device=input.device)
+    elif tuple(out.shape) != (N, Ho, Wo, C) or out.dtype != input.dtype or not out.is_contiguous() \
+            or out.device != input.device:
+        raise ValueError("out has the wrong shape, dtype, device or layout")
+    with torch.cuda.device(input.device):
+        rc = load_library().dcn_core_forward(
+            _ptr(input), _ptr(offset), _ptr(mask), _ptr(out), N, H, W, group, Cg, kernel_size,
+            stride, pad, dilation, float(offset_scale), int(bool(softmax)), _DTYPE[input.dtype],
+            _stream(input.device))
+    _check(rc, "dcn_core_forward")
+    return out
+
+
+def backward(input, offset, mask, grad_output, *, kernel_size=3, stride=1, pad=1, dilation=1,
+             offset_scale=1.0, softmax=False, group=1):
+    """Gradients (grad_input, grad_offset, grad_mask) for grad_output."""
+    N, H, W, C, Cg, Ho, Wo = _geometry(input, offset, mask, kernel_size, stride, pad, dilation, group)
+    if tuple(grad_output.shape) != (N, Ho, Wo, C) or grad_output.dtype != input.dtype \
+            or not grad_output.is_contiguous() or grad_output.device != input.device:
+        raise ValueError("grad_output has the wrong shape, dtype, device or layout")
+    gi = torch.empty_like(input)
+    goff = torch.empty_like(offset)
+    gm = torch.empty_like(mask)
+    with torch.cuda.device(input.device):
+        rc = load_library().dcn_core_backward(
+            _ptr(input), _ptr(offset), _ptr(mask), _ptr(grad_output), _ptr(gi), _ptr(goff), _ptr(gm),
+            N, H, W, group, Cg, kernel_size, stride, pad, dilation, float(offset_scale),
+            int(bool(softmax)), _DTYPE[input.dtype], _stream(input.device))
+    _check(rc, "dcn_core_backward")
+    return gi, goff, gm
+
+
+class DCNCoreFunction(torch.autograd.Function):
+    """Autograd wrapper: the backward recomputes the sampling from the saved
+    input, offset and mask (nothing else is kept between the passes)."""
+
+    @staticmethod
+    def forward(ctx, input, offset, mask, kernel_size, stride, pad, dilation, offset_scale,
+                softmax, group):
+        ctx.save_for_backward(input, offset, mask)
+        ctx.cfg = dict(kernel_size=kernel_size, stride=stride, pad=pad, dilation=dilation,
+                       offset_scale=offset_scale, softmax=softmax, group=group)
+        return forward(input, offset, mask, **ctx.cfg)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        input, offset, mask = ctx.saved_tensors
+        gi, goff, gm = backward(input, offset, mask, grad_out.contiguous(), **ctx.cfg)
+        return gi, goff, gm, None, None, None, None, None, None, None
+
+
+def dcn_core(input, offset, mask, kernel_size=3, stride=1, pad=1, dilation=1, offset_scale=1.0,
+             softmax=False, group=1):
+    """Differentiable entry point (forward + analytic backward in HIP)."""
+    return DCNCoreFunction.apply(input, offset, mask, kernel_size, stride, pad, dilation,
+                                 offset_scale, softmax, group)

@@ -1,0 +1,248 @@
+// dcn_core.hip -- C ABI of the deformable sampling core (declared in
+// include/dcn_core.h): host-side validation, launch geometry and the choice
+// of one template variant of each kernel.  The operation is defined in the
+// header; the kernels live in dcn_kernels.hpp.
+//
+// Variants are compile-time specialisations of one kernel (element type,
+// gather width, channels per lane, K = 3 or runtime K), chosen from the
+// sizes and pointer alignment of the call; there is no other code path.
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "dcn_core.h"
+#include "dcn_kernels.hpp"
+
+using namespace dcn;
+
+namespace {
+
+constexpr int64_t kMaxImageBytes = (1ll << 31) - 4096;   // one image must fit a buffer resource
+
+struct Call {
+    int N, H, W, G, Cg, K, stride, pad, dil, Ho, Wo;
+    float alpha;
+    int softmax, dtype, ebytes;
+};
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int elem_bytes(int dtype)
+{
+    switch (dtype) {
+    case DCN_F32: return 4;
+    case DCN_F16: return 2;
+    case DCN_BF16: return 2;
+    default: return 0;
+    }
+}
+
+// Host validation shared by forward and backward; touches no device state.
+int validate(Call& c, int N, int H, int W, int G, int Cg, int K, int stride, int pad, int dil,
+             float alpha, int softmax, int dtype)
+{
+    c = Call{N, H, W, G, Cg, K, stride, pad, dil, 0, 0, alpha, softmax, dtype, elem_bytes(dtype)};
+    if (c.ebytes == 0) return DCN_ERR_INVALID_ARG;
+    if (N < 0 || H < 1 || W < 1 || G < 1 || Cg < 1 || K < 1 || stride < 1 || dil < 1 || pad < 0)
+        return DCN_ERR_INVALID_ARG;
+    if (softmax != 0 && softmax != 1) return DCN_ERR_INVALID_ARG;
+    if (!(alpha == alpha) || alpha - alpha != 0.0f) return DCN_ERR_INVALID_ARG;   // NaN or Inf
+    c.Ho = dcn_core_out_size(H, K, stride, pad, dil);
+    c.Wo = dcn_core_out_size(W, K, stride, pad, dil);
+    if (c.Ho <= 0 || c.Wo <= 0) return DCN_ERR_INVALID_ARG;
+    if (K > 16) return DCN_ERR_UNSUPPORTED;
+    const int64_t C = (int64_t)G * Cg;
+    const int64_t P = (int64_t)K * K;
+    if (C >= (1ll << 31)) return DCN_ERR_UNSUPPORTED;
+    const int64_t in_img = (int64_t)H * W * C, out_img = (int64_t)c.Ho * c.Wo * C;
+    const int64_t off_img = (int64_t)c.Ho * c.Wo * G * P * 2;
+    if (in_img * c.ebytes > kMaxImageBytes || out_img >= (1ll << 31) || off_img >= (1ll << 31))
+        return DCN_ERR_UNSUPPORTED;
+    return DCN_OK;
+}
+
+Geometry make_geometry(const Call& c, int cpl)
+{
+    Geometry g{};
+    g.H = c.H; g.W = c.W; g.C = c.G * c.Cg; g.groups = c.G; g.Ho = c.Ho; g.Wo = c.Wo;
+    g.K = c.K; g.P = c.K * c.K; g.stride = c.stride; g.pad = c.pad; g.dil = c.dil;
+    g.c0 = c.dil * (c.K - 1) / 2;
+    g.alpha = c.alpha;
+    g.softmax = c.softmax;
+    g.in_row_bytes = (uint32_t)(g.C * c.ebytes);
+    g.in_line_bytes = (uint32_t)((int64_t)c.W * g.C * c.ebytes);
+    g.in_image_bytes = (uint32_t)((int64_t)c.H * c.W * g.C * c.ebytes);
+    const uint32_t chunks = (uint32_t)(g.C / cpl);
+    g.lanes_per_image = (uint32_t)c.Ho * (uint32_t)c.Wo * chunks;
+    g.blocks_per_image = (g.lanes_per_image + kBlock - 1) / kBlock;
+    g.chunks = make_fastdiv(chunks);
+    g.lanes_per_group = make_fastdiv((uint32_t)(c.Cg / cpl));
+    g.wo_div = make_fastdiv((uint32_t)c.Wo);
+    return g;
+}
+
+int launch_status()
+{
+    return hipGetLastError() == hipSuccess ? DCN_OK : DCN_ERR_HIP;
+}
+
+template <typename T, int LB, int NL>
+int forward_variant(const FwdArgs& base, const Call& c, hipStream_t st)
+{
+    constexpr int CPL = NL * LB / (int)sizeof(T);
+    FwdArgs a = base;
+    a.geo = make_geometry(c, CPL);
+    const uint64_t blocks = (uint64_t)c.N * a.geo.blocks_per_image;
+    if (blocks >= (1ull << 31)) return DCN_ERR_UNSUPPORTED;
+    if (c.K == 3)
+        hipLaunchKernelGGL((dcn_forward_kernel<T, LB, NL, 3>), dim3((uint32_t)blocks), dim3(kBlock), 0, st, a);
+    else
+        hipLaunchKernelGGL((dcn_forward_kernel<T, LB, NL, 0>), dim3((uint32_t)blocks), dim3(kBlock), 0, st, a);
+    return launch_status();
+}
+
+// Widest gather whose size divides a group's row and whose alignment the
+// input and output pointers allow; two 16-byte loads per corner when a
+// group row holds 32 bytes or more.
+template <typename T>
+int forward_typed(const FwdArgs& a, const Call& c, hipStream_t st)
+{
+    const int row = c.Cg * (int)sizeof(T);
+    auto ok = [&](int lb) {
+        return row % lb == 0 && aligned(a.input, lb) && aligned(a.output, lb);
+    };
+    if (ok(16) && row % 32 == 0) return forward_variant<T, 16, 2>(a, c, st);
+    if (ok(16)) return forward_variant<T, 16, 1>(a, c, st);
+    if (ok(8)) return forward_variant<T, 8, 1>(a, c, st);
+    if (ok(4)) return forward_variant<T, 4, 1>(a, c, st);
+    if constexpr (sizeof(T) == 2) {
+        if (ok(2)) return forward_variant<T, 2, 1>(a, c, st);
+    }
+    return DCN_ERR_INVALID_ARG;   // pointers not aligned to their element size
+}
+
+template <int LB, int L>
+int backward_variant(const BwdArgs& base, const Call& c, hipStream_t st)
+{
+    BwdArgs a = base;
+    a.geo = make_geometry(c, LB / 4);
+    const uint64_t blocks = (uint64_t)c.N * a.geo.blocks_per_image;
+    if (blocks >= (1ll << 31)) return DCN_ERR_UNSUPPORTED;
+    if (c.K == 3)
+        hipLaunchKernelGGL((dcn_backward_kernel<LB, L, 3>), dim3((uint32_t)blocks), dim3(kBlock), 0, st, a);
+    else
+        hipLaunchKernelGGL((dcn_backward_kernel<LB, L, 0>), dim3((uint32_t)blocks), dim3(kBlock), 0, st, a);
+    return launch_status();
+}
+
+template <int LB>
+int backward_lanes(const BwdArgs& a, const Call& c, hipStream_t st, int L)
+{
+    switch (L) {
+    case 1: return backward_variant<LB, 1>(a, c, st);
+    case 2: return backward_variant<LB, 2>(a, c, st);
+    case 4: return backward_variant<LB, 4>(a, c, st);
+    case 8: return backward_variant<LB, 8>(a, c, st);
+    case 16: return backward_variant<LB, 16>(a, c, st);
+    case 32: return backward_variant<LB, 32>(a, c, st);
+    case 64: return backward_variant<LB, 64>(a, c, st);
+    default: return DCN_ERR_UNSUPPORTED;
+    }
+}
+
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int zero_fill(float* p, int64_t n, hipStream_t st)
+{
+    if (n <= 0) return DCN_OK;
+    int64_t head = 0;
+    while (head < n && !aligned(p + head, 16)) ++head;   // at most 3 floats
+    const int64_t n4 = (n - head) / 4;
+    const int64_t tail = (n - head) - 4 * n4;
+    // head and tail floats (at most 3 + 3) are written by block 0
+    if (head > 0)
+        hipLaunchKernelGGL(dcn_zero_kernel, dim3(1), dim3(kBlock), 0, st, (float4*)nullptr, (size_t)0, p,
+                           (int)head);
+    const int64_t blocks = n4 > 0 ? (n4 + kBlock - 1) / kBlock : 1;
+    hipLaunchKernelGGL(dcn_zero_kernel, dim3((uint32_t)(blocks < 4096 ? blocks : 4096)), dim3(kBlock), 0, st,
+                       (float4*)(p + head), (size_t)n4, p + head + 4 * n4, (int)tail);
+    return launch_status();
+}
+
+}  // namespace
+
+extern "C" int dcn_core_out_size(int in, int K, int stride, int pad, int dilation)
+{
+    if (in < 1 || K < 1 || stride < 1 || pad < 0 || dilation < 1) return 0;
+    const int64_t span = (int64_t)dilation * (K - 1) + 1;
+    const int64_t num = (int64_t)in + 2ll * pad - span;
+    if (num < 0) return 0;
+    const int64_t out = num / stride + 1;
+    return out < (1ll << 31) ? (int)out : 0;
+}
+
+extern "C" int dcn_core_forward(const void* input, const void* offset, const void* mask, void* output,
+                                int N, int H, int W, int G, int Cg, int K, int stride, int pad,
+                                int dilation, float offset_scale, int softmax_flag, int dtype,
+                                void* stream)
+{
+    Call c;
+    int rc = validate(c, N, H, W, G, Cg, K, stride, pad, dilation, offset_scale, softmax_flag, dtype);
+    if (rc != DCN_OK) return rc;
+    if (N == 0) return DCN_OK;
+    if (!input || !offset || !mask || !output) return DCN_ERR_INVALID_ARG;
+    if (!aligned(offset, 2 * c.ebytes) || !aligned(mask, c.ebytes)) return DCN_ERR_INVALID_ARG;
+    FwdArgs a{};
+    a.input = input; a.offset = offset; a.mask = mask; a.output = output;
+    hipStream_t st = (hipStream_t)stream;
+    switch (dtype) {
+    case DCN_F32: return forward_typed<float>(a, c, st);
+    case DCN_F16: return forward_typed<_Float16>(a, c, st);
+    default: return forward_typed<__bf16>(a, c, st);
+    }
+}
+
+extern "C" int dcn_core_backward(const void* input, const void* offset, const void* mask,
+                                 const void* grad_output, void* grad_input, void* grad_offset,
+                                 void* grad_mask, int N, int H, int W, int G, int Cg, int K, int stride,
+                                 int pad, int dilation, float offset_scale, int softmax_flag, int dtype,
+                                 void* stream)
+{
+    Call c;
+    int rc = validate(c, N, H, W, G, Cg, K, stride, pad, dilation, offset_scale, softmax_flag, dtype);
+    if (rc != DCN_OK) return rc;
+    if (dtype != DCN_F32) return DCN_ERR_UNSUPPORTED;
+    if (N == 0) return DCN_OK;
+    if (!input || !offset || !mask || !grad_output || !grad_input || !grad_offset || !grad_mask)
+        return DCN_ERR_INVALID_ARG;
+    if (!aligned(input, 4) || !aligned(grad_output, 4) || !aligned(grad_input, 4) ||
+        !aligned(offset, 8) || !aligned(grad_offset, 8) || !aligned(mask, 4) || !aligned(grad_mask, 4))
+        return DCN_ERR_INVALID_ARG;
+    int LB, L;
+    if (Cg % 4 == 0 && pow2(Cg / 4) && Cg / 4 <= 64 && aligned(input, 16) && aligned(grad_input, 16)) {
+        LB = 16; L = Cg / 4;
+    } else if (pow2(Cg) && Cg <= 64) {
+        LB = 4; L = Cg;
+    } else {
+        return DCN_ERR_UNSUPPORTED;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    rc = zero_fill((float*)grad_input, (int64_t)N * H * W * G * Cg, st);
+    if (rc != DCN_OK) return rc;
+    BwdArgs a{};
+    a.input = input; a.offset = offset; a.mask = mask; a.grad_out = grad_output;
+    a.grad_input = (float*)grad_input; a.grad_offset = (float*)grad_offset; a.grad_mask = (float*)grad_mask;
+    return LB == 16 ? backward_lanes<16>(a, c, st, L) : backward_lanes<4>(a, c, st, L);
+}
+
+extern "C" const char* dcn_status_string(int status)
+{
+    switch (status) {
+    case DCN_OK: return "DCN_OK";
+    case DCN_ERR_INVALID_ARG: return "DCN_ERR_INVALID_ARG: invalid size, geometry, dtype, pointer or alignment";
+    case DCN_ERR_UNSUPPORTED: return "DCN_ERR_UNSUPPORTED: valid request outside what this build implements";
+    case DCN_ERR_HIP: return "DCN_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown dcn_status";
+    }
+}

@@ -1,0 +1,467 @@
+// dcn_kernels.hpp -- gfx950 kernels of the deformable sampling core.
+//
+// Pages cited (title, site):
+//   [FB]  "没有CUDA内核也能跑：InternImage-G的DCNv3纯PyTorch回退实现逐行解读"
+//         (the DCNv3 pure-PyTorch fallback read line by line), trdm.cn
+//   [FII] FlashInternImage image-classification guide, m.nxbn.cn: section 2.2
+//         (one fused kernel instead of several memory-bound ones; no sampled
+//         intermediate written to global memory)
+//   [V4]  "DCNv4高效实践指南：掌握可变形卷积的3倍速度提升技术", seekfood.cn:
+//         core-architecture section (no softmax; fewer redundant memory ops)
+//
+// One lane owns CPL contiguous channels of one (pixel, group).  The lanes of
+// a wave cover consecutive channel chunks of consecutive pixels of one image,
+// so each bilinear corner read is a contiguous NHWC row segment and the
+// output store of a wave is one contiguous span.  The P offsets and mask
+// values of a (pixel, group) are read once per lane (the L = Cg/CPL lanes of
+// a group read the same bytes, which L1 serves).  Nothing is staged through
+// global memory: coordinates, weights, the optional softmax and the
+// accumulation stay in registers ([FII] section 2.2).
+//
+// Gathers go through a buffer resource spanning exactly one image.  Every
+// corner that lies off the map gets an out-of-range offset, for which the
+// hardware returns zeros, so no lane reads outside the image it samples and
+// off-map pixels never contaminate a sum (even if a neighbouring row holds
+// a NaN).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dcn {
+
+constexpr int kBlock = 256;
+constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past any image (images are < 2^31 bytes)
+
+// ---------------------------------------------------------------------------
+// Division by a runtime-invariant divisor with a precomputed multiplier
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994): for 1 <= d < 2^31 and x < 2^31,
+// q = (umulhi(x, m) + x) >> s with s = ceil(log2 d), m = ceil(2^(32+s)/d) - 2^32.
+struct FastDiv {
+    uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    FastDiv f;
+    f.d = d;
+    f.s = 0;
+    while ((1ull << f.s) < d) ++f.s;
+    f.m = (uint32_t)((((1ull << 32) * ((1ull << f.s) - d)) / d) + 1);
+    return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t x, const FastDiv& f)
+{
+    return (__umulhi(x, f.m) + x) >> f.s;
+}
+
+// ---------------------------------------------------------------------------
+// Element types: widened exactly to float, rounded once (nearest even) back.
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+    static constexpr int bytes = 4;
+    __device__ static float widen(uint32_t u) { return __uint_as_float(u); }
+    __device__ static uint32_t narrow(float f) { return __float_as_uint(f); }
+};
+template <> struct Elem<_Float16> {
+    static constexpr int bytes = 2;
+    __device__ static float widen(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)u); }
+    __device__ static uint32_t narrow(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+};
+template <> struct Elem<__bf16> {
+    static constexpr int bytes = 2;
+    __device__ static float widen(uint32_t u) { return __uint_as_float(u << 16); }
+    __device__ static uint32_t narrow(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+};
+
+template <typename T>
+__device__ __forceinline__ float ld1(const T* p)
+{
+    if constexpr (sizeof(T) == 4) return *(const float*)p;
+    else return Elem<T>::widen(*(const uint16_t*)p);
+}
+
+// Two consecutive elements (an offset pair; 2*sizeof(T)-aligned).
+template <typename T>
+__device__ __forceinline__ float2 ld2(const T* p)
+{
+    if constexpr (sizeof(T) == 4) return *(const float2*)p;
+    else {
+        const uint32_t u = *(const uint32_t*)p;
+        return make_float2(Elem<T>::widen(u & 0xffffu), Elem<T>::widen(u >> 16));
+    }
+}
+
+// LB bytes (LB in {2,4,8,16}, >= sizeof(T)) from a buffer resource, widened
+// to LB/sizeof(T) floats.
+template <typename T, int LB>
+__device__ __forceinline__ void gather(__amdgpu_buffer_rsrc_t r, uint32_t off, float* f)
+{
+    constexpr int E = LB / Elem<T>::bytes;
+    uint32_t d[LB >= 4 ? LB / 4 : 1];
+    if constexpr (LB == 16) {
+        auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
+    } else if constexpr (LB == 8) {
+        auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        d[0] = v[0]; d[1] = v[1];
+    } else if constexpr (LB == 4) {
+        d[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    } else {
+        static_assert(LB == 2 && Elem<T>::bytes == 2, "load width");
+        d[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    }
+    if constexpr (Elem<T>::bytes == 4) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) f[e] = __uint_as_float(d[e]);
+    } else if constexpr (LB == 2) {
+        f[0] = Elem<T>::widen(d[0]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < LB / 4; ++q) {
+            f[2 * q] = Elem<T>::widen(d[q] & 0xffffu);
+            f[2 * q + 1] = Elem<T>::widen(d[q] >> 16);
+        }
+    }
+}
+
+// Store LB bytes built from LB/sizeof(T) floats (pointer LB-aligned).
+template <typename T, int LB>
+__device__ __forceinline__ void store(void* p, const float* f)
+{
+    if constexpr (LB == 2) {
+        *(uint16_t*)p = (uint16_t)Elem<T>::narrow(f[0]);
+    } else {
+        struct alignas(LB) V { uint32_t d[LB / 4]; } v;
+#pragma unroll
+        for (int q = 0; q < LB / 4; ++q) {
+            if constexpr (Elem<T>::bytes == 4) v.d[q] = __float_as_uint(f[q]);
+            else v.d[q] = Elem<T>::narrow(f[2 * q]) | (Elem<T>::narrow(f[2 * q + 1]) << 16);
+        }
+        *(V*)p = v;
+    }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t image_rsrc(const void* base, uint32_t bytes)
+{
+    // dword3 0x00020000: raw (unswizzled) buffer, 32-bit data format, gfx9 family
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// The hardware hands workgroup b to XCD (b mod 8).  Renumber so each XCD gets
+// one contiguous range of logical tiles: neighbouring tiles, which sample
+// overlapping input rows, then share that XCD's L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb)
+{
+    const uint32_t xcd = b & 7u, k = b >> 3, q = nb >> 3, r = nb & 7u;
+    return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
+}
+
+struct Geometry {
+    int H, W, C, groups, Ho, Wo, K, P, stride, pad, dil, c0;
+    float alpha;
+    int softmax;
+    uint32_t in_image_bytes;      // H*W*C*b
+    uint32_t in_row_bytes;        // C*b     (one pixel)
+    uint32_t in_line_bytes;       // W*C*b   (one image row)
+    uint32_t lanes_per_image;     // Ho*Wo*C/CPL
+    uint32_t blocks_per_image;
+    FastDiv chunks;               // C/CPL channel chunks per pixel
+    FastDiv lanes_per_group;      // L = Cg/CPL
+    FastDiv wo_div;               // Wo
+};
+
+struct FwdArgs {
+    const void* input;
+    const void* offset;
+    const void* mask;
+    void* output;
+    Geometry geo;
+};
+
+struct BwdArgs {
+    const void* input;
+    const void* offset;
+    const void* mask;
+    const void* grad_out;
+    float* grad_input;
+    float* grad_offset;
+    float* grad_mask;
+    Geometry geo;
+};
+
+// The (image, pixel, group, channel chunk) a lane owns.
+struct LaneWork {
+    uint32_t n, pix, ho, wo, g, cc;
+    bool active;
+};
+
+__device__ __forceinline__ LaneWork lane_work(const Geometry& G)
+{
+    LaneWork w;
+    const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
+    w.n = b / G.blocks_per_image;                         // wave-uniform
+    const uint32_t t = (b - w.n * G.blocks_per_image) * kBlock + threadIdx.x;
+    w.active = t < G.lanes_per_image;
+    w.pix = fdiv(t, G.chunks);
+    w.cc = t - w.pix * G.chunks.d;
+    w.g = fdiv(w.cc, G.lanes_per_group);
+    w.ho = fdiv(w.pix, G.wo_div);
+    w.wo = w.pix - w.ho * G.Wo;
+    return w;
+}
+
+// One sampling point: binary32 coordinates in the documented order, floor,
+// fractions, corner validity and the four gather offsets (out of range for
+// off-map corners).  Corners are 00, 01, 10, 11 = (y0,x0), (y0,x0+1),
+// (y0+1,x0), (y0+1,x0+1).
+struct Sample {
+    float lx, ly;
+    bool inmap;
+    bool v[4];
+    uint32_t off[4];
+};
+
+__device__ __forceinline__ Sample make_sample(const Geometry& G, float bx, float by, int i, int j,
+                                              float dx, float dy, uint32_t chan_bytes)
+{
+    Sample s;
+    const float tx = (float)(i * G.dil - G.c0) + dx;
+    const float ty = (float)(j * G.dil - G.c0) + dy;
+    float x = fmaf(G.alpha, tx, bx);
+    float y = fmaf(G.alpha, ty, by);
+    s.inmap = x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H;
+    x = s.inmap ? x : -2.0f;          // off the map or NaN: park where no corner is valid
+    y = s.inmap ? y : -2.0f;
+    const float fx = floorf(x), fy = floorf(y);
+    s.lx = x - fx;
+    s.ly = y - fy;
+    const int x0 = (int)fx, y0 = (int)fy;
+    const bool vx0 = (uint32_t)x0 < (uint32_t)G.W, vx1 = (uint32_t)(x0 + 1) < (uint32_t)G.W;
+    const bool vy0 = (uint32_t)y0 < (uint32_t)G.H, vy1 = (uint32_t)(y0 + 1) < (uint32_t)G.H;
+    s.v[0] = vy0 && vx0; s.v[1] = vy0 && vx1; s.v[2] = vy1 && vx0; s.v[3] = vy1 && vx1;
+    // modular arithmetic: a00 may wrap when x0 or y0 is -1, but only valid
+    // corners keep their offset and those are in [0, image bytes)
+    const uint32_t a00 = (uint32_t)y0 * G.in_line_bytes + (uint32_t)x0 * G.in_row_bytes + chan_bytes;
+    s.off[0] = s.v[0] ? a00 : kOOB;
+    s.off[1] = s.v[1] ? a00 + G.in_row_bytes : kOOB;
+    s.off[2] = s.v[2] ? a00 + G.in_line_bytes : kOOB;
+    s.off[3] = s.v[3] ? a00 + G.in_line_bytes + G.in_row_bytes : kOOB;
+    return s;
+}
+
+// ---------------------------------------------------------------------------
+// Forward.  T: element type; LB: bytes per gather load; NL: loads per corner
+// per lane, so CPL = NL*LB/sizeof(T) channels per lane; KT: K, or 0 for a
+// runtime K.
+template <typename T, int LB, int NL, int KT>
+__global__ __launch_bounds__(kBlock) void dcn_forward_kernel(FwdArgs a)
+{
+    constexpr int EPL = LB / Elem<T>::bytes;          // elements per load
+    constexpr int CPL = NL * EPL;                      // channels per lane
+    const Geometry& G = a.geo;
+    const LaneWork lw = lane_work(G);
+    if (!lw.active) return;
+
+    const char* in_img = (const char*)a.input + (size_t)lw.n * G.in_image_bytes;
+    const __amdgpu_buffer_rsrc_t rin = image_rsrc(in_img, G.in_image_bytes);
+    const uint32_t chan_bytes = lw.cc * (CPL * Elem<T>::bytes);
+    const size_t pix_global = (size_t)lw.n * G.Ho * G.Wo + lw.pix;
+    const size_t pg = pix_global * G.groups + lw.g;
+    const T* off = (const T*)a.offset + pg * G.P * 2;
+    const T* mk = (const T*)a.mask + pg * G.P;
+    const float bx = (float)((int)lw.wo * G.stride - G.pad + G.c0);
+    const float by = (float)((int)lw.ho * G.stride - G.pad + G.c0);
+
+    float acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+
+    auto point = [&](int i, int j, float m, float2 d) {
+        const Sample s = make_sample(G, bx, by, i, j, d.x, d.y, chan_bytes);
+        const float mm = s.inmap ? m : 0.f;
+        const float hy = 1.0f - s.ly, hx = 1.0f - s.lx;
+        const float mhy = mm * hy, mly = mm * s.ly;
+        float w[4] = {mhy * hx, mhy * s.lx, mly * hx, mly * s.lx};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = s.v[k] ? w[k] : 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+#pragma unroll
+            for (int l = 0; l < NL; ++l) {
+                float f[EPL];
+                gather<T, LB>(rin, s.off[k] + l * LB, f);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[l * EPL + e] = fmaf(w[k], f[e], acc[l * EPL + e]);
+            }
+        }
+    };
+
+    if constexpr (KT > 0) {
+        constexpr int P = KT * KT;
+        float m[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) m[p] = ld1(mk + p);
+        if (G.softmax) {
+            float mx = m[0];
+#pragma unroll
+            for (int p = 1; p < P; ++p) mx = fmaxf(mx, m[p]);
+            float sum = 0.f;
+#pragma unroll
+            for (int p = 0; p < P; ++p) { m[p] = __expf(m[p] - mx); sum += m[p]; }
+            const float inv = 1.0f / sum;
+#pragma unroll
+            for (int p = 0; p < P; ++p) m[p] *= inv;
+        }
+#pragma unroll
+        for (int i = 0; i < KT; ++i)
+#pragma unroll
+            for (int j = 0; j < KT; ++j) point(i, j, m[i * KT + j], ld2(off + 2 * (i * KT + j)));
+    } else {
+        float mx = 0.f, inv = 1.f;
+        if (G.softmax) {
+            mx = ld1(mk);
+            for (int p = 1; p < G.P; ++p) mx = fmaxf(mx, ld1(mk + p));
+            float sum = 0.f;
+            for (int p = 0; p < G.P; ++p) sum += __expf(ld1(mk + p) - mx);
+            inv = 1.0f / sum;
+        }
+        for (int i = 0; i < G.K; ++i)
+            for (int j = 0; j < G.K; ++j) {
+                const int p = i * G.K + j;
+                float m = ld1(mk + p);
+                if (G.softmax) m = __expf(m - mx) * inv;
+                point(i, j, m, ld2(off + 2 * p));
+            }
+    }
+
+    char* out = (char*)a.output + (pix_global * G.C + lw.cc * CPL) * Elem<T>::bytes;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) store<T, LB>(out + l * LB, &acc[l * EPL]);
+}
+
+// ---------------------------------------------------------------------------
+// Backward (binary32).  Same lane mapping; L = Cg/CPL lanes per group, a
+// power of two.  Per point and corner k each lane forms
+// s_k = sum over its channels of g_c * f_kc; then
+//   gm  = sum_k w_k s_k,   gdx = sum_k (dw_k/dx) s_k,   gdy = sum_k (dw_k/dy) s_k
+// are summed over the L lanes of the group with cross-lane adds, and every
+// valid corner receives grad_input[corner, c] += m * w_k * g_c as a float
+// atomic (performed at L2).  For the softmax case grad_mask is finished in a
+// second pass over P that rereads the raw gm_p this same lane stored.
+template <int L>
+__device__ __forceinline__ float group_sum(float v)
+{
+#pragma unroll
+    for (int o = 1; o < L; o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+template <int LB, int L, int KT>
+__global__ __launch_bounds__(kBlock) void dcn_backward_kernel(BwdArgs a)
+{
+    constexpr int CPL = LB / 4;
+    const Geometry& G = a.geo;
+    const LaneWork lw = lane_work(G);
+    // Inactive lanes (past the image) stay for the cross-lane sums but touch
+    // no memory; a group is always wholly active or wholly inactive.
+    const bool act = lw.active;
+
+    const char* in_img = (const char*)a.input + (size_t)lw.n * G.in_image_bytes;
+    const __amdgpu_buffer_rsrc_t rin = image_rsrc(in_img, G.in_image_bytes);
+    const uint32_t chan_bytes = lw.cc * (CPL * 4);
+    const size_t pix_global = (size_t)lw.n * G.Ho * G.Wo + lw.pix;
+    const size_t pg = pix_global * G.groups + lw.g;
+    const float* off = (const float*)a.offset + pg * G.P * 2;
+    const float* mk = (const float*)a.mask + pg * G.P;
+    float* goff = a.grad_offset + pg * G.P * 2;
+    float* gmk = a.grad_mask + pg * G.P;
+    char* gin = (char*)a.grad_input + (size_t)lw.n * G.in_image_bytes;
+    const float bx = (float)((int)lw.wo * G.stride - G.pad + G.c0);
+    const float by = (float)((int)lw.ho * G.stride - G.pad + G.c0);
+    const bool leader = (lw.cc & (L - 1)) == 0;
+
+    float go[CPL];
+    {
+        const float* gp = (const float*)a.grad_out + pix_global * G.C + lw.cc * CPL;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) go[c] = act ? gp[c] : 0.f;
+    }
+
+    float mx = 0.f, inv = 1.f;
+    if (G.softmax && act) {
+        mx = mk[0];
+        for (int p = 1; p < G.P; ++p) mx = fmaxf(mx, mk[p]);
+        float sum = 0.f;
+        for (int p = 0; p < G.P; ++p) sum += __expf(mk[p] - mx);
+        inv = 1.0f / sum;
+    }
+    float dot = 0.f;   // sum_q m_q gm_q (softmax)
+
+    const int K = KT > 0 ? KT : G.K;
+    for (int i = 0; i < K; ++i)
+        for (int j = 0; j < K; ++j) {
+            const int p = i * K + j;
+            float m = 0.f;
+            float2 d = make_float2(__builtin_nanf(""), 0.f);   // inactive: never on the map
+            if (act) {
+                m = mk[p];
+                if (G.softmax) m = __expf(m - mx) * inv;
+                d = ld2(off + 2 * p);
+            }
+            const Sample s = make_sample(G, bx, by, i, j, d.x, d.y, chan_bytes);
+            const float hy = 1.0f - s.ly, hx = 1.0f - s.lx;
+            const float wb[4] = {hy * hx, hy * s.lx, s.ly * hx, s.ly * s.lx};
+            const float dwx[4] = {-hy, hy, -s.ly, s.ly};
+            const float dwy[4] = {-hx, -s.lx, hx, s.lx};
+            float gm = 0.f, gdx = 0.f, gdy = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float f[CPL];
+                gather<float, LB>(rin, s.off[k], f);
+                float sk = 0.f;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) sk = fmaf(go[c], f[c], sk);
+                gm = fmaf(wb[k], sk, gm);
+                gdx = fmaf(dwx[k], sk, gdx);
+                gdy = fmaf(dwy[k], sk, gdy);
+                if (s.v[k]) {
+                    const float mw = m * wb[k];
+                    float* dst = (float*)(gin + s.off[k]);
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) atomicAdd(dst + c, mw * go[c]);
+                }
+            }
+            gm = group_sum<L>(gm);
+            gdx = group_sum<L>(gdx);
+            gdy = group_sum<L>(gdy);
+            if (!s.inmap) { gm = 0.f; gdx = 0.f; gdy = 0.f; }
+            if (act && leader) {
+                *(float2*)(goff + 2 * p) = make_float2(G.alpha * m * gdx, G.alpha * m * gdy);
+                gmk[p] = gm;
+            }
+            dot = fmaf(m, gm, dot);
+        }
+    if (G.softmax && act && leader) {
+        for (int p = 0; p < G.P; ++p) {
+            const float m = __expf(mk[p] - mx) * inv;
+            gmk[p] = m * (gmk[p] - dot);
+        }
+    }
+}
+
+// Zero fill on the caller's stream (a kernel rather than a memset node, so
+// a caller may capture the call in a graph).
+__global__ __launch_bounds__(kBlock) void dcn_zero_kernel(float4* p, size_t n4, float* tail, int ntail)
+{
+    const size_t stride = (size_t)gridDim.x * kBlock;
+    for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < n4; i += stride)
+        p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0.f;
+}
+
+}  // namespace dcn

@@ -1,0 +1,120 @@
+/*
+ * dcn_core.h -- C ABI of the MI355X (gfx950) deformable sampling core used by
+ * DCNv3 and DCNv4.
+ *
+ * Pages cited (title, site):
+ *   [FB]  "没有CUDA内核也能跑：InternImage-G的DCNv3纯PyTorch回退实现逐行解读"
+ *         (the DCNv3 pure-PyTorch fallback read line by line), trdm.cn
+ *   [V4]  "DCNv4高效实践指南：掌握可变形卷积的3倍速度提升技术"
+ *         (DCNv4 practice guide), seekfood.cn
+ *   [A100] "告别DCNv3的卡顿：实测DCNv4在A100上3倍提速…", framerc.cn
+ *
+ * The operation ([FB] section 4, steps 1-5; the DCNv4 variant drops the
+ * softmax, [V4] core-architecture section, [A100] section 1):
+ *
+ *   out[n,ho,wo,g*Cg+c] = sum_{i<K, j<K} m[n,ho,wo,g,p] * B(in[n,:,:,g*Cg+c], x_p, y_p)
+ *
+ *   p   = i*K + j            i = kernel column (x), j = kernel row (y)
+ *   c0  = floor(dilation*(K-1)/2)
+ *   x_p = fmaf(offset_scale, (float)(i*dilation - c0) + dx, (float)(wo*stride - pad + c0))
+ *   y_p = fmaf(offset_scale, (float)(j*dilation - c0) + dy, (float)(ho*stride - pad + c0))
+ *         -- formed in binary32 in exactly this order; these are pixel
+ *         coordinates in the UNPADDED map (the zero padding of step 1 is
+ *         virtual: everything outside [0,H) x [0,W) reads as zero)
+ *   B   = bilinear interpolation from the four pixels around (x_p, y_p);
+ *         corners outside the map contribute zero; a sample with no corner
+ *         on the map (or a NaN/Inf coordinate) contributes nothing
+ *   m   = softmax over the P = K*K points of each (pixel, group) when
+ *         softmax_flag != 0 (DCNv3, [FB] section 3 item 3), else the raw
+ *         mask (DCNv4)
+ *
+ * Weights, softmax and accumulation are binary32 for every dtype; half
+ * precision inputs are widened exactly and the result is rounded once (to
+ * nearest even) to the output dtype.
+ *
+ * Tensor layout (all dense, row-major, channels last, one dtype for all):
+ *   input   (N, H,  W,  G*Cg)        channel = g*Cg + c
+ *   offset  (N, Ho, Wo, G, P, 2)     last axis = (dx, dy) in pixels
+ *   mask    (N, Ho, Wo, G, P)        logits (softmax_flag) or raw weights
+ *   output  (N, Ho, Wo, G*Cg)
+ *   Ho = dcn_core_out_size(H, K, stride, pad, dilation), Wo likewise.
+ * Gradients have the shape and dtype of their primal.
+ *
+ * Ownership and threading: every pointer is a device pointer owned by the
+ * caller.  The library allocates no memory, keeps no state between calls,
+ * and is safe to call from several host threads.  Calls are asynchronous on
+ * `stream` (a hipStream_t passed as void*; NULL = the default stream) and
+ * never synchronise; a kernel fault surfaces at the caller's next
+ * synchronising call.
+ *
+ * Errors: arguments are validated on the host before any HIP call; a
+ * rejected call launches nothing and touches no buffer.
+ */
+#ifndef DCN_CORE_H
+#define DCN_CORE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum dcn_dtype { DCN_F32 = 0, DCN_F16 = 1, DCN_BF16 = 2 };
+
+enum dcn_status {
+    DCN_OK = 0,
+    DCN_ERR_INVALID_ARG = 1,  /* bad size, geometry, dtype or null pointer */
+    DCN_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement */
+    DCN_ERR_HIP = 3           /* the HIP runtime reported an error at launch */
+};
+
+/* Output extent along one axis of a K-tap sampling grid with the given
+ * stride, zero padding and dilation: floor((in + 2*pad - dilation*(K-1) - 1)
+ * / stride) + 1 ([FB] section 4 step 1 takes H_out, W_out from the offset
+ * tensor and notes that stride 2 halves them).  Returns a value <= 0 when the
+ * arguments are invalid (in, K, stride, dilation < 1; pad < 0) or the grid
+ * does not fit. */
+int dcn_core_out_size(int in, int K, int stride, int pad, int dilation);
+
+/* Forward sampling core (definition above).
+ *   input, offset, mask: device pointers, read only; output: device pointer,
+ *   overwritten.  N >= 0 (N == 0 is a no-op and then the pointers may be
+ *   NULL); H, W, G, Cg, K, stride, dilation >= 1; pad >= 0; the output grid
+ *   must be non-empty.  offset_scale is any finite float; softmax_flag is 0
+ *   (raw mask) or 1 (softmax); dtype is a dcn_dtype.
+ * Returns DCN_OK, DCN_ERR_INVALID_ARG, DCN_ERR_UNSUPPORTED (one image of
+ * any tensor holds 2^31 elements or more, or K > 16), or DCN_ERR_HIP. */
+int dcn_core_forward(const void* input, const void* offset, const void* mask, void* output,
+                     int N, int H, int W, int G, int Cg, int K, int stride, int pad,
+                     int dilation, float offset_scale, int softmax_flag, int dtype,
+                     void* stream);
+
+/* Backward of the forward above for an upstream gradient grad_output
+ * (N, Ho, Wo, G*Cg).  Writes:
+ *   grad_input  (N, H, W, G*Cg): zero-filled on `stream`, then every valid
+ *               corner of every sample scatter-adds m_p * w * grad_output
+ *               with float atomics, so its summation order (and its last
+ *               bits) can vary from run to run;
+ *   grad_offset (N, Ho, Wo, G, P, 2): offset_scale * m_p * sum_c g_c * dB/dx
+ *               (and dB/dy), the derivative of the bilinear read taken from
+ *               the right where floor() jumps;
+ *   grad_mask   (N, Ho, Wo, G, P): sum_c g_c * B_p for a raw mask, or the
+ *               softmax Jacobian applied to it, m_p * (gm_p - sum_q m_q gm_q),
+ *               when softmax_flag is set (gradient w.r.t. the logits).
+ * Samples that contribute nothing to the forward get zero gradients.  The
+ * three outputs are overwritten, never accumulated into.  The pages print
+ * no gradient formulas; these are the derivatives of the definition.
+ * Same arguments and errors as dcn_core_forward; dtype must be DCN_F32
+ * (half precision returns DCN_ERR_UNSUPPORTED). */
+int dcn_core_backward(const void* input, const void* offset, const void* mask,
+                      const void* grad_output, void* grad_input, void* grad_offset,
+                      void* grad_mask, int N, int H, int W, int G, int Cg, int K, int stride,
+                      int pad, int dilation, float offset_scale, int softmax_flag, int dtype,
+                      void* stream);
+
+/* Static, human-readable name of a dcn_status value. */
+const char* dcn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCN_CORE_H */

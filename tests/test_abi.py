@@ -1,0 +1,125 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, computes output sizes, and rejects invalid calls on the host
+before any HIP call (no valid compute call is made here)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+import torch
+
+import deformable_convolution_core_amd as dcn
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dcn_core.h")
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dcn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = dcn.load_library()
+    names = declared_functions()
+    assert set(names) == set(dcn.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_out_size_matches_oracle():
+    for n in (1, 2, 3, 7, 8, 14, 56, 128):
+        for K in (1, 2, 3, 5, 7):
+            for s in (1, 2, 3):
+                for p in (0, 1, 2, 3):
+                    for d in (1, 2):
+                        assert dcn.out_size(n, K, s, p, d) == oracle.out_size(n, K, s, p, d)
+    assert dcn.out_size(0, 3, 1, 1, 1) <= 0
+    assert dcn.out_size(8, 0, 1, 1, 1) <= 0
+    assert dcn.out_size(8, 3, 0, 1, 1) <= 0
+    assert dcn.out_size(8, 3, 1, -1, 1) <= 0
+    assert dcn.out_size(8, 3, 1, 1, 0) <= 0
+    assert dcn.out_size(2, 5, 1, 0, 1) <= 0   # window larger than the padded map
+
+
+def fwd(lib, ptrs=(0x1000, 0x2000, 0x3000, 0x4000), N=1, H=8, W=8, G=2, Cg=8, K=3, s=1, p=1, d=1,
+        alpha=1.0, softmax=0, dtype=0):
+    vp = [ctypes.c_void_p(x) if x else None for x in ptrs]
+    return lib.dcn_core_forward(*vp, N, H, W, G, Cg, K, s, p, d, alpha, softmax, dtype, None)
+
+
+def bwd(lib, N=1, H=8, W=8, G=2, Cg=8, K=3, s=1, p=1, d=1, alpha=1.0, softmax=0, dtype=0, null=False):
+    vp = [None if null else ctypes.c_void_p(0x1000 * (i + 1)) for i in range(7)]
+    return lib.dcn_core_backward(*vp, N, H, W, G, Cg, K, s, p, d, alpha, softmax, dtype, None)
+
+
+INVALID_FWD = [
+    dict(N=-1), dict(H=0), dict(W=-3), dict(G=0), dict(Cg=0), dict(K=0), dict(s=0), dict(d=0),
+    dict(p=-1), dict(dtype=3), dict(dtype=-1), dict(softmax=2), dict(alpha=float("nan")),
+    dict(alpha=float("inf")), dict(H=2, W=2, K=5, p=0),       # empty output grid
+    dict(ptrs=(0, 0x2000, 0x3000, 0x4000)), dict(ptrs=(0x1000, 0, 0x3000, 0x4000)),
+    dict(ptrs=(0x1000, 0x2000, 0, 0x4000)), dict(ptrs=(0x1000, 0x2000, 0x3000, 0)),
+    dict(ptrs=(0x1000, 0x2002, 0x3000, 0x4000), dtype=1),   # offset pair not 4-byte aligned (f16)
+    dict(ptrs=(0x1000, 0x2004, 0x3000, 0x4000), dtype=0),   # offset pair not 8-byte aligned (f32)
+    dict(ptrs=(0x1000, 0x2000, 0x3001, 0x4000), dtype=2),   # mask not element aligned
+    dict(ptrs=(0x1001, 0x2000, 0x3000, 0x4000), dtype=0),   # input not element aligned
+    dict(ptrs=(0x1000, 0x2000, 0x3000, 0x4003), dtype=0),   # output not element aligned
+]
+
+
+@pytest.mark.parametrize("kw", INVALID_FWD)
+def test_forward_rejects_invalid_arguments_on_host(kw):
+    assert fwd(dcn.load_library(), **kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(K=17, H=40, W=40, p=8), dict(N=1, H=40000, W=40000, G=1, Cg=8),
+                                dict(N=1, H=8, W=8, G=1 << 20, Cg=1 << 12)])
+def test_forward_unsupported_sizes(kw):
+    assert fwd(dcn.load_library(), **kw) == UNSUPPORTED
+
+
+def test_forward_empty_batch_is_noop():
+    lib = dcn.load_library()
+    assert fwd(lib, N=0) == OK
+    assert fwd(lib, N=0, ptrs=(0, 0, 0, 0)) == OK
+
+
+def test_backward_validation():
+    lib = dcn.load_library()
+    assert bwd(lib, dtype=1) == UNSUPPORTED
+    assert bwd(lib, dtype=2) == UNSUPPORTED
+    assert bwd(lib, K=0) == INVALID
+    assert bwd(lib, null=True) == INVALID
+    assert bwd(lib, N=0, null=True) == OK
+    assert bwd(lib, Cg=12) == UNSUPPORTED    # lanes per group would not be a power of two
+    assert bwd(lib, Cg=3) == UNSUPPORTED
+
+
+def test_status_strings():
+    lib = dcn.load_library()
+    for code, prefix in ((0, b"DCN_OK"), (1, b"DCN_ERR_INVALID_ARG"), (2, b"DCN_ERR_UNSUPPORTED"),
+                         (3, b"DCN_ERR_HIP"), (99, b"unknown")):
+        assert lib.dcn_status_string(code).startswith(prefix)
+
+
+def test_binding_rejects_bad_tensors_before_calling():
+    x = torch.zeros(1, 8, 8, 16)
+    off = torch.zeros(1, 8, 8, 2 * 9 * 2)
+    m = torch.zeros(1, 8, 8, 2 * 9)
+    with pytest.raises(ValueError):
+        dcn.forward(x, off, m, group=2)                 # CPU tensors
+    with pytest.raises(ValueError):
+        dcn.forward(x, off[..., :-1], m, group=2)        # wrong offset shape
+    with pytest.raises(ValueError):
+        dcn.forward(x, off, m, group=3)                  # channels not divisible
+    with pytest.raises(ValueError):
+        dcn.forward(x, off, m, group=2, kernel_size=9, pad=0)   # empty grid
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        dcn.load_library(str(tmp_path / "nope.so"))

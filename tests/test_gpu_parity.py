@@ -1,0 +1,280 @@
+"""GPU parity: the HIP path (through the C ABI) against the binary64 oracle.
+
+Every workload of the benchmark family is compared element by element at its
+full size (the oracle finishes each in seconds), plus a sweep of geometries,
+dtypes, channel counts and alignments that exercises every kernel variant,
+bit-exact invariants, edge cases and the backward pass.  Tolerances are the
+ones tests/tolerance.py derives (1e-5 relative for fp32, 2e-2 for fp16/bf16,
+with a binary32 summation floor where terms cancel).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import deformable_convolution_core_amd as dcn
+import oracle
+from deformable_convolution_core_amd import inputs
+from tests import tolerance
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(autouse=True)
+def announce(request):
+    print(f"\n[gpu-case] {request.node.nodeid}", file=sys.stderr, flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+def cfg_of(w):
+    return dict(kernel_size=w.K, stride=w.stride, pad=w.pad, dilation=w.dilation,
+                offset_scale=w.offset_scale, softmax=w.softmax, group=w.G)
+
+
+def oracle_fwd(t, w):
+    return oracle.forward(inputs.to_f64(t["input"]), inputs.to_f64(t["offset"]), inputs.to_f64(t["mask"]),
+                          K=w.K, stride=w.stride, pad=w.pad, dilation=w.dilation,
+                          offset_scale=w.offset_scale, softmax=w.softmax, group=w.G,
+                          coord_mode=oracle.COORD_BINARY32)
+
+
+def gpu_fwd(t, w):
+    d = {k: v.to(DEV) for k, v in t.items()}
+    return dcn.forward(d["input"], d["offset"], d["mask"], **cfg_of(w))
+
+
+def check_forward(w, t=None):
+    t = t if t is not None else inputs.make(w, with_grad=False)
+    out = gpu_fwd(t, w)
+    torch.cuda.synchronize()
+    ref, S = oracle_fwd(t, w)
+    st = tolerance.compare(out.float().cpu().numpy(), ref, S, 4 * w.P, w.dtype)
+    assert st["ok"], (w.name, st)
+    return st
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_workload_forward_full_size(name):
+    check_forward(inputs.WORKLOADS[name])
+
+
+def test_forward_is_deterministic():
+    w = inputs.scaled(inputs.WORKLOADS["c3a_dcnv4_bf16_56"], N=4)
+    t = {k: v.to(DEV) for k, v in inputs.make(w).items()}
+    a = dcn.forward(t["input"], t["offset"], t["mask"], **cfg_of(w))
+    b = dcn.forward(t["input"], t["offset"], t["mask"], **cfg_of(w))
+    assert torch.equal(a, b)
+
+
+SWEEP = [  # name, N, H, W, G, Cg, K, stride, pad, dil, alpha, softmax, dtype
+    ("k1", 2, 9, 13, 3, 4, 1, 1, 0, 1, 1.0, False, "f32"),
+    ("k2_even", 1, 10, 7, 2, 8, 2, 1, 1, 1, 1.0, True, "bf16"),
+    ("k5_runtime", 2, 11, 9, 2, 16, 5, 1, 2, 1, 0.7, True, "f16"),
+    ("k3_s2_d2", 1, 17, 15, 4, 8, 3, 2, 2, 2, 1.3, False, "f32"),
+    ("k3_s3_pad0", 2, 16, 19, 1, 32, 3, 3, 0, 1, 0.5, True, "bf16"),
+    ("cg1_f16", 1, 12, 12, 8, 1, 3, 1, 1, 1, 1.0, False, "f16"),
+    ("cg1_f32", 1, 12, 12, 8, 1, 3, 1, 1, 1, 1.0, True, "f32"),
+    ("cg2_bf16", 3, 9, 9, 5, 2, 3, 1, 1, 1, 1.0, True, "bf16"),
+    ("cg3_odd", 2, 8, 11, 3, 3, 3, 1, 1, 1, 1.0, False, "bf16"),
+    ("cg6_f32", 1, 7, 9, 2, 6, 3, 2, 1, 1, 1.0, True, "f32"),
+    ("cg12_f16", 1, 9, 8, 2, 12, 3, 1, 1, 1, 1.0, False, "f16"),
+    ("cg24_bf16", 2, 6, 10, 2, 24, 3, 1, 1, 1, 1.0, True, "bf16"),
+    ("cg64_f32", 1, 8, 8, 2, 64, 3, 1, 1, 1, 1.0, False, "f32"),
+    ("cg64_bf16", 1, 9, 7, 3, 64, 3, 1, 1, 1, 1.0, True, "bf16"),
+    ("ragged_tail", 3, 5, 7, 3, 8, 3, 1, 1, 1, 1.0, False, "f16"),
+    ("wide_map", 1, 3, 130, 2, 16, 3, 1, 1, 1, 1.0, True, "bf16"),
+    ("tall_map", 1, 131, 3, 2, 16, 3, 1, 1, 1, 1.0, False, "f32"),
+    ("one_pixel", 1, 1, 1, 2, 16, 3, 1, 1, 1, 1.0, True, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: c[0])
+def test_geometry_sweep(case):
+    name, N, H, W, G, Cg, K, s, p, d, a, sm, dt = case
+    Ho, Wo = oracle.out_size(H, K, s, p, d), oracle.out_size(W, K, s, p, d)
+    w = inputs.Workload(name=name, N=N, H=H, W=W, G=G, Cg=Cg, Ho=Ho, Wo=Wo, K=K, stride=s, pad=p,
+                        dilation=d, offset_scale=a, softmax=sm, dtype=dt, offset_sigma=2.5,
+                        mask_sigma=1.0 if sm else 0.5, seed_base=90000 + 17 * len(name))
+    check_forward(w)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_misaligned_tensors_use_narrower_loads(dtype):
+    """Views whose data starts one element into a buffer: the library picks
+    a narrower gather and must still match."""
+    w = inputs.Workload(name="misaligned", N=2, H=9, W=10, G=2, Cg=16, Ho=9, Wo=10,
+                        dtype=dtype, softmax=True, mask_sigma=1.0, seed_base=91000)
+    t = inputs.make(w)
+    td = {}
+    for k, v in t.items():
+        buf = torch.empty(v.numel() + 2, dtype=v.dtype, device=DEV)
+        # keep offset pairs element-pair aligned, shift the others by one element
+        sh = 2 if k == "offset" else 1
+        td[k] = buf[sh:sh + v.numel()].view(v.shape).copy_(v.to(DEV))
+    outbuf = torch.empty(int(np.prod(w.shapes()["output"])) + 1, dtype=td["input"].dtype, device=DEV)
+    out = outbuf[1:].view(w.shapes()["output"])
+    dcn.forward(td["input"], td["offset"], td["mask"], out=out, **cfg_of(w))
+    torch.cuda.synchronize()
+    ref, S = oracle_fwd(t, w)
+    st = tolerance.compare(out.float().cpu().numpy(), ref, S, 4 * w.P, dtype)
+    assert st["ok"], st
+
+
+def test_empty_batch():
+    x = torch.zeros(0, 8, 8, 16, device=DEV, dtype=torch.bfloat16)
+    off = torch.zeros(0, 8, 8, 2 * 18, device=DEV, dtype=torch.bfloat16)
+    m = torch.zeros(0, 8, 8, 2 * 9, device=DEV, dtype=torch.bfloat16)
+    out = dcn.forward(x, off, m, group=2)
+    assert out.shape == (0, 8, 8, 16)
+
+
+# ---------------------------------------------------------------- invariants
+def identity_inputs(N, H, W, G, Cg, dtype, softmax, seed):
+    x = inputs.normal((N, H, W, G * Cg), seed, 1.0, dtype)
+    off = torch.zeros(N, H, W, G * 18, dtype=inputs.DTYPES[dtype])
+    m = torch.full((N, H, W, G, 9), -1e4 if softmax else 0.0)
+    m[..., 4] = 0.0 if softmax else 1.0
+    return x, off, m.reshape(N, H, W, G * 9).to(inputs.DTYPES[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("softmax", [False, True])
+def test_identity_bit_exact(dtype, softmax):
+    x, off, m = identity_inputs(2, 13, 11, 4, 16, dtype, softmax, 5)
+    out = dcn.forward(x.to(DEV), off.to(DEV), m.to(DEV), group=4, softmax=softmax)
+    assert torch.equal(out.cpu(), x)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_integer_offsets_are_exact_shifts(dtype):
+    N, H, W, G, Cg = 1, 12, 10, 2, 8
+    x = inputs.normal((N, H, W, G * Cg), 6, 1.0, dtype)
+    for (p, dx, dy) in [(4, 1, 0), (4, -2, 3), (0, 0, 0), (8, -3, -1), (5, 4, -4)]:
+        i, j = divmod(p, 3)
+        off = torch.zeros(N, H, W, G, 9, 2)
+        off[..., p, 0] = dx
+        off[..., p, 1] = dy
+        m = torch.zeros(N, H, W, G, 9)
+        m[..., p] = 1.0
+        T = inputs.DTYPES[dtype]
+        out = dcn.forward(x.to(DEV), off.reshape(N, H, W, -1).to(T).to(DEV),
+                          m.reshape(N, H, W, -1).to(T).to(DEV), group=G).cpu()
+        exp = torch.zeros_like(x)
+        sx, sy = (i - 1) + dx, (j - 1) + dy
+        ys = slice(max(0, -sy), min(H, H - sy))
+        xs = slice(max(0, -sx), min(W, W - sx))
+        exp[:, ys, xs] = x[:, ys.start + sy:ys.stop + sy, xs.start + sx:xs.stop + sx]
+        assert torch.equal(out, exp), (p, dx, dy)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_far_outside_and_nan_offsets_give_zero(dtype):
+    N, H, W, G, Cg = 1, 6, 7, 2, 16
+    T = inputs.DTYPES[dtype]
+    x = inputs.normal((N, H, W, G * Cg), 7, 1.0, dtype).to(DEV)
+    m = inputs.normal((N, H, W, G * 9), 8, 1.0, dtype).to(DEV)
+    for big in (1e4, -1e4, float("inf"), float("-inf"), float("nan")):
+        off = torch.full((N, H, W, G * 18), big, dtype=T, device=DEV)
+        for sm in (False, True):
+            out = dcn.forward(x, off, m, group=G, softmax=sm)
+            assert torch.equal(out, torch.zeros_like(out)), (big, sm)
+
+
+def test_nan_input_does_not_leak_to_other_pixels():
+    """A NaN at one pixel reaches only outputs whose sample has a corner on
+    that pixel; an off-map corner whose address would wrap onto it reads 0."""
+    N, H, W, G, Cg = 1, 10, 10, 1, 16
+    x = torch.randn(N, H, W, G * Cg, generator=torch.Generator().manual_seed(1))
+    x[0, 0, 9] = float("nan")                   # right end of row 0
+    off = torch.zeros(N, H, W, 2)               # K = 1: one sample per pixel
+    off[..., 0] = -0.5                          # half a pixel left of each pixel
+    m = torch.ones(N, H, W, 1)
+    out = dcn.forward(x.to(DEV), off.to(DEV), m.to(DEV), kernel_size=1, pad=0, group=1).cpu()
+    # only (0, 9) samples x = 8.5 between pixels 8 and 9 of row 0; (1, 0) samples
+    # x = -0.5, whose left corner is off the map (its flat address is pixel (0, 9))
+    nan_pix = torch.isnan(out).any(-1)
+    assert nan_pix[0, 0, 9] and nan_pix.sum() == 1
+    assert torch.equal(out[0, 1, 0], (0.5 * x[0, 1, 0]).float())
+
+
+# ---------------------------------------------------------------- backward
+def oracle_bwd(t, w):
+    return oracle.backward(inputs.to_f64(t["input"]), inputs.to_f64(t["offset"]),
+                           inputs.to_f64(t["mask"]), inputs.to_f64(t["grad_out"]),
+                           K=w.K, stride=w.stride, pad=w.pad, dilation=w.dilation,
+                           offset_scale=w.offset_scale, softmax=w.softmax, group=w.G,
+                           coord_mode=oracle.COORD_BINARY32)
+
+
+def check_backward(w):
+    t = inputs.make(w, with_grad=True)
+    d = {k: v.to(DEV) for k, v in t.items()}
+    gi, goff, gm = dcn.backward(d["input"], d["offset"], d["mask"], d["grad_out"], **cfg_of(w))
+    torch.cuda.synchronize()
+    r = oracle_bwd(t, w)
+    Cg, P = w.Cg, w.P
+    stats = {}
+    for key, got, S, n in (("grad_input", gi, r["gi_abs"], r["gi_cnt"]),
+                           ("grad_offset", goff, r["goff_abs"], 4 * Cg),
+                           ("grad_mask", gm, r["gmask_abs"], 4 * Cg * (P + 1) if w.softmax else 4 * Cg)):
+        st = tolerance.compare(got.cpu().numpy().reshape(r[key].shape), r[key], S, n, "f32")
+        assert st["ok"], (w.name, key, st)
+        stats[key] = st
+    return stats
+
+
+def test_workload_backward_full_size():
+    check_backward(inputs.WORKLOADS["c5_dcnv4_f32_56_fwdbwd"])
+
+
+BWD_SWEEP = [  # name, N, H, W, G, Cg, K, stride, pad, dil, alpha, softmax
+    ("softmax_k3", 2, 9, 11, 2, 16, 3, 1, 1, 1, 1.0, True),
+    ("cg4_L1", 1, 8, 8, 3, 4, 3, 1, 1, 1, 1.0, False),
+    ("cg8_s2_d2", 1, 13, 12, 2, 8, 3, 2, 2, 2, 0.75, True),
+    ("cg32", 1, 7, 9, 2, 32, 3, 1, 1, 1, 1.0, False),
+    ("cg64_L16", 1, 6, 6, 1, 64, 3, 1, 1, 1, 1.0, True),
+    ("cg1_scalar", 2, 8, 9, 4, 1, 3, 1, 1, 1, 1.0, False),
+    ("cg2_scalar", 1, 9, 8, 3, 2, 3, 1, 1, 1, 1.3, True),
+    ("k5_runtime", 1, 10, 10, 2, 16, 5, 1, 2, 1, 1.0, True),
+    ("k1_runtime", 1, 9, 9, 2, 8, 1, 1, 0, 1, 1.0, False),
+    ("ragged", 3, 5, 7, 3, 16, 3, 1, 1, 1, 1.0, False),
+]
+
+
+@pytest.mark.parametrize("case", BWD_SWEEP, ids=lambda c: c[0])
+def test_backward_sweep(case):
+    name, N, H, W, G, Cg, K, s, p, d, a, sm = case
+    Ho, Wo = oracle.out_size(H, K, s, p, d), oracle.out_size(W, K, s, p, d)
+    w = inputs.Workload(name=name, N=N, H=H, W=W, G=G, Cg=Cg, Ho=Ho, Wo=Wo, K=K, stride=s, pad=p,
+                        dilation=d, offset_scale=a, softmax=sm, dtype="f32", offset_sigma=2.0,
+                        mask_sigma=1.0 if sm else 0.5, seed_base=92000 + 31 * len(name), backward=True)
+    check_backward(w)
+
+
+def test_backward_repeat_within_tolerance_and_autograd():
+    w = inputs.scaled(inputs.WORKLOADS["c5_dcnv4_f32_56_fwdbwd"], N=2)
+    t = {k: v.to(DEV) for k, v in inputs.make(w, with_grad=True).items()}
+    a = dcn.backward(t["input"], t["offset"], t["mask"], t["grad_out"], **cfg_of(w))
+    b = dcn.backward(t["input"], t["offset"], t["mask"], t["grad_out"], **cfg_of(w))
+    for x, y in zip(a, b):
+        assert torch.allclose(x, y, rtol=1e-5, atol=1e-5)
+    xi = t["input"].clone().requires_grad_(True)
+    oi = t["offset"].clone().requires_grad_(True)
+    mi = t["mask"].clone().requires_grad_(True)
+    out = dcn.dcn_core(xi, oi, mi, w.K, w.stride, w.pad, w.dilation, w.offset_scale, w.softmax, w.G)
+    out.backward(t["grad_out"])
+    for got, want in zip((xi.grad, oi.grad, mi.grad), a):
+        assert torch.allclose(got, want, rtol=1e-5, atol=1e-5)
+
+
+def test_backward_unsupported_group_width_raises():
+    x = torch.zeros(1, 4, 4, 12, device=DEV)
+    off = torch.zeros(1, 4, 4, 18, device=DEV)
+    m = torch.zeros(1, 4, 4, 9, device=DEV)
+    with pytest.raises(dcn.DCNError) as e:
+        dcn.backward(x, off, m, torch.zeros_like(x), group=1)
+    assert e.value.status == 2
