@@ -200,6 +200,30 @@ def traffic_record(name, min_bytes):
     return None if e is None else e.get("hbm_bytes_per_launch")
 
 
+def profile_mode(w, args):
+    """Launch one workload eagerly `steps` times over rotating buffers, then
+    (optionally) copy a buffer of known size `steps` times: a target for
+    rocprofv3 counter passes (per-dispatch counters of a plain copy calibrate
+    FETCH_SIZE / WRITE_SIZE)."""
+    sets = rotating_sets(w, args.backward)
+    launch = launcher(w, args.backward)
+    h = torch.cuda.current_stream().cuda_stream
+    for i in range(args.warmup + args.steps):
+        launch(sets[i % len(sets)], h)
+    torch.cuda.synchronize()
+    log(f"profiled {args.warmup + args.steps} launches of {w.name} "
+        f"({'backward' if args.backward else 'forward'}), rotating sets {len(sets)}")
+    if args.copy_mb:
+        n = args.copy_mb * (1 << 20) // 4
+        bufs = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(4)]
+        for b in bufs:
+            b.fill_(1.0)
+        for i in range(args.steps):
+            bufs[(2 * i + 1) % 4].copy_(bufs[(2 * i) % 4])
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_mb} MiB x {args.steps} (read {args.copy_mb} MiB + write {args.copy_mb} MiB each)")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +232,11 @@ def main():
     ap.add_argument("--workload", default=inputs.HEADLINE, choices=list(inputs.WORKLOADS))
     ap.add_argument("--quick", action="store_true", help="headline only (no sweep, no CPU leg)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="for counter runs: eager launches of --workload only (plus --copy-mb), no JSON")
+    ap.add_argument("--backward", action="store_true", help="with --profile: launch the backward")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="with --profile: also run plain device copies of this many MB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -221,6 +250,9 @@ def main():
     torch.cuda.set_device(0)
 
     w = inputs.WORKLOADS[args.workload]
+    if args.profile:
+        profile_mode(w, args)
+        return
     log(f"headline {w.name}: steps={args.steps} warmup={args.warmup}")
     head = forward_record(w, args.steps, args.warmup)
     log(f"headline {head['us']} us, {head['GBps']} GB/s")

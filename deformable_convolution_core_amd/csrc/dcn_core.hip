@@ -7,6 +7,7 @@
 // gather width, channels per lane, K = 3 or runtime K), chosen from the
 // sizes and pointer alignment of the call; there is no other code path.
 
+#include <math.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
@@ -17,6 +18,13 @@
 using namespace dcn;
 
 namespace {
+
+#ifndef DCN_USE_TILES
+#define DCN_USE_TILES 1       // stage input tiles in LDS where the shape allows
+#endif
+#ifndef DCN_WIDE_ROWS
+#define DCN_WIDE_ROWS 1   // one lane gathers a 32-byte group row as two 16-byte loads
+#endif
 
 constexpr int64_t kMaxImageBytes = (1ll << 31) - 4096;   // one image must fit a buffer resource
 
@@ -102,17 +110,106 @@ int forward_variant(const FwdArgs& base, const Call& c, hipStream_t st)
     return launch_status();
 }
 
+// ---------------------------------------------------------------- tiled path
+#ifndef DCN_TILE_REACH
+#define DCN_TILE_REACH 5      // offsets up to this many pixels stay inside the staged region
+#endif
+#ifndef DCN_TILE_FORCE_TW
+#define DCN_TILE_FORCE_TW 0   // nonzero: fixed tile width (tuning builds)
+#endif
+#ifndef DCN_TILE_FORCE_TH
+#define DCN_TILE_FORCE_TH 0
+#endif
+constexpr int64_t kMaxTileLds = 96 * 1024;
+
+struct TilePlan {
+    TileGeo tg;
+    int threads;
+    uint32_t lds_bytes;
+    uint64_t blocks;
+};
+
+// The tiled kernel applies when a lane's 32 bytes never straddle two groups
+// and 128-byte slabs tile the channel row: Cg*b in {32, 64, 128}, C*b a
+// multiple of 128, 16-byte aligned input and output.  Among tile shapes with
+// at most 128 pixels it picks the cheapest by a simple cost model: lane slots
+// issued (idle lanes of ragged tiles count) plus region chunks staged.
+bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan)
+{
+    const int eb = c.ebytes, rowg = c.Cg * eb, rowc = c.G * c.Cg * eb;
+    if (!(rowg == 32 || rowg == 64 || rowg == 128) || rowc % 128 != 0) return false;
+    if (!aligned(in, 16) || !aligned(out, 16)) return false;
+    if (c.stride > 4 || c.K > 7) return false;
+    const float a = c.alpha < 0 ? -c.alpha : c.alpha;
+    const int c0 = c.dil * (c.K - 1) / 2;
+    const int span = c0 > c.dil * (c.K - 1) - c0 ? c0 : c.dil * (c.K - 1) - c0;
+    const int ml = (int)ceilf(a * (float)span + a * (float)DCN_TILE_REACH);
+    const uint32_t slabs = (uint32_t)(rowc / 128);
+    double best = -1.0;
+    for (int nt = 256; nt <= 512; nt *= 2) {
+        const int maxpx = nt / 4;
+        for (int tw = 1; tw <= 32 && tw <= c.Wo; ++tw) {
+            int th = maxpx / tw;
+            if (th > c.Ho) th = c.Ho;
+            if (th < 1) continue;
+            if (DCN_TILE_FORCE_TW && (tw != DCN_TILE_FORCE_TW || th != DCN_TILE_FORCE_TH)) continue;
+            const int rh = (th - 1) * c.stride + 2 * ml + 2, rw = (tw - 1) * c.stride + 2 * ml + 2;
+            const int64_t lds = (int64_t)rh * rw * 128;
+            if (lds > kMaxTileLds) continue;
+            const uint64_t tx = (uint64_t)((c.Wo + tw - 1) / tw), ty = (uint64_t)((c.Ho + th - 1) / th);
+            const uint64_t tiles = tx * ty * slabs * (uint64_t)c.N;
+            const int lanes = ((th * tw * 4 + 63) / 64) * 64;
+            // LDS per block bounds the blocks a CU holds; fewer resident waves cost latency hiding
+            const int per_cu = (int)(160 * 1024 / lds) < 2048 / nt ? (int)(160 * 1024 / lds) : 2048 / nt;
+            const double occ_penalty = per_cu * nt / 64 >= 12 ? 1.0 : 1.0 + 0.04 * (12 - per_cu * nt / 64);
+            const double cost = (double)tiles * ((double)lanes * 900.0 * occ_penalty + (double)rh * rw * 8 * 3.0);
+            if (best < 0 || cost < best) {
+                best = cost;
+                plan.tg = TileGeo{th, tw, rh, rw, ml, 0, (uint32_t)tx, (uint32_t)ty, slabs};
+                plan.threads = nt;
+                plan.lds_bytes = (uint32_t)lds;
+                plan.blocks = tiles;
+            }
+        }
+    }
+    if (best < 0 || plan.blocks >= (1ull << 31)) return false;
+    int gs = 0;
+    while ((32 << gs) < rowg) ++gs;
+    plan.tg.gshift = gs;
+    return true;
+}
+
+template <typename T, int KT, int NT>
+int launch_tiled(const FwdArgs& a, const TilePlan& pl, hipStream_t st)
+{
+    hipLaunchKernelGGL((dcn_forward_tiled<T, KT, NT>), dim3((uint32_t)pl.blocks), dim3(NT), pl.lds_bytes, st,
+                       a, pl.tg);
+    return launch_status();
+}
+
+template <typename T>
+int forward_tiled(const FwdArgs& base, const Call& c, const TilePlan& pl, hipStream_t st)
+{
+    FwdArgs a = base;
+    a.geo = make_geometry(c, 32 / (int)sizeof(T));
+    if (pl.threads == 512)
+        return c.K == 3 ? launch_tiled<T, 3, 512>(a, pl, st) : launch_tiled<T, 0, 512>(a, pl, st);
+    return c.K == 3 ? launch_tiled<T, 3, 256>(a, pl, st) : launch_tiled<T, 0, 256>(a, pl, st);
+}
+
 // Widest gather whose size divides a group's row and whose alignment the
 // input and output pointers allow; two 16-byte loads per corner when a
 // group row holds 32 bytes or more.
 template <typename T>
 int forward_typed(const FwdArgs& a, const Call& c, hipStream_t st)
 {
+    TilePlan pl;
+    if (DCN_USE_TILES && plan_tiles(c, a.input, a.output, pl)) return forward_tiled<T>(a, c, pl, st);
     const int row = c.Cg * (int)sizeof(T);
     auto ok = [&](int lb) {
         return row % lb == 0 && aligned(a.input, lb) && aligned(a.output, lb);
     };
-    if (ok(16) && row % 32 == 0) return forward_variant<T, 16, 2>(a, c, st);
+    if (DCN_WIDE_ROWS && ok(16) && row % 32 == 0) return forward_variant<T, 16, 2>(a, c, st);
     if (ok(16)) return forward_variant<T, 16, 1>(a, c, st);
     if (ok(8)) return forward_variant<T, 8, 1>(a, c, st);
     if (ok(4)) return forward_variant<T, 4, 1>(a, c, st);

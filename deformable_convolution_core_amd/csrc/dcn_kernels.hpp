@@ -345,6 +345,193 @@ __global__ __launch_bounds__(kBlock) void dcn_forward_kernel(FwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Tiled forward.  A workgroup owns one output tile (TH x TW pixels) of one
+// image and one 128-byte channel slab (the groups whose channels fall in
+// that slab).  It first stages the input region those samples can reach --
+// the tile's sampling centres widened by a margin ML on every side -- into
+// LDS, reading each 128-byte pixel slab once with coalesced 16-byte loads;
+// pixels outside the image are stored as zeros, which is exactly the zero
+// padding of the definition.  Every lane then owns 32 bytes of channels of
+// one output pixel (4 lanes per pixel slab) and reads its four bilinear
+// corners from LDS.  A sample whose offset carries it outside the staged
+// region (or a NaN coordinate) takes the global gather path instead, with
+// the same off-map rules as the untiled kernel.
+//
+// LDS layout: region[ry][rx][128 bytes], rows of RW pixels.  Every pixel
+// slab starts on bank 0, so a 16-byte read is conflict free when the 8 lanes
+// served together read 8 different 16-byte slots of their (different)
+// pixels.  Lanes 4k..4k+3 hold slots {0,2,4,6} of their first read; pixels
+// with odd index read their two 16-byte halves in the opposite order, so the
+// other four lanes of the 8 hold slots {1,3,5,7}.  The swap is undone when
+// the result is stored.
+struct TileGeo {
+    int TH, TW;              // output tile, pixels
+    int RH, RW;              // staged input region, pixels
+    int ML;                  // region origin = first tile centre - ML (both axes)
+    int gshift;              // log2(Cg * elem_bytes / 32): lanes per group = 1 << gshift
+    uint32_t tiles_x, tiles_y, slabs;
+};
+
+#ifndef DCN_TILE_UNROLL
+#define DCN_TILE_UNROLL 1
+#endif
+#define DCN_PRAGMA(x) _Pragma(#x)
+#define DCN_UNROLL(n) DCN_PRAGMA(unroll n)
+#ifndef DCN_TILE_WAVES_PER_EU
+#define DCN_TILE_WAVES_PER_EU 4   // register budget 512/4 = 128 VGPRs per lane
+#endif
+
+template <typename T, int KT, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DCN_TILE_WAVES_PER_EU)))
+void dcn_forward_tiled(FwdArgs a, TileGeo tg)
+{
+    constexpr int EB = Elem<T>::bytes;
+    constexpr int CPL = 32 / EB;        // channels per lane
+    constexpr int EPR = 16 / EB;        // elements per 16-byte read
+    extern __shared__ uint4 region[];
+    const Geometry& G = a.geo;
+
+    uint32_t rest = xcd_remap(blockIdx.x, gridDim.x);
+    const uint32_t tile_x = rest % tg.tiles_x;
+    rest /= tg.tiles_x;
+    const uint32_t tile_y = rest % tg.tiles_y;
+    rest /= tg.tiles_y;
+    const uint32_t slab = rest % tg.slabs;
+    const uint32_t n = rest / tg.slabs;
+    const int ho0 = (int)tile_y * tg.TH, wo0 = (int)tile_x * tg.TW;
+    const int y_lo = ho0 * G.stride - G.pad + G.c0 - tg.ML;
+    const int x_lo = wo0 * G.stride - G.pad + G.c0 - tg.ML;
+    const int t = threadIdx.x;
+    const int RW8 = tg.RW * 8;
+
+    const char* in_img = (const char*)a.input + (size_t)n * G.in_image_bytes;
+    const __amdgpu_buffer_rsrc_t rin = image_rsrc(in_img, G.in_image_bytes);
+    const uint32_t slab_bytes = slab * 128u;
+
+    // ---- stage the region: lane t loads 16-byte chunk e of every region row
+    for (int e = t; e < RW8; e += NT) {
+        const int gx = x_lo + (e >> 3);
+        const bool col_ok = (uint32_t)gx < (uint32_t)G.W;
+        const uint32_t col_off = (uint32_t)gx * G.in_row_bytes + slab_bytes + (uint32_t)(e & 7) * 16u;
+        for (int ry = 0; ry < tg.RH; ++ry) {
+            const int gy = y_lo + ry;
+            const bool ok = col_ok && (uint32_t)gy < (uint32_t)G.H;
+            const uint32_t off = ok ? (uint32_t)gy * G.in_line_bytes + col_off : kOOB;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rin, off, 0, 0);
+            region[ry * RW8 + e] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+    }
+    __syncthreads();
+
+    // ---- one lane = 32 bytes of channels of one output pixel
+    const int p = t >> 2, sub = t & 3;
+    const int py = p / tg.TW, px = p - py * tg.TW;
+    const int ho = ho0 + py, wo = wo0 + px;
+    if (p >= tg.TH * tg.TW || ho >= G.Ho || wo >= G.Wo) return;   // after the barrier
+
+    const int swp = p & 1;                       // read order of the two halves
+    const uint32_t lane_chunk = (uint32_t)(sub * 2 + swp);          // first 16-byte slot
+    const uint32_t g = slab * (4u >> tg.gshift) + ((uint32_t)sub >> tg.gshift);
+    const size_t pix_global = ((size_t)n * G.Ho + ho) * G.Wo + wo;
+    const size_t pg = pix_global * G.groups + g;
+    const T* off = (const T*)a.offset + pg * G.P * 2;
+    const T* mk = (const T*)a.mask + pg * G.P;
+    const float bx = (float)(wo * G.stride - G.pad + G.c0);
+    const float by = (float)(ho * G.stride - G.pad + G.c0);
+    const float xlo_f = (float)x_lo, xhi_f = (float)(x_lo + tg.RW - 1);
+    const float ylo_f = (float)y_lo, yhi_f = (float)(y_lo + tg.RH - 1);
+    // byte offset of this lane's first half inside a pixel row (global path)
+    const uint32_t gl_first = slab_bytes + (uint32_t)sub * 32u + (uint32_t)swp * 16u;
+    const uint32_t gl_second = slab_bytes + (uint32_t)sub * 32u + (uint32_t)(swp ^ 1) * 16u;
+
+    float acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+
+    auto point = [&](int i, int j, float m, float2 d) {
+        const float tx = (float)(i * G.dil - G.c0) + d.x;
+        const float ty = (float)(j * G.dil - G.c0) + d.y;
+        const float x = fmaf(G.alpha, tx, bx);
+        const float y = fmaf(G.alpha, ty, by);
+        float fx = floorf(x), fy = floorf(y);
+        float lx = x - fx, ly = y - fy;
+        float mm = m;
+        uint32_t raw[4][8];
+        if (x >= xlo_f && x < xhi_f && y >= ylo_f && y < yhi_f) {
+            const int base = (((int)fy - y_lo) * tg.RW + ((int)fx - x_lo)) * 8 + (int)lane_chunk;
+            const int cofs[4] = {0, 8, RW8, RW8 + 8};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint4 v0 = region[base + cofs[k]];
+                const uint4 v1 = region[base + cofs[k] + 1 - 2 * swp];
+                raw[k][0] = v0.x; raw[k][1] = v0.y; raw[k][2] = v0.z; raw[k][3] = v0.w;
+                raw[k][4] = v1.x; raw[k][5] = v1.y; raw[k][6] = v1.z; raw[k][7] = v1.w;
+            }
+        } else {
+            const bool inmap = x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H;
+            if (!inmap) { fx = -2.0f; fy = -2.0f; lx = 0.f; ly = 0.f; mm = 0.f; }
+            const int x0 = (int)fx, y0 = (int)fy;
+            const bool vx0 = (uint32_t)x0 < (uint32_t)G.W, vx1 = (uint32_t)(x0 + 1) < (uint32_t)G.W;
+            const bool vy0 = (uint32_t)y0 < (uint32_t)G.H, vy1 = (uint32_t)(y0 + 1) < (uint32_t)G.H;
+            const bool vk[4] = {vy0 && vx0, vy0 && vx1, vy1 && vx0, vy1 && vx1};
+            const uint32_t a00 = (uint32_t)y0 * G.in_line_bytes + (uint32_t)x0 * G.in_row_bytes;
+            const uint32_t ck[4] = {0u, G.in_row_bytes, G.in_line_bytes, G.in_line_bytes + G.in_row_bytes};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t o0 = vk[k] ? a00 + ck[k] + gl_first : kOOB;
+                const uint32_t o1 = vk[k] ? a00 + ck[k] + gl_second : kOOB;
+                const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rin, o0, 0, 0);
+                const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rin, o1, 0, 0);
+                raw[k][0] = v0[0]; raw[k][1] = v0[1]; raw[k][2] = v0[2]; raw[k][3] = v0[3];
+                raw[k][4] = v1[0]; raw[k][5] = v1[1]; raw[k][6] = v1[2]; raw[k][7] = v1[3];
+            }
+        }
+        // bilinear weights with the modulation folded in
+        const float mly = mm * ly, mhy = mm - mly;
+        const float w01 = mhy * lx, w11 = mly * lx;
+        const float w[4] = {mhy - w01, w01, mly - w11, w11};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                if constexpr (EB == 4) {
+                    acc[q] = fmaf(w[k], __uint_as_float(raw[k][q]), acc[q]);
+                } else {
+                    acc[2 * q] = fmaf(w[k], Elem<T>::widen(raw[k][q] & 0xffffu), acc[2 * q]);
+                    acc[2 * q + 1] = fmaf(w[k], Elem<T>::widen(raw[k][q] >> 16), acc[2 * q + 1]);
+                }
+            }
+        }
+    };
+
+    // Points are visited in a rolled loop (unrolled DCN_TILE_UNROLL times):
+    // fully unrolled, the compiler hoists every point's corner reads and
+    // runs out of registers.  Mask and offsets are re-read per point (L1).
+    const int K = KT > 0 ? KT : G.K;
+    const int P = K * K;
+    float mx = 0.f, inv = 1.f;
+    if (G.softmax) {
+        mx = ld1(mk);
+        for (int q = 1; q < P; ++q) mx = fmaxf(mx, ld1(mk + q));
+        float sum = 0.f;
+        for (int q = 0; q < P; ++q) sum += __expf(ld1(mk + q) - mx);
+        inv = 1.0f / sum;
+    }
+    DCN_UNROLL(DCN_TILE_UNROLL)
+    for (int q = 0; q < P; ++q) {
+        const int i = q / K, j = q - i * K;
+        float m = ld1(mk + q);
+        if (G.softmax) m = __expf(m - mx) * inv;
+        point(i, j, m, ld2(off + 2 * q));
+    }
+
+    // store the lane's 32 bytes, undoing the half swap
+    char* out = (char*)a.output + (pix_global * G.C) * EB + slab_bytes + (uint32_t)sub * 32u;
+    store<T, 16>(out + swp * 16, &acc[0]);
+    store<T, 16>(out + (swp ^ 1) * 16, &acc[EPR]);
+}
+
+// ---------------------------------------------------------------------------
 // Backward (binary32).  Same lane mapping; L = Cg/CPL lanes per group, a
 // power of two.  Per point and corner k each lane forms
 // s_k = sum over its channels of g_c * f_kc; then

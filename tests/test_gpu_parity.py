@@ -89,7 +89,28 @@ SWEEP = [  # name, N, H, W, G, Cg, K, stride, pad, dil, alpha, softmax, dtype
     ("wide_map", 1, 3, 130, 2, 16, 3, 1, 1, 1, 1.0, True, "bf16"),
     ("tall_map", 1, 131, 3, 2, 16, 3, 1, 1, 1, 1.0, False, "f32"),
     ("one_pixel", 1, 1, 1, 2, 16, 3, 1, 1, 1, 1.0, True, "bf16"),
+    # shapes the LDS-tiled kernel takes (group rows of 32/64/128 bytes, channel
+    # rows a multiple of 128 bytes): ragged tiles, several slabs, stride and
+    # dilation, runtime K, and offsets that leave the staged region
+    ("tiled_f16_k5", 2, 19, 23, 4, 16, 5, 1, 2, 1, 0.8, True, "f16"),
+    ("tiled_bf16_s2_d2", 1, 33, 30, 8, 16, 3, 2, 1, 2, 1.2, False, "bf16"),
+    ("tiled_f32_cg32", 1, 17, 13, 4, 32, 3, 1, 1, 1, 1.0, True, "f32"),
+    ("tiled_f32_cg16", 2, 21, 18, 4, 16, 3, 1, 1, 1, 1.0, False, "f32"),
+    ("tiled_bf16_cg32", 1, 20, 9, 8, 32, 3, 1, 1, 1, 1.0, True, "bf16"),
+    ("tiled_bf16_cg64", 1, 11, 12, 2, 64, 3, 1, 1, 1, 1.0, False, "bf16"),
+    ("tiled_f16_k1", 1, 10, 37, 4, 16, 1, 1, 0, 1, 1.0, False, "f16"),
+    ("tiled_bf16_s3_pad0", 2, 26, 25, 4, 16, 3, 3, 0, 1, 1.0, True, "bf16"),
+    ("tiled_neg_alpha", 1, 16, 16, 4, 16, 3, 1, 1, 1, -0.9, False, "f16"),
 ]
+
+
+@pytest.mark.parametrize("sigma", [0.25, 6.0, 40.0])
+def test_tiled_offset_spread(sigma):
+    """Small offsets stay in the staged region; large ones take the global
+    gather fallback, very large ones fall off the map."""
+    w = inputs.Workload(name="spread", N=2, H=24, W=20, G=4, Cg=16, Ho=24, Wo=20, dtype="bf16",
+                        offset_sigma=sigma, mask_sigma=0.5, seed_base=93000 + int(sigma * 10))
+    check_forward(w)
 
 
 @pytest.mark.parametrize("case", SWEEP, ids=lambda c: c[0])
@@ -182,6 +203,24 @@ def test_far_outside_and_nan_offsets_give_zero(dtype):
         for sm in (False, True):
             out = dcn.forward(x, off, m, group=G, softmax=sm)
             assert torch.equal(out, torch.zeros_like(out)), (big, sm)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nan_input_does_not_leak_tiled(dtype):
+    """Same check on a shape the tiled kernel serves (channel row of 128
+    bytes or more): off-map corners read the staged zeros, not a wrapped
+    neighbour."""
+    N, H, W, G, Cg = 1, 12, 12, 4, 16
+    T = inputs.DTYPES[dtype]
+    x = torch.randn(N, H, W, G * Cg, generator=torch.Generator().manual_seed(2)).to(T)
+    x[0, 0, 11] = float("nan")
+    off = torch.zeros(N, H, W, G, 2)
+    off[..., 0] = -0.5
+    m = torch.ones(N, H, W, G)
+    out = dcn.forward(x.to(DEV), off.reshape(N, H, W, -1).to(T).to(DEV), m.reshape(N, H, W, -1).to(T).to(DEV),
+                      kernel_size=1, pad=0, group=G).cpu()
+    nan_pix = torch.isnan(out.float()).any(-1)
+    assert nan_pix[0, 0, 11] and nan_pix.sum() == 1
 
 
 def test_nan_input_does_not_leak_to_other_pixels():
