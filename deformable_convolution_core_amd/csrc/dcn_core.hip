@@ -139,7 +139,9 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan)
     const int eb = c.ebytes, rowg = c.Cg * eb, rowc = c.G * c.Cg * eb;
     if (!(rowg == 32 || rowg == 64 || rowg == 128) || rowc % 128 != 0) return false;
     if (!aligned(in, 16) || !aligned(out, 16)) return false;
-    if (c.stride > 4 || c.K > 7) return false;
+    if (c.stride > 4 || c.K * c.K > kMaxTiledTaps) return false;
+    const int64_t off_img = (int64_t)c.Ho * c.Wo * c.G * c.K * c.K * 2 * eb;
+    if (off_img >= (1ll << 31)) return false;
     const float a = c.alpha < 0 ? -c.alpha : c.alpha;
     const int c0 = c.dil * (c.K - 1) / 2;
     const int span = c0 > c.dil * (c.K - 1) - c0 ? c0 : c.dil * (c.K - 1) - c0;
@@ -176,15 +178,28 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan)
     int gs = 0;
     while ((32 << gs) < rowg) ++gs;
     plan.tg.gshift = gs;
+    plan.tg.off_image_bytes = (uint32_t)off_img;
+    plan.tg.mask_image_bytes = (uint32_t)(off_img / 2);
+    for (int i = 0; i < c.K; ++i)
+        for (int j = 0; j < c.K; ++j) {
+            plan.tg.tap_x[i * c.K + j] = (float)(i * c.dil - c0);
+            plan.tg.tap_y[i * c.K + j] = (float)(j * c.dil - c0);
+        }
     return true;
 }
 
-template <typename T, int KT, int NT>
+template <typename T, int KT, int NT, bool SM>
 int launch_tiled(const FwdArgs& a, const TilePlan& pl, hipStream_t st)
 {
-    hipLaunchKernelGGL((dcn_forward_tiled<T, KT, NT>), dim3((uint32_t)pl.blocks), dim3(NT), pl.lds_bytes, st,
+    hipLaunchKernelGGL((dcn_forward_tiled<T, KT, NT, SM>), dim3((uint32_t)pl.blocks), dim3(NT), pl.lds_bytes, st,
                        a, pl.tg);
     return launch_status();
+}
+
+template <typename T, int NT, bool SM>
+int forward_tiled_k(const FwdArgs& a, const Call& c, const TilePlan& pl, hipStream_t st)
+{
+    return c.K == 3 ? launch_tiled<T, 3, NT, SM>(a, pl, st) : launch_tiled<T, 0, NT, SM>(a, pl, st);
 }
 
 template <typename T>
@@ -193,8 +208,8 @@ int forward_tiled(const FwdArgs& base, const Call& c, const TilePlan& pl, hipStr
     FwdArgs a = base;
     a.geo = make_geometry(c, 32 / (int)sizeof(T));
     if (pl.threads == 512)
-        return c.K == 3 ? launch_tiled<T, 3, 512>(a, pl, st) : launch_tiled<T, 0, 512>(a, pl, st);
-    return c.K == 3 ? launch_tiled<T, 3, 256>(a, pl, st) : launch_tiled<T, 0, 256>(a, pl, st);
+        return c.softmax ? forward_tiled_k<T, 512, true>(a, c, pl, st) : forward_tiled_k<T, 512, false>(a, c, pl, st);
+    return c.softmax ? forward_tiled_k<T, 256, true>(a, c, pl, st) : forward_tiled_k<T, 256, false>(a, c, pl, st);
 }
 
 // Widest gather whose size divides a group's row and whose alignment the

@@ -230,10 +230,8 @@ __device__ __forceinline__ Sample make_sample(const Geometry& G, float bx, float
                                               float dx, float dy, uint32_t chan_bytes)
 {
     Sample s;
-    const float tx = (float)(i * G.dil - G.c0) + dx;
-    const float ty = (float)(j * G.dil - G.c0) + dy;
-    float x = fmaf(G.alpha, tx, bx);
-    float y = fmaf(G.alpha, ty, by);
+    float x = fmaf(G.alpha, dx, fmaf(G.alpha, (float)(i * G.dil - G.c0), bx));
+    float y = fmaf(G.alpha, dy, fmaf(G.alpha, (float)(j * G.dil - G.c0), by));
     s.inmap = x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H;
     x = s.inmap ? x : -2.0f;          // off the map or NaN: park where no corner is valid
     y = s.inmap ? y : -2.0f;
@@ -364,12 +362,17 @@ __global__ __launch_bounds__(kBlock) void dcn_forward_kernel(FwdArgs a)
 // with odd index read their two 16-byte halves in the opposite order, so the
 // other four lanes of the 8 hold slots {1,3,5,7}.  The swap is undone when
 // the result is stored.
+constexpr int kMaxTiledTaps = 49;     // the tiled kernel serves K <= 7
+
 struct TileGeo {
     int TH, TW;              // output tile, pixels
     int RH, RW;              // staged input region, pixels
     int ML;                  // region origin = first tile centre - ML (both axes)
     int gshift;              // log2(Cg * elem_bytes / 32): lanes per group = 1 << gshift
     uint32_t tiles_x, tiles_y, slabs;
+    uint32_t off_image_bytes, mask_image_bytes;   // one image of offset / mask
+    float tap_x[kMaxTiledTaps];                   // (float)(i*dilation - c0) of point p
+    float tap_y[kMaxTiledTaps];                   // (float)(j*dilation - c0) of point p
 };
 
 #ifndef DCN_TILE_UNROLL
@@ -381,7 +384,45 @@ struct TileGeo {
 #define DCN_TILE_WAVES_PER_EU 4   // register budget 512/4 = 128 VGPRs per lane
 #endif
 
-template <typename T, int KT, int NT>
+// floor(x) as an integer in one instruction (v_cvt_flr_i32_f32; NaN gives 0,
+// +-Inf and out-of-range values saturate).
+__device__ __forceinline__ int cvt_flr(float x)
+{
+    int r;
+    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
+// Neither argument is NaN.
+__device__ __forceinline__ bool ordered(float x, float y)
+{
+    return !__builtin_isunordered(x, y);
+}
+
+// Offset pair (dx, dy) and mask value of point q of a (pixel, group), read
+// through per-image buffer resources with the point in the scalar offset.
+template <typename T>
+__device__ __forceinline__ float2 load_offset_pair(__amdgpu_buffer_rsrc_t r, uint32_t voff, int q)
+{
+    if constexpr (Elem<T>::bytes == 4) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, q * 8, 0);
+        return make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
+    } else {
+        const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(r, voff, q * 4, 0);
+        return make_float2(Elem<T>::widen(u & 0xffffu), Elem<T>::widen(u >> 16));
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ float load_mask_value(__amdgpu_buffer_rsrc_t r, uint32_t voff, int q)
+{
+    if constexpr (Elem<T>::bytes == 4)
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, q * 4, 0));
+    else
+        return Elem<T>::widen(__builtin_amdgcn_raw_buffer_load_b16(r, voff, q * 2, 0));
+}
+
+template <typename T, int KT, int NT, bool SOFTMAX>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DCN_TILE_WAVES_PER_EU)))
 void dcn_forward_tiled(FwdArgs a, TileGeo tg)
 {
@@ -429,45 +470,75 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
     const int ho = ho0 + py, wo = wo0 + px;
     if (p >= tg.TH * tg.TW || ho >= G.Ho || wo >= G.Wo) return;   // after the barrier
 
+    const int P = KT > 0 ? KT * KT : G.P;
     const int swp = p & 1;                       // read order of the two halves
-    const uint32_t lane_chunk = (uint32_t)(sub * 2 + swp);          // first 16-byte slot
     const uint32_t g = slab * (4u >> tg.gshift) + ((uint32_t)sub >> tg.gshift);
-    const size_t pix_global = ((size_t)n * G.Ho + ho) * G.Wo + wo;
-    const size_t pg = pix_global * G.groups + g;
-    const T* off = (const T*)a.offset + pg * G.P * 2;
-    const T* mk = (const T*)a.mask + pg * G.P;
+    const uint32_t pg_img = ((uint32_t)ho * (uint32_t)G.Wo + (uint32_t)wo) * (uint32_t)G.groups + g;
+    const __amdgpu_buffer_rsrc_t roff =
+        image_rsrc((const char*)a.offset + (size_t)n * tg.off_image_bytes, tg.off_image_bytes);
+    const __amdgpu_buffer_rsrc_t rmk =
+        image_rsrc((const char*)a.mask + (size_t)n * tg.mask_image_bytes, tg.mask_image_bytes);
+    const uint32_t voff = pg_img * (uint32_t)(P * 2 * EB);
+    const uint32_t vmk = pg_img * (uint32_t)(P * EB);
     const float bx = (float)(wo * G.stride - G.pad + G.c0);
     const float by = (float)(ho * G.stride - G.pad + G.c0);
-    const float xlo_f = (float)x_lo, xhi_f = (float)(x_lo + tg.RW - 1);
-    const float ylo_f = (float)y_lo, yhi_f = (float)(y_lo + tg.RH - 1);
-    // byte offset of this lane's first half inside a pixel row (global path)
-    const uint32_t gl_first = slab_bytes + (uint32_t)sub * 32u + (uint32_t)swp * 16u;
-    const uint32_t gl_second = slab_bytes + (uint32_t)sub * 32u + (uint32_t)(swp ^ 1) * 16u;
+    const uint32_t xlim = (uint32_t)(tg.RW - 1), ylim = (uint32_t)(tg.RH - 1);
+    const uint32_t lane_first = (uint32_t)sub * 32u + (uint32_t)swp * 16u;   // byte within a pixel slab
+    const uint32_t RWB = (uint32_t)tg.RW * 128u;
+    const char* lds = (const char*)region;
+    // byte offsets of this lane's two halves inside an input pixel row (global path)
+    const uint32_t gl_first = slab_bytes + lane_first;
+    const uint32_t gl_second = gl_first ^ 16u;
+
+    float mx = 0.f, inv = 1.f;
+    if constexpr (SOFTMAX) {
+        mx = load_mask_value<T>(rmk, vmk, 0);
+        for (int q = 1; q < P; ++q) mx = fmaxf(mx, load_mask_value<T>(rmk, vmk, q));
+        float sum = 0.f;
+        for (int q = 0; q < P; ++q) sum += __expf(load_mask_value<T>(rmk, vmk, q) - mx);
+        inv = 1.0f / sum;
+    }
 
     float acc[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
 
-    auto point = [&](int i, int j, float m, float2 d) {
-        const float tx = (float)(i * G.dil - G.c0) + d.x;
-        const float ty = (float)(j * G.dil - G.c0) + d.y;
-        const float x = fmaf(G.alpha, tx, bx);
-        const float y = fmaf(G.alpha, ty, by);
-        float fx = floorf(x), fy = floorf(y);
-        float lx = x - fx, ly = y - fy;
-        float mm = m;
+    // Points in a rolled loop (unrolled DCN_TILE_UNROLL times): fully
+    // unrolled, the compiler hoists every point's corner reads and runs out
+    // of registers.
+    DCN_UNROLL(DCN_TILE_UNROLL)
+    for (int q = 0; q < P; ++q) {
+        const float2 d = load_offset_pair<T>(roff, voff, q);
+        float m = load_mask_value<T>(rmk, vmk, q);
+        if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
+        const float x = fmaf(G.alpha, d.x, fmaf(G.alpha, tg.tap_x[q], bx));
+        const float y = fmaf(G.alpha, d.y, fmaf(G.alpha, tg.tap_y[q], by));
+        // Floor and fraction come from the absolute coordinate (x - x_lo is
+        // not exact when x_lo < 0); the region test is on the integer floor.
+        // cvt_flr saturates +-Inf to out-of-range values; NaN is rejected by
+        // the ordered compare.
+        const uint32_t ix = (uint32_t)(cvt_flr(x) - x_lo), iy = (uint32_t)(cvt_flr(y) - y_lo);
+        float lx, ly, mm = m;
         uint32_t raw[4][8];
-        if (x >= xlo_f && x < xhi_f && y >= ylo_f && y < yhi_f) {
-            const int base = (((int)fy - y_lo) * tg.RW + ((int)fx - x_lo)) * 8 + (int)lane_chunk;
-            const int cofs[4] = {0, 8, RW8, RW8 + 8};
+        if ((ix < xlim) & (iy < ylim) & ordered(x, y)) {
+            lx = __builtin_amdgcn_fractf(x);
+            ly = __builtin_amdgcn_fractf(y);
+            const uint32_t a0 = (__umul24(iy, (uint32_t)tg.RW) + ix) * 128u + lane_first;
+            const uint32_t a1 = a0 ^ 16u;
+            const uint32_t ca[4] = {0u, 128u, RWB, RWB + 128u};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const uint4 v0 = region[base + cofs[k]];
-                const uint4 v1 = region[base + cofs[k] + 1 - 2 * swp];
+                const uint4 v0 = *(const uint4*)(lds + a0 + ca[k]);
+                const uint4 v1 = *(const uint4*)(lds + a1 + ca[k]);
                 raw[k][0] = v0.x; raw[k][1] = v0.y; raw[k][2] = v0.z; raw[k][3] = v0.w;
                 raw[k][4] = v1.x; raw[k][5] = v1.y; raw[k][6] = v1.z; raw[k][7] = v1.w;
             }
         } else {
+            // outside the staged region: gather from global memory with the
+            // untiled kernel's off-map rules
+            float fx = floorf(x), fy = floorf(y);
+            lx = x - fx;
+            ly = y - fy;
             const bool inmap = x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H;
             if (!inmap) { fx = -2.0f; fy = -2.0f; lx = 0.f; ly = 0.f; mm = 0.f; }
             const int x0 = (int)fx, y0 = (int)fy;
@@ -486,47 +557,28 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
                 raw[k][4] = v1[0]; raw[k][5] = v1[1]; raw[k][6] = v1[2]; raw[k][7] = v1[3];
             }
         }
-        // bilinear weights with the modulation folded in
-        const float mly = mm * ly, mhy = mm - mly;
-        const float w01 = mhy * lx, w11 = mly * lx;
-        const float w[4] = {mhy - w01, w01, mly - w11, w11};
+        // bilinear weights with the modulation folded in; each is formed
+        // with relative error <= 2 ulp (the one-minus factors are fused, so
+        // a weight near zero is not the difference of two rounded values)
+        const float mly = mm * ly, mhy = fmaf(-mm, ly, mm);
+        const float w[4] = {fmaf(-mhy, lx, mhy), mhy * lx, fmaf(-mly, lx, mly), mly * lx};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
+            for (int c = 0; c < 8; ++c) {
                 if constexpr (EB == 4) {
-                    acc[q] = fmaf(w[k], __uint_as_float(raw[k][q]), acc[q]);
+                    acc[c] = fmaf(w[k], __uint_as_float(raw[k][c]), acc[c]);
                 } else {
-                    acc[2 * q] = fmaf(w[k], Elem<T>::widen(raw[k][q] & 0xffffu), acc[2 * q]);
-                    acc[2 * q + 1] = fmaf(w[k], Elem<T>::widen(raw[k][q] >> 16), acc[2 * q + 1]);
+                    acc[2 * c] = fmaf(w[k], Elem<T>::widen(raw[k][c] & 0xffffu), acc[2 * c]);
+                    acc[2 * c + 1] = fmaf(w[k], Elem<T>::widen(raw[k][c] >> 16), acc[2 * c + 1]);
                 }
             }
         }
-    };
-
-    // Points are visited in a rolled loop (unrolled DCN_TILE_UNROLL times):
-    // fully unrolled, the compiler hoists every point's corner reads and
-    // runs out of registers.  Mask and offsets are re-read per point (L1).
-    const int K = KT > 0 ? KT : G.K;
-    const int P = K * K;
-    float mx = 0.f, inv = 1.f;
-    if (G.softmax) {
-        mx = ld1(mk);
-        for (int q = 1; q < P; ++q) mx = fmaxf(mx, ld1(mk + q));
-        float sum = 0.f;
-        for (int q = 0; q < P; ++q) sum += __expf(ld1(mk + q) - mx);
-        inv = 1.0f / sum;
-    }
-    DCN_UNROLL(DCN_TILE_UNROLL)
-    for (int q = 0; q < P; ++q) {
-        const int i = q / K, j = q - i * K;
-        float m = ld1(mk + q);
-        if (G.softmax) m = __expf(m - mx) * inv;
-        point(i, j, m, ld2(off + 2 * q));
     }
 
     // store the lane's 32 bytes, undoing the half swap
-    char* out = (char*)a.output + (pix_global * G.C) * EB + slab_bytes + (uint32_t)sub * 32u;
+    char* out = (char*)a.output + ((size_t)n * G.Ho * G.Wo + (size_t)ho * G.Wo + wo) * G.C * EB +
+                slab_bytes + (uint32_t)sub * 32u;
     store<T, 16>(out + swp * 16, &acc[0]);
     store<T, 16>(out + (swp ^ 1) * 16, &acc[EPR]);
 }

@@ -16,9 +16,10 @@
  *
  *   p   = i*K + j            i = kernel column (x), j = kernel row (y)
  *   c0  = floor(dilation*(K-1)/2)
- *   x_p = fmaf(offset_scale, (float)(i*dilation - c0) + dx, (float)(wo*stride - pad + c0))
- *   y_p = fmaf(offset_scale, (float)(j*dilation - c0) + dy, (float)(ho*stride - pad + c0))
- *         -- formed in binary32 in exactly this order; these are pixel
+ *   x_p = fmaf(offset_scale, dx, fmaf(offset_scale, (float)(i*dilation - c0), (float)(wo*stride - pad + c0)))
+ *   y_p = fmaf(offset_scale, dy, fmaf(offset_scale, (float)(j*dilation - c0), (float)(ho*stride - pad + c0)))
+ *         -- formed in binary32 in exactly this order (the inner fmaf is
+ *         exact when offset_scale is 1); these are pixel
  *         coordinates in the UNPADDED map (the zero padding of step 1 is
  *         virtual: everything outside [0,H) x [0,W) reads as zero)
  *   B   = bilinear interpolation from the four pixels around (x_p, y_p);

@@ -40,12 +40,14 @@
  * Coordinate precision: coord_mode 0 forms x_p, y_p in binary64 (the exact
  * real-number definition up to one rounding).  coord_mode 1 forms them in
  * binary32 in the fixed order the library documents:
- *     t = (float)(i*d - c0) + dx;  x = fmaf(alpha, t, (float)(wo*s - pad + c0))
- * so that both sides land on the same floor() branch; everything after the
- * coordinates (weights, products, sums, softmax) is binary64 in both modes.
+ *     b = fmaf(alpha, (float)(i*d - c0), (float)(wo*s - pad + c0));
+ *     x = fmaf(alpha, dx, b)
+ * (b is exact when alpha is 1) so that both sides land on the same floor()
+ * branch; everything after the coordinates (weights, products, sums,
+ * softmax) is binary64 in both modes.
  *
  * Build with -ffp-contract=off so the compiler fuses nothing it was not told
- * to (the one fmaf above is explicit).
+ * to (the two fmaf calls above are explicit).
  */
 #include <math.h>
 #include <stdlib.h>
@@ -67,9 +69,8 @@ static double coord(int o, int s, int pad, int c0, int tap, int d, double alpha,
                     double delta, int coord_mode)
 {
     if (coord_mode == 1) {
-        float t = (float)(tap * d - c0) + (float)delta;
-        float base = (float)(o * s - pad + c0);
-        return (double)fmaf((float)alpha, t, base);
+        float b = fmaf((float)alpha, (float)(tap * d - c0), (float)(o * s - pad + c0));
+        return (double)fmaf((float)alpha, (float)delta, b);
     }
     return (double)(o * s - pad + c0) + alpha * ((double)(tap * d - c0) + delta);
 }
