@@ -161,9 +161,12 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan)
             const uint64_t tx = (uint64_t)((c.Wo + tw - 1) / tw), ty = (uint64_t)((c.Ho + th - 1) / th);
             const uint64_t tiles = tx * ty * slabs * (uint64_t)c.N;
             const int lanes = ((th * tw * 4 + 63) / 64) * 64;
-            // LDS per block bounds the blocks a CU holds; fewer resident waves cost latency hiding
+            // LDS per block bounds the blocks a CU holds; below 16 resident
+            // waves per CU the latency of the corner reads shows
             const int per_cu = (int)(160 * 1024 / lds) < 2048 / nt ? (int)(160 * 1024 / lds) : 2048 / nt;
-            const double occ_penalty = per_cu * nt / 64 >= 12 ? 1.0 : 1.0 + 0.04 * (12 - per_cu * nt / 64);
+            const int waves = per_cu * nt / 64;
+            if (waves < 12) continue;   // too few resident waves: the untiled kernel does better
+            const double occ_penalty = waves >= 16 ? 1.0 : 16.0 / (double)waves;
             const double cost = (double)tiles * ((double)lanes * 900.0 * occ_penalty + (double)rh * rw * 8 * 3.0);
             if (best < 0 || cost < best) {
                 best = cost;

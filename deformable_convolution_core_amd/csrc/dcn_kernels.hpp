@@ -401,6 +401,38 @@ __device__ __forceinline__ bool ordered(float x, float y)
 
 // Offset pair (dx, dy) and mask value of point q of a (pixel, group), read
 // through per-image buffer resources with the point in the scalar offset.
+// The raw forms keep the loaded bits (one dword per offset pair for half
+// types) so a prefetch of all points stays small; widen_* converts later.
+template <typename T> struct RawPair { uint32_t v[Elem<T>::bytes == 4 ? 2 : 1]; };
+
+template <typename T>
+__device__ __forceinline__ RawPair<T> load_offset_raw(__amdgpu_buffer_rsrc_t r, uint32_t voff, int q)
+{
+    RawPair<T> rp;
+    if constexpr (Elem<T>::bytes == 4) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, q * 8, 0);
+        rp.v[0] = v[0];
+        rp.v[1] = v[1];
+    } else {
+        rp.v[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, q * 4, 0);
+    }
+    return rp;
+}
+
+template <typename T>
+__device__ __forceinline__ float2 widen_pair(const RawPair<T>& rp)
+{
+    if constexpr (Elem<T>::bytes == 4) return make_float2(__uint_as_float(rp.v[0]), __uint_as_float(rp.v[1]));
+    else return make_float2(Elem<T>::widen(rp.v[0] & 0xffffu), Elem<T>::widen(rp.v[0] >> 16));
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t load_mask_raw(__amdgpu_buffer_rsrc_t r, uint32_t voff, int q)
+{
+    if constexpr (Elem<T>::bytes == 4) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, q * 4, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b16(r, voff, q * 2, 0);
+}
+
 template <typename T>
 __device__ __forceinline__ float2 load_offset_pair(__amdgpu_buffer_rsrc_t r, uint32_t voff, int q)
 {
@@ -422,6 +454,103 @@ __device__ __forceinline__ float load_mask_value(__amdgpu_buffer_rsrc_t r, uint3
         return Elem<T>::widen(__builtin_amdgcn_raw_buffer_load_b16(r, voff, q * 2, 0));
 }
 
+// One sampling point of the tiled kernel: its four corner rows (8 dwords
+// each, this lane's 32 bytes) and its modulated bilinear weights.
+struct TiledPoint {
+    uint32_t raw[4][8];
+    float w[4];
+};
+
+// Per-lane constants of the tiled kernel's compute phase.
+struct TiledLane {
+    float bx, by;                 // sampling centre (absolute input coordinates)
+    int x_lo, y_lo;               // staged region origin
+    uint32_t xlim, ylim;          // RW-1, RH-1
+    uint32_t lane_first;          // this lane's first 16-byte slot in a pixel slab
+    uint32_t RW, RWB;             // region width in pixels and in bytes
+    uint32_t gl_first, gl_second; // the two halves inside an input pixel row
+};
+
+// Coordinates, weights and corner reads of one point: from the staged region
+// when all four corners lie inside it, else gathered from global memory with
+// the untiled kernel's off-map rules.
+template <typename T>
+__device__ __forceinline__ TiledPoint tiled_fetch(const Geometry& G, const TiledLane& L, const char* lds,
+                                                  __amdgpu_buffer_rsrc_t rin, float tapx, float tapy,
+                                                  float2 d, float m)
+{
+    TiledPoint pt;
+    const float x = fmaf(G.alpha, d.x, fmaf(G.alpha, tapx, L.bx));
+    const float y = fmaf(G.alpha, d.y, fmaf(G.alpha, tapy, L.by));
+    // Floor and fraction come from the absolute coordinate (x - x_lo is not
+    // exact when x_lo < 0); the region test is on the integer floor.
+    // cvt_flr saturates +-Inf to out-of-range values; NaN is rejected by the
+    // ordered compare.
+    const uint32_t ix = (uint32_t)(cvt_flr(x) - L.x_lo), iy = (uint32_t)(cvt_flr(y) - L.y_lo);
+    float lx, ly, mm = m;
+    if ((ix < L.xlim) & (iy < L.ylim) & ordered(x, y)) {
+        lx = __builtin_amdgcn_fractf(x);
+        ly = __builtin_amdgcn_fractf(y);
+        const uint32_t a0 = (__umul24(iy, L.RW) + ix) * 128u + L.lane_first;
+        const uint32_t a1 = a0 ^ 16u;
+        const uint32_t ca[4] = {0u, 128u, L.RWB, L.RWB + 128u};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint4 v0 = *(const uint4*)(lds + a0 + ca[k]);
+            const uint4 v1 = *(const uint4*)(lds + a1 + ca[k]);
+            pt.raw[k][0] = v0.x; pt.raw[k][1] = v0.y; pt.raw[k][2] = v0.z; pt.raw[k][3] = v0.w;
+            pt.raw[k][4] = v1.x; pt.raw[k][5] = v1.y; pt.raw[k][6] = v1.z; pt.raw[k][7] = v1.w;
+        }
+    } else {
+        float fx = floorf(x), fy = floorf(y);
+        lx = x - fx;
+        ly = y - fy;
+        const bool inmap = x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H;
+        if (!inmap) { fx = -2.0f; fy = -2.0f; lx = 0.f; ly = 0.f; mm = 0.f; }
+        const int x0 = (int)fx, y0 = (int)fy;
+        const bool vx0 = (uint32_t)x0 < (uint32_t)G.W, vx1 = (uint32_t)(x0 + 1) < (uint32_t)G.W;
+        const bool vy0 = (uint32_t)y0 < (uint32_t)G.H, vy1 = (uint32_t)(y0 + 1) < (uint32_t)G.H;
+        const bool vk[4] = {vy0 && vx0, vy0 && vx1, vy1 && vx0, vy1 && vx1};
+        const uint32_t a00 = (uint32_t)y0 * G.in_line_bytes + (uint32_t)x0 * G.in_row_bytes;
+        const uint32_t ck[4] = {0u, G.in_row_bytes, G.in_line_bytes, G.in_line_bytes + G.in_row_bytes};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t o0 = vk[k] ? a00 + ck[k] + L.gl_first : kOOB;
+            const uint32_t o1 = vk[k] ? a00 + ck[k] + L.gl_second : kOOB;
+            const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rin, o0, 0, 0);
+            const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rin, o1, 0, 0);
+            pt.raw[k][0] = v0[0]; pt.raw[k][1] = v0[1]; pt.raw[k][2] = v0[2]; pt.raw[k][3] = v0[3];
+            pt.raw[k][4] = v1[0]; pt.raw[k][5] = v1[1]; pt.raw[k][6] = v1[2]; pt.raw[k][7] = v1[3];
+        }
+    }
+    // bilinear weights with the modulation folded in; each is formed with
+    // relative error <= 2 ulp (the one-minus factors are fused, so a weight
+    // near zero is not the difference of two rounded values)
+    const float mly = mm * ly, mhy = fmaf(-mm, ly, mm);
+    pt.w[0] = fmaf(-mhy, lx, mhy);
+    pt.w[1] = mhy * lx;
+    pt.w[2] = fmaf(-mly, lx, mly);
+    pt.w[3] = mly * lx;
+    return pt;
+}
+
+template <typename T, int CPL>
+__device__ __forceinline__ void tiled_accumulate(const TiledPoint& pt, float* acc)
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            if constexpr (Elem<T>::bytes == 4) {
+                acc[c] = fmaf(pt.w[k], __uint_as_float(pt.raw[k][c]), acc[c]);
+            } else {
+                acc[2 * c] = fmaf(pt.w[k], Elem<T>::widen(pt.raw[k][c] & 0xffffu), acc[2 * c]);
+                acc[2 * c + 1] = fmaf(pt.w[k], Elem<T>::widen(pt.raw[k][c] >> 16), acc[2 * c + 1]);
+            }
+        }
+    }
+}
+
 template <typename T, int KT, int NT, bool SOFTMAX>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DCN_TILE_WAVES_PER_EU)))
 void dcn_forward_tiled(FwdArgs a, TileGeo tg)
@@ -429,6 +558,7 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
     constexpr int EB = Elem<T>::bytes;
     constexpr int CPL = 32 / EB;        // channels per lane
     constexpr int EPR = 16 / EB;        // elements per 16-byte read
+    constexpr int PK = KT * KT;         // points when K is a template constant
     extern __shared__ uint4 region[];
     const Geometry& G = a.geo;
 
@@ -449,131 +579,93 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
     const __amdgpu_buffer_rsrc_t rin = image_rsrc(in_img, G.in_image_bytes);
     const uint32_t slab_bytes = slab * 128u;
 
-    // ---- stage the region: lane t loads 16-byte chunk e of every region row
-    for (int e = t; e < RW8; e += NT) {
-        const int gx = x_lo + (e >> 3);
-        const bool col_ok = (uint32_t)gx < (uint32_t)G.W;
-        const uint32_t col_off = (uint32_t)gx * G.in_row_bytes + slab_bytes + (uint32_t)(e & 7) * 16u;
-        for (int ry = 0; ry < tg.RH; ++ry) {
-            const int gy = y_lo + ry;
-            const bool ok = col_ok && (uint32_t)gy < (uint32_t)G.H;
-            const uint32_t off = ok ? (uint32_t)gy * G.in_line_bytes + col_off : kOOB;
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rin, off, 0, 0);
-            region[ry * RW8 + e] = make_uint4(v[0], v[1], v[2], v[3]);
-        }
-    }
-    __syncthreads();
-
-    // ---- one lane = 32 bytes of channels of one output pixel
+    // ---- this lane: 32 bytes of channels of one output pixel
     const int p = t >> 2, sub = t & 3;
     const int py = p / tg.TW, px = p - py * tg.TW;
     const int ho = ho0 + py, wo = wo0 + px;
-    if (p >= tg.TH * tg.TW || ho >= G.Ho || wo >= G.Wo) return;   // after the barrier
-
-    const int P = KT > 0 ? KT * KT : G.P;
-    const int swp = p & 1;                       // read order of the two halves
+    const bool active = p < tg.TH * tg.TW && ho < G.Ho && wo < G.Wo;
+    const int P = KT > 0 ? PK : G.P;
     const uint32_t g = slab * (4u >> tg.gshift) + ((uint32_t)sub >> tg.gshift);
-    const uint32_t pg_img = ((uint32_t)ho * (uint32_t)G.Wo + (uint32_t)wo) * (uint32_t)G.groups + g;
+    const uint32_t pg_img = active ? ((uint32_t)ho * (uint32_t)G.Wo + (uint32_t)wo) * (uint32_t)G.groups + g : 0u;
     const __amdgpu_buffer_rsrc_t roff =
         image_rsrc((const char*)a.offset + (size_t)n * tg.off_image_bytes, tg.off_image_bytes);
     const __amdgpu_buffer_rsrc_t rmk =
         image_rsrc((const char*)a.mask + (size_t)n * tg.mask_image_bytes, tg.mask_image_bytes);
     const uint32_t voff = pg_img * (uint32_t)(P * 2 * EB);
     const uint32_t vmk = pg_img * (uint32_t)(P * EB);
-    const float bx = (float)(wo * G.stride - G.pad + G.c0);
-    const float by = (float)(ho * G.stride - G.pad + G.c0);
-    const uint32_t xlim = (uint32_t)(tg.RW - 1), ylim = (uint32_t)(tg.RH - 1);
-    const uint32_t lane_first = (uint32_t)sub * 32u + (uint32_t)swp * 16u;   // byte within a pixel slab
-    const uint32_t RWB = (uint32_t)tg.RW * 128u;
-    const char* lds = (const char*)region;
-    // byte offsets of this lane's two halves inside an input pixel row (global path)
-    const uint32_t gl_first = slab_bytes + lane_first;
-    const uint32_t gl_second = gl_first ^ 16u;
 
-    float mx = 0.f, inv = 1.f;
-    if constexpr (SOFTMAX) {
-        mx = load_mask_value<T>(rmk, vmk, 0);
-        for (int q = 1; q < P; ++q) mx = fmaxf(mx, load_mask_value<T>(rmk, vmk, q));
-        float sum = 0.f;
-        for (int q = 0; q < P; ++q) sum += __expf(load_mask_value<T>(rmk, vmk, q) - mx);
-        inv = 1.0f / sum;
+    // The first point's offsets and mask are requested before the region is
+    // staged (their latency hides under the staging); inside the point loop
+    // each iteration requests the next point's values (one-point lookahead).
+    RawPair<T> d_next = load_offset_raw<T>(roff, voff, 0);
+    uint32_t m_next = load_mask_raw<T>(rmk, vmk, 0);
+
+    // ---- stage the region with LDS-direct buffer loads (asynchronous, no
+    // registers): lane t copies 16-byte chunk e of every region row; the 64
+    // lanes of a wave fill 1 KB of LDS contiguously, lane l at base + 16*l.
+    // Off-image pixels get an out-of-range offset and are written as zeros.
+    for (int e = t; e < RW8; e += NT) {
+        const int gx = x_lo + (e >> 3);
+        const bool col_ok = (uint32_t)gx < (uint32_t)G.W;
+        const uint32_t col_off = (uint32_t)gx * G.in_row_bytes + slab_bytes + (uint32_t)(e & 7) * 16u;
+        uint4* wave_dst = region + (e & ~63);
+        for (int ry = 0; ry < tg.RH; ++ry) {
+            const int gy = y_lo + ry;
+            const bool ok = col_ok && (uint32_t)gy < (uint32_t)G.H;
+            const uint32_t off = ok ? (uint32_t)gy * G.in_line_bytes + col_off : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rin, (__attribute__((address_space(3))) void*)(wave_dst + ry * RW8), 16, off, 0, 0, 0);
+        }
     }
+    __builtin_amdgcn_s_waitcnt(0);   // all loads (region and lookahead) landed
+    __syncthreads();
+    if (!active) return;   // after the barrier
+
+    const int swp = p & 1;                       // read order of the two halves
+    TiledLane L;
+    L.bx = (float)(wo * G.stride - G.pad + G.c0);
+    L.by = (float)(ho * G.stride - G.pad + G.c0);
+    L.x_lo = x_lo;
+    L.y_lo = y_lo;
+    L.xlim = (uint32_t)(tg.RW - 1);
+    L.ylim = (uint32_t)(tg.RH - 1);
+    L.lane_first = (uint32_t)sub * 32u + (uint32_t)swp * 16u;
+    L.RW = (uint32_t)tg.RW;
+    L.RWB = (uint32_t)tg.RW * 128u;
+    L.gl_first = slab_bytes + L.lane_first;
+    L.gl_second = L.gl_first ^ 16u;
+    const char* lds = (const char*)region;
 
     float acc[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
 
-    // Points in a rolled loop (unrolled DCN_TILE_UNROLL times): fully
-    // unrolled, the compiler hoists every point's corner reads and runs out
-    // of registers.
+    auto mval = [&](uint32_t raw) {
+        return Elem<T>::bytes == 4 ? __uint_as_float(raw) : Elem<T>::widen(raw);
+    };
+    float mx = 0.f, inv = 1.f;
+    if constexpr (SOFTMAX) {
+        mx = mval(m_next);
+        for (int q = 1; q < P; ++q) mx = fmaxf(mx, load_mask_value<T>(rmk, vmk, q));
+        float sum = 0.f;
+        for (int q = 0; q < P; ++q) sum += __expf(load_mask_value<T>(rmk, vmk, q) - mx);
+        inv = 1.0f / sum;
+    }
+    // Rolled point loop: unrolled, the compiler hoists several points' corner
+    // reads and runs out of registers; the lookahead loads and the other
+    // resident waves cover the latencies instead.
     DCN_UNROLL(DCN_TILE_UNROLL)
     for (int q = 0; q < P; ++q) {
-        const float2 d = load_offset_pair<T>(roff, voff, q);
-        float m = load_mask_value<T>(rmk, vmk, q);
+        const RawPair<T> d_cur = d_next;
+        const uint32_t m_cur = m_next;
+        if (q + 1 < P) {
+            d_next = load_offset_raw<T>(roff, voff, q + 1);
+            m_next = load_mask_raw<T>(rmk, vmk, q + 1);
+        }
+        float m = mval(m_cur);
         if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
-        const float x = fmaf(G.alpha, d.x, fmaf(G.alpha, tg.tap_x[q], bx));
-        const float y = fmaf(G.alpha, d.y, fmaf(G.alpha, tg.tap_y[q], by));
-        // Floor and fraction come from the absolute coordinate (x - x_lo is
-        // not exact when x_lo < 0); the region test is on the integer floor.
-        // cvt_flr saturates +-Inf to out-of-range values; NaN is rejected by
-        // the ordered compare.
-        const uint32_t ix = (uint32_t)(cvt_flr(x) - x_lo), iy = (uint32_t)(cvt_flr(y) - y_lo);
-        float lx, ly, mm = m;
-        uint32_t raw[4][8];
-        if ((ix < xlim) & (iy < ylim) & ordered(x, y)) {
-            lx = __builtin_amdgcn_fractf(x);
-            ly = __builtin_amdgcn_fractf(y);
-            const uint32_t a0 = (__umul24(iy, (uint32_t)tg.RW) + ix) * 128u + lane_first;
-            const uint32_t a1 = a0 ^ 16u;
-            const uint32_t ca[4] = {0u, 128u, RWB, RWB + 128u};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint4 v0 = *(const uint4*)(lds + a0 + ca[k]);
-                const uint4 v1 = *(const uint4*)(lds + a1 + ca[k]);
-                raw[k][0] = v0.x; raw[k][1] = v0.y; raw[k][2] = v0.z; raw[k][3] = v0.w;
-                raw[k][4] = v1.x; raw[k][5] = v1.y; raw[k][6] = v1.z; raw[k][7] = v1.w;
-            }
-        } else {
-            // outside the staged region: gather from global memory with the
-            // untiled kernel's off-map rules
-            float fx = floorf(x), fy = floorf(y);
-            lx = x - fx;
-            ly = y - fy;
-            const bool inmap = x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H;
-            if (!inmap) { fx = -2.0f; fy = -2.0f; lx = 0.f; ly = 0.f; mm = 0.f; }
-            const int x0 = (int)fx, y0 = (int)fy;
-            const bool vx0 = (uint32_t)x0 < (uint32_t)G.W, vx1 = (uint32_t)(x0 + 1) < (uint32_t)G.W;
-            const bool vy0 = (uint32_t)y0 < (uint32_t)G.H, vy1 = (uint32_t)(y0 + 1) < (uint32_t)G.H;
-            const bool vk[4] = {vy0 && vx0, vy0 && vx1, vy1 && vx0, vy1 && vx1};
-            const uint32_t a00 = (uint32_t)y0 * G.in_line_bytes + (uint32_t)x0 * G.in_row_bytes;
-            const uint32_t ck[4] = {0u, G.in_row_bytes, G.in_line_bytes, G.in_line_bytes + G.in_row_bytes};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t o0 = vk[k] ? a00 + ck[k] + gl_first : kOOB;
-                const uint32_t o1 = vk[k] ? a00 + ck[k] + gl_second : kOOB;
-                const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rin, o0, 0, 0);
-                const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rin, o1, 0, 0);
-                raw[k][0] = v0[0]; raw[k][1] = v0[1]; raw[k][2] = v0[2]; raw[k][3] = v0[3];
-                raw[k][4] = v1[0]; raw[k][5] = v1[1]; raw[k][6] = v1[2]; raw[k][7] = v1[3];
-            }
-        }
-        // bilinear weights with the modulation folded in; each is formed
-        // with relative error <= 2 ulp (the one-minus factors are fused, so
-        // a weight near zero is not the difference of two rounded values)
-        const float mly = mm * ly, mhy = fmaf(-mm, ly, mm);
-        const float w[4] = {fmaf(-mhy, lx, mhy), mhy * lx, fmaf(-mly, lx, mly), mly * lx};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                if constexpr (EB == 4) {
-                    acc[c] = fmaf(w[k], __uint_as_float(raw[k][c]), acc[c]);
-                } else {
-                    acc[2 * c] = fmaf(w[k], Elem<T>::widen(raw[k][c] & 0xffffu), acc[2 * c]);
-                    acc[2 * c + 1] = fmaf(w[k], Elem<T>::widen(raw[k][c] >> 16), acc[2 * c + 1]);
-                }
-            }
-        }
+        const TiledPoint pt = tiled_fetch<T>(G, L, lds, rin, tg.tap_x[q], tg.tap_y[q], widen_pair<T>(d_cur), m);
+        tiled_accumulate<T, CPL>(pt, acc);
     }
 
     // store the lane's 32 bytes, undoing the half swap
