@@ -433,6 +433,51 @@ __device__ __forceinline__ uint32_t load_mask_raw(__amdgpu_buffer_rsrc_t r, uint
     else return __builtin_amdgcn_raw_buffer_load_b16(r, voff, q * 2, 0);
 }
 
+// The whole offset record (PK pairs) and mask record (PK values) of one
+// (pixel, group), fetched once with the widest loads the record's alignment
+// allows: an offset record starts on a 4-byte boundary (8 for fp32), a
+// half-precision mask record only on a 2-byte one.
+template <typename T, int PK>
+struct PointRecord {
+    uint32_t off[PK * 2 * Elem<T>::bytes / 4];
+    uint32_t mask[PK];
+};
+
+template <typename T, int PK>
+__device__ __forceinline__ void load_record(PointRecord<T, PK>& rec, __amdgpu_buffer_rsrc_t roff, uint32_t voff,
+                                            __amdgpu_buffer_rsrc_t rmk, uint32_t vmk)
+{
+    constexpr int ND = PK * 2 * Elem<T>::bytes / 4;      // offset dwords
+    int i = 0;
+#pragma unroll
+    for (; i + 4 <= ND; i += 4) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(roff, voff, i * 4, 0);
+        rec.off[i] = v[0]; rec.off[i + 1] = v[1]; rec.off[i + 2] = v[2]; rec.off[i + 3] = v[3];
+    }
+#pragma unroll
+    for (; i < ND; ++i) rec.off[i] = __builtin_amdgcn_raw_buffer_load_b32(roff, voff, i * 4, 0);
+    if constexpr (Elem<T>::bytes == 4) {
+        int j = 0;
+#pragma unroll
+        for (; j + 4 <= PK; j += 4) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rmk, vmk, j * 4, 0);
+            rec.mask[j] = v[0]; rec.mask[j + 1] = v[1]; rec.mask[j + 2] = v[2]; rec.mask[j + 3] = v[3];
+        }
+#pragma unroll
+        for (; j < PK; ++j) rec.mask[j] = __builtin_amdgcn_raw_buffer_load_b32(rmk, vmk, j * 4, 0);
+    } else {
+#pragma unroll
+        for (int j = 0; j < PK; ++j) rec.mask[j] = __builtin_amdgcn_raw_buffer_load_b16(rmk, vmk, j * 2, 0);
+    }
+}
+
+template <typename T, int PK>
+__device__ __forceinline__ float2 record_pair(const PointRecord<T, PK>& rec, int q)
+{
+    if constexpr (Elem<T>::bytes == 4) return make_float2(__uint_as_float(rec.off[2 * q]), __uint_as_float(rec.off[2 * q + 1]));
+    else return make_float2(Elem<T>::widen(rec.off[q] & 0xffffu), Elem<T>::widen(rec.off[q] >> 16));
+}
+
 template <typename T>
 __device__ __forceinline__ float2 load_offset_pair(__amdgpu_buffer_rsrc_t r, uint32_t voff, int q)
 {
@@ -551,128 +596,223 @@ __device__ __forceinline__ void tiled_accumulate(const TiledPoint& pt, float* ac
     }
 }
 
-template <typename T, int KT, int NT, bool SOFTMAX>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DCN_TILE_WAVES_PER_EU)))
-void dcn_forward_tiled(FwdArgs a, TileGeo tg)
+// Image, slab and region origin of one tile (wave-uniform values).
+struct TileCoord {
+    uint32_t n, slab;
+    int ho0, wo0, y_lo, x_lo;
+};
+
+__device__ __forceinline__ TileCoord tile_coord(const Geometry& G, const TileGeo& tg, uint32_t tile)
 {
-    constexpr int EB = Elem<T>::bytes;
-    constexpr int CPL = 32 / EB;        // channels per lane
-    constexpr int EPR = 16 / EB;        // elements per 16-byte read
-    constexpr int PK = KT * KT;         // points when K is a template constant
-    extern __shared__ uint4 region[];
-    const Geometry& G = a.geo;
-
-    uint32_t rest = xcd_remap(blockIdx.x, gridDim.x);
-    const uint32_t tile_x = rest % tg.tiles_x;
+    TileCoord c;
+    uint32_t rest = tile;
+    const uint32_t tx = rest % tg.tiles_x;
     rest /= tg.tiles_x;
-    const uint32_t tile_y = rest % tg.tiles_y;
+    const uint32_t ty = rest % tg.tiles_y;
     rest /= tg.tiles_y;
-    const uint32_t slab = rest % tg.slabs;
-    const uint32_t n = rest / tg.slabs;
-    const int ho0 = (int)tile_y * tg.TH, wo0 = (int)tile_x * tg.TW;
-    const int y_lo = ho0 * G.stride - G.pad + G.c0 - tg.ML;
-    const int x_lo = wo0 * G.stride - G.pad + G.c0 - tg.ML;
-    const int t = threadIdx.x;
+    c.slab = rest % tg.slabs;
+    c.n = rest / tg.slabs;
+    c.ho0 = (int)ty * tg.TH;
+    c.wo0 = (int)tx * tg.TW;
+    c.y_lo = c.ho0 * G.stride - G.pad + G.c0 - tg.ML;
+    c.x_lo = c.wo0 * G.stride - G.pad + G.c0 - tg.ML;
+    return c;
+}
+
+// Stage region rows [r0, r1) of tile c into buf with LDS-direct buffer loads
+// (asynchronous, no registers): lane t copies 16-byte chunk e of each row;
+// the 64 lanes of a wave fill 1 KB of LDS contiguously (lane l at base +
+// 16*l).  Off-image pixels get an out-of-range offset and are written as
+// zeros, which is the zero padding of the definition.
+template <int NT>
+__device__ __forceinline__ void stage_rows(const Geometry& G, const TileGeo& tg, const void* input,
+                                           const TileCoord& c, uint4* buf, int r0, int r1, int t)
+{
     const int RW8 = tg.RW * 8;
-
-    const char* in_img = (const char*)a.input + (size_t)n * G.in_image_bytes;
-    const __amdgpu_buffer_rsrc_t rin = image_rsrc(in_img, G.in_image_bytes);
-    const uint32_t slab_bytes = slab * 128u;
-
-    // ---- this lane: 32 bytes of channels of one output pixel
-    const int p = t >> 2, sub = t & 3;
-    const int py = p / tg.TW, px = p - py * tg.TW;
-    const int ho = ho0 + py, wo = wo0 + px;
-    const bool active = p < tg.TH * tg.TW && ho < G.Ho && wo < G.Wo;
-    const int P = KT > 0 ? PK : G.P;
-    const uint32_t g = slab * (4u >> tg.gshift) + ((uint32_t)sub >> tg.gshift);
-    const uint32_t pg_img = active ? ((uint32_t)ho * (uint32_t)G.Wo + (uint32_t)wo) * (uint32_t)G.groups + g : 0u;
-    const __amdgpu_buffer_rsrc_t roff =
-        image_rsrc((const char*)a.offset + (size_t)n * tg.off_image_bytes, tg.off_image_bytes);
-    const __amdgpu_buffer_rsrc_t rmk =
-        image_rsrc((const char*)a.mask + (size_t)n * tg.mask_image_bytes, tg.mask_image_bytes);
-    const uint32_t voff = pg_img * (uint32_t)(P * 2 * EB);
-    const uint32_t vmk = pg_img * (uint32_t)(P * EB);
-
-    // The first point's offsets and mask are requested before the region is
-    // staged (their latency hides under the staging); inside the point loop
-    // each iteration requests the next point's values (one-point lookahead).
-    RawPair<T> d_next = load_offset_raw<T>(roff, voff, 0);
-    uint32_t m_next = load_mask_raw<T>(rmk, vmk, 0);
-
-    // ---- stage the region with LDS-direct buffer loads (asynchronous, no
-    // registers): lane t copies 16-byte chunk e of every region row; the 64
-    // lanes of a wave fill 1 KB of LDS contiguously, lane l at base + 16*l.
-    // Off-image pixels get an out-of-range offset and are written as zeros.
+    const __amdgpu_buffer_rsrc_t rin =
+        image_rsrc((const char*)input + (size_t)c.n * G.in_image_bytes, G.in_image_bytes);
     for (int e = t; e < RW8; e += NT) {
-        const int gx = x_lo + (e >> 3);
+        const int gx = c.x_lo + (e >> 3);
         const bool col_ok = (uint32_t)gx < (uint32_t)G.W;
-        const uint32_t col_off = (uint32_t)gx * G.in_row_bytes + slab_bytes + (uint32_t)(e & 7) * 16u;
-        uint4* wave_dst = region + (e & ~63);
-        for (int ry = 0; ry < tg.RH; ++ry) {
-            const int gy = y_lo + ry;
+        const uint32_t col_off = (uint32_t)gx * G.in_row_bytes + c.slab * 128u + (uint32_t)(e & 7) * 16u;
+        uint4* wave_dst = buf + (e & ~63);
+        for (int ry = r0; ry < r1; ++ry) {
+            const int gy = c.y_lo + ry;
             const bool ok = col_ok && (uint32_t)gy < (uint32_t)G.H;
             const uint32_t off = ok ? (uint32_t)gy * G.in_line_bytes + col_off : kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rin, (__attribute__((address_space(3))) void*)(wave_dst + ry * RW8), 16, off, 0, 0, 0);
         }
     }
-    __builtin_amdgcn_s_waitcnt(0);   // all loads (region and lookahead) landed
-    __syncthreads();
-    if (!active) return;   // after the barrier
+}
 
+// Persistent tiled forward: a workgroup walks the contiguous tile range
+// [first, first + count).  With two LDS buffers, tile k is computed from one
+// while tile k+1's region streams into the other; the next tile's rows are
+// issued in slices between points so that waits on a point's own loads never
+// have to drain a whole region's worth of earlier loads (vector memory
+// counters retire in order).  With one buffer (count == 1) it stages, waits
+// and computes.
+template <typename T, int KT, int NT, bool SOFTMAX, bool PERSIST>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DCN_TILE_WAVES_PER_EU)))
+void dcn_forward_tiled(FwdArgs a, TileGeo tg, uint32_t tiles_total, uint32_t tiles_per_block)
+{
+    constexpr int EB = Elem<T>::bytes;
+    constexpr int CPL = 32 / EB;        // channels per lane
+    constexpr int EPR = 16 / EB;        // elements per 16-byte read
+    extern __shared__ uint4 region[];
+    const Geometry& G = a.geo;
+    const int t = threadIdx.x;
+    const uint32_t region_elems = (uint32_t)(tg.RH * tg.RW * 8);
+
+    const uint32_t first = xcd_remap(blockIdx.x, gridDim.x) * tiles_per_block;
+    if (first >= tiles_total) return;                       // whole workgroup
+    const uint32_t last = first + tiles_per_block < tiles_total ? first + tiles_per_block : tiles_total;
+
+    TileCoord cur = tile_coord(G, tg, first);
+    stage_rows<NT>(G, tg, a.input, cur, region, 0, tg.RH, t);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // ---- this lane: 32 bytes of channels of one output pixel of each tile
+    const int p = t >> 2, sub = t & 3;
+    const int py = p / tg.TW, px = p - py * tg.TW;
+    const int P = KT > 0 ? KT * KT : G.P;
     const int swp = p & 1;                       // read order of the two halves
     TiledLane L;
-    L.bx = (float)(wo * G.stride - G.pad + G.c0);
-    L.by = (float)(ho * G.stride - G.pad + G.c0);
-    L.x_lo = x_lo;
-    L.y_lo = y_lo;
     L.xlim = (uint32_t)(tg.RW - 1);
     L.ylim = (uint32_t)(tg.RH - 1);
     L.lane_first = (uint32_t)sub * 32u + (uint32_t)swp * 16u;
     L.RW = (uint32_t)tg.RW;
     L.RWB = (uint32_t)tg.RW * 128u;
-    L.gl_first = slab_bytes + L.lane_first;
-    L.gl_second = L.gl_first ^ 16u;
-    const char* lds = (const char*)region;
 
-    float acc[CPL];
+    for (uint32_t tile = first; tile < last; ++tile) {
+        const uint32_t k = tile - first;
+        uint4* buf = region + (k & 1u) * region_elems;
+        uint4* nbuf = region + ((k + 1u) & 1u) * region_elems;
+        const bool has_next = PERSIST && tile + 1 < last;
+        const TileCoord nxt = tile_coord(G, tg, has_next ? tile + 1 : tile);
+
+        const int ho = cur.ho0 + py, wo = cur.wo0 + px;
+        const bool active = p < tg.TH * tg.TW && ho < G.Ho && wo < G.Wo;
+        const uint32_t g = cur.slab * (4u >> tg.gshift) + ((uint32_t)sub >> tg.gshift);
+        const uint32_t pg_img = active ? ((uint32_t)ho * (uint32_t)G.Wo + (uint32_t)wo) * (uint32_t)G.groups + g : 0u;
+        const __amdgpu_buffer_rsrc_t rin =
+            image_rsrc((const char*)a.input + (size_t)cur.n * G.in_image_bytes, G.in_image_bytes);
+        const __amdgpu_buffer_rsrc_t roff =
+            image_rsrc((const char*)a.offset + (size_t)cur.n * tg.off_image_bytes, tg.off_image_bytes);
+        const __amdgpu_buffer_rsrc_t rmk =
+            image_rsrc((const char*)a.mask + (size_t)cur.n * tg.mask_image_bytes, tg.mask_image_bytes);
+        const uint32_t voff = pg_img * (uint32_t)(P * 2 * EB);
+        const uint32_t vmk = pg_img * (uint32_t)(P * EB);
+        L.bx = (float)(wo * G.stride - G.pad + G.c0);
+        L.by = (float)(ho * G.stride - G.pad + G.c0);
+        L.x_lo = cur.x_lo;
+        L.y_lo = cur.y_lo;
+        L.gl_first = cur.slab * 128u + L.lane_first;
+        L.gl_second = L.gl_first ^ 16u;
+        const char* lds = (const char*)buf;
+
+        auto mval = [&](uint32_t raw) {
+            return Elem<T>::bytes == 4 ? __uint_as_float(raw) : Elem<T>::widen(raw);
+        };
+        float acc[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+        for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
 
-    auto mval = [&](uint32_t raw) {
-        return Elem<T>::bytes == 4 ? __uint_as_float(raw) : Elem<T>::widen(raw);
-    };
-    float mx = 0.f, inv = 1.f;
-    if constexpr (SOFTMAX) {
-        mx = mval(m_next);
-        for (int q = 1; q < P; ++q) mx = fmaxf(mx, load_mask_value<T>(rmk, vmk, q));
-        float sum = 0.f;
-        for (int q = 0; q < P; ++q) sum += __expf(load_mask_value<T>(rmk, vmk, q) - mx);
-        inv = 1.0f / sum;
-    }
-    // Rolled point loop: unrolled, the compiler hoists several points' corner
-    // reads and runs out of registers; the lookahead loads and the other
-    // resident waves cover the latencies instead.
-    DCN_UNROLL(DCN_TILE_UNROLL)
-    for (int q = 0; q < P; ++q) {
-        const RawPair<T> d_cur = d_next;
-        const uint32_t m_cur = m_next;
-        if (q + 1 < P) {
-            d_next = load_offset_raw<T>(roff, voff, q + 1);
-            m_next = load_mask_raw<T>(rmk, vmk, q + 1);
+        if constexpr (KT > 0) {
+            // K fixed: the (pixel, group)'s offset and mask records come in once
+            // (a per-point load would re-touch the same cache lines P times)
+            // and the points are unrolled so the record stays in registers.
+            constexpr int PK = KT * KT;
+            PointRecord<T, PK> rec;
+            load_record<T, PK>(rec, roff, voff, rmk, vmk);
+            float mx = 0.f, inv = 1.f;
+            if constexpr (SOFTMAX) {
+                mx = mval(rec.mask[0]);
+#pragma unroll
+                for (int q = 1; q < PK; ++q) mx = fmaxf(mx, mval(rec.mask[q]));
+                float sum = 0.f;
+#pragma unroll
+                for (int q = 0; q < PK; ++q) sum += __expf(mval(rec.mask[q]) - mx);
+                inv = 1.0f / sum;
+            }
+#pragma unroll
+            for (int q = 0; q < PK; ++q) {
+                if (active) {
+                    float m = mval(rec.mask[q]);
+                    if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
+                    const TiledPoint pt = tiled_fetch<T>(G, L, lds, rin, tg.tap_x[q], tg.tap_y[q], record_pair<T, PK>(rec, q), m);
+                    tiled_accumulate<T, CPL>(pt, acc);
+                }
+                if constexpr (PERSIST)
+                    if (has_next) stage_rows<NT>(G, tg, a.input, nxt, nbuf, (q * tg.RH) / PK, ((q + 1) * tg.RH) / PK, t);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            float mx = 0.f, inv = 1.f;
+            if constexpr (SOFTMAX) {
+                mx = load_mask_value<T>(rmk, vmk, 0);
+                for (int q = 1; q < P; ++q) mx = fmaxf(mx, load_mask_value<T>(rmk, vmk, q));
+                float sum = 0.f;
+                for (int q = 0; q < P; ++q) sum += __expf(load_mask_value<T>(rmk, vmk, q) - mx);
+                inv = 1.0f / sum;
+            }
+            auto fetch = [&](int q, const RawPair<T>& d, uint32_t mraw) {
+                float m = mval(mraw);
+                if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
+                return tiled_fetch<T>(G, L, lds, rin, tg.tap_x[q], tg.tap_y[q], widen_pair<T>(d), m);
+            };
+
+            // Software pipeline over the points, two per (rolled) iteration: the
+            // corner reads of point q+1 are in flight while point q accumulates,
+            // and each point's offsets and mask are requested two points ahead.
+            // Rolled, the compiler cannot hoist further points' reads and run
+            // out of registers.
+            RawPair<T> dA, dB;
+            uint32_t mA = 0u, mB = 0u;
+            dA = load_offset_raw<T>(roff, voff, 0);
+            mA = load_mask_raw<T>(rmk, vmk, 0);
+            if (P > 1) { dB = load_offset_raw<T>(roff, voff, 1); mB = load_mask_raw<T>(rmk, vmk, 1); }
+            TiledPoint ptA, ptB;
+            if (active) ptA = fetch(0, dA, mA);
+            if (P > 2) { dA = load_offset_raw<T>(roff, voff, 2); mA = load_mask_raw<T>(rmk, vmk, 2); }
+            int q = 0;
+            DCN_UNROLL(1)
+            for (; q + 1 < P; q += 2) {
+                // here: ptA = point q (reads issued), dB = point q+1, dA = point q+2
+                if (active) ptB = fetch(q + 1, dB, mB);
+                if (q + 3 < P) { dB = load_offset_raw<T>(roff, voff, q + 3); mB = load_mask_raw<T>(rmk, vmk, q + 3); }
+                if (active) tiled_accumulate<T, CPL>(ptA, acc);
+                if constexpr (PERSIST)
+                    if (has_next) stage_rows<NT>(G, tg, a.input, nxt, nbuf, (q * tg.RH) / P, ((q + 1) * tg.RH) / P, t);
+                if (q + 2 < P) {
+                    if (active) ptA = fetch(q + 2, dA, mA);
+                    if (q + 4 < P) { dA = load_offset_raw<T>(roff, voff, q + 4); mA = load_mask_raw<T>(rmk, vmk, q + 4); }
+                }
+                if (active) tiled_accumulate<T, CPL>(ptB, acc);
+                if constexpr (PERSIST)
+                    if (has_next)
+                        stage_rows<NT>(G, tg, a.input, nxt, nbuf, ((q + 1) * tg.RH) / P, ((q + 2) * tg.RH) / P, t);
+            }
+            if (q < P) {   // odd number of points: the last one is in ptA
+                if (active) tiled_accumulate<T, CPL>(ptA, acc);
+                if constexpr (PERSIST)
+                    if (has_next) stage_rows<NT>(G, tg, a.input, nxt, nbuf, (q * tg.RH) / P, tg.RH, t);
+            }
         }
-        float m = mval(m_cur);
-        if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
-        const TiledPoint pt = tiled_fetch<T>(G, L, lds, rin, tg.tap_x[q], tg.tap_y[q], widen_pair<T>(d_cur), m);
-        tiled_accumulate<T, CPL>(pt, acc);
-    }
 
-    // store the lane's 32 bytes, undoing the half swap
-    char* out = (char*)a.output + ((size_t)n * G.Ho * G.Wo + (size_t)ho * G.Wo + wo) * G.C * EB +
-                slab_bytes + (uint32_t)sub * 32u;
-    store<T, 16>(out + swp * 16, &acc[0]);
-    store<T, 16>(out + (swp ^ 1) * 16, &acc[EPR]);
+        if (active) {
+            // store the lane's 32 bytes, undoing the half swap
+            char* out = (char*)a.output + ((size_t)cur.n * G.Ho * G.Wo + (size_t)ho * G.Wo + wo) * G.C * EB +
+                        cur.slab * 128u + (uint32_t)sub * 32u;
+            store<T, 16>(out + swp * 16, &acc[0]);
+            store<T, 16>(out + (swp ^ 1) * 16, &acc[EPR]);
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // the next region has landed
+        __syncthreads();                 // and nobody still reads this one
+        cur = nxt;
+    }
 }
 
 // ---------------------------------------------------------------------------
