@@ -163,7 +163,7 @@ def forward_record(w, steps, warmup):
 
 def cpu_baseline(w):
     """The oracle as it stands, on the host cores, over whole batches of the
-    headline workload, repeated until at least ~3 s of wall time."""
+    headline workload, repeated until at least ~10 s of wall time."""
     import oracle   # test infrastructure, used here only for this timing leg
     t = inputs.make(w, with_grad=False)
     x, o, m = (inputs.to_f64(t[k]) for k in ("input", "offset", "mask"))
@@ -175,10 +175,10 @@ def cpu_baseline(w):
         oracle.forward(x, o, m, **kw)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= 3.0 or reps >= 200:
+        if el >= 10.0 or reps >= 1000:
             break
     per = el / reps
-    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    cores = oracle.max_threads()
     return dict(value=round(w.min_bytes_forward() / per / 1e9, 3), unit="GB/s", cores=cores,
                 kind="oracle",
                 sample=f"{reps} full batches of {w.name} (N={w.N}), binary64 C loops with OpenMP, "

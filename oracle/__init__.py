@@ -51,6 +51,8 @@ def _open(path):
     i, d = ctypes.c_int, ctypes.c_double
     lib.oracle_out_size.argtypes = [i, i, i, i, i]
     lib.oracle_out_size.restype = i
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = i
     lib.oracle_forward.argtypes = [dp, dp, dp, dp, dp] + [i] * 9 + [d, i, i]
     lib.oracle_forward.restype = i
     lib.oracle_backward.argtypes = [dp] * 11 + [i] * 9 + [d, i, i]
@@ -89,6 +91,11 @@ def _ptr(a):
     if a is None:
         return None
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def max_threads() -> int:
+    """Threads the oracle's OpenMP loops run on."""
+    return int(_load().oracle_max_threads())
 
 
 def out_size(n: int, K: int, stride: int, pad: int, dilation: int) -> int:

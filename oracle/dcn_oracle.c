@@ -52,6 +52,19 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the parallel loops below use (1 without OpenMP). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* Output extent of a convolution-shaped sampling grid ([FB] section 4 step 1
  * takes H_out/W_out from the offset tensor; a stride of 2 halves it). */
