@@ -254,6 +254,94 @@ int forward_typed(const FwdArgs& a, const Call& c, hipStream_t st)
     return DCN_ERR_INVALID_ARG;   // pointers not aligned to their element size
 }
 
+// ------------------------------------------------------ backward, owner tiles
+#ifndef DCN_USE_OWNER
+#define DCN_USE_OWNER 1       // grad_input by owner tiles where the shape allows
+#endif
+#ifndef DCN_OWNER_REACH
+#define DCN_OWNER_REACH 4     // corners of offsets up to this many pixels are added by owners
+#endif
+constexpr int64_t kMaxOwnerLds = 64 * 1024;
+
+struct OwnerPlan {
+    OwnerGeo og;
+    int threads;
+    uint32_t lds_bytes;
+    uint64_t blocks;
+};
+
+// The owner kernel applies to binary32 gradients whose 32-byte lane chunks
+// stay inside one group (Cg a multiple of 8) and whose 128-byte slabs tile
+// the channel row (C a multiple of 32), with 16-byte aligned grad_output and
+// grad_input.  Among tiles of at most 512 pixels it picks the one with the
+// shortest makespan: blocks per CU (256 CUs) times a block's lane slots
+// issued over its visited output pixels (idle lanes of the last pass count)
+// plus its own zero fill and store.  It declines shapes
+// where the visited area is many times the output (a very large
+// offset_scale makes every output pixel near every tile).
+bool plan_owner(const Call& c, const void* gout, const void* gin, OwnerPlan& pl)
+{
+    const int C = c.G * c.Cg;
+    if (c.Cg % 8 != 0 || C % 32 != 0) return false;
+    if (!aligned(gout, 16) || !aligned(gin, 16)) return false;
+    const float a = c.alpha < 0 ? -c.alpha : c.alpha;
+    const int c0 = c.dil * (c.K - 1) / 2;
+    const int span = c0 > c.dil * (c.K - 1) - c0 ? c0 : c.dil * (c.K - 1) - c0;
+    const float mf = ceilf(a * ((float)span + (float)DCN_OWNER_REACH)) + 1.0f;
+    if (!(mf <= 1024.0f)) return false;
+    const int M = (int)mf;
+    const uint32_t slabs = (uint32_t)(C / 32);
+    double best = -1.0;
+    for (int nt = 256; nt <= 512; nt *= 2) {
+        for (int tw = 1; tw <= 64 && tw <= c.W; ++tw)
+            for (int th = 1; th <= 64 && th <= c.H; ++th) {
+                const int64_t lds = (int64_t)th * tw * 128;
+                if (lds > kMaxOwnerLds) continue;
+                const int per_cu = (int)(160 * 1024 / lds) < 2048 / nt ? (int)(160 * 1024 / lds) : 2048 / nt;
+                const int waves = per_cu * nt / 64;
+                if (waves < 8) continue;
+                const int64_t tx = (c.W + tw - 1) / tw, ty = (c.H + th - 1) / th;
+                int64_t ew = (tw - 1 + 2 * M) / c.stride + 1, eh = (th - 1 + 2 * M) / c.stride + 1;
+                if (ew > c.Wo) ew = c.Wo;
+                if (eh > c.Ho) eh = c.Ho;
+                const int64_t passes = (ew * eh * 4 + nt - 1) / nt;
+                const double occ = waves >= 16 ? 1.0 : 16.0 / (double)waves;
+                // makespan: the busiest CU runs ceil(blocks / CUs) blocks
+                const int64_t blocks = tx * ty * (int64_t)slabs * c.N;
+                const double rounds = (double)((blocks + 255) / 256);
+                const double cost = rounds * ((double)passes * nt * 10.0 + (double)th * tw * 16.0) * occ;
+                if (best < 0 || cost < best) {
+                    best = cost;
+                    pl.og = OwnerGeo{th, tw, M, c.Cg, (uint32_t)tx, (uint32_t)ty, slabs, 0u, 0u};
+                    pl.threads = nt;
+                    pl.lds_bytes = (uint32_t)lds;
+                    pl.blocks = (uint64_t)(tx * ty) * slabs * (uint64_t)c.N;
+                }
+            }
+    }
+    if (best < 0 || pl.blocks >= (1ull << 31)) return false;
+    const int64_t off_img = (int64_t)c.Ho * c.Wo * c.G * c.K * c.K * 2 * 4;
+    if (off_img >= (1ll << 31)) return false;
+    pl.og.off_image_bytes = (uint32_t)off_img;
+    pl.og.mask_image_bytes = (uint32_t)(off_img / 2);
+    // visited output pixels per output pixel: beyond 8x the atomic scatter is cheaper
+    const double visits = (double)pl.og.tiles_x * pl.og.tiles_y *
+                          (double)((pl.og.TW - 1 + 2 * M) / c.stride + 1) * ((pl.og.TH - 1 + 2 * M) / c.stride + 1);
+    return visits <= 8.0 * (double)c.Ho * c.Wo;
+}
+
+template <int KT>
+int launch_owner(const BwdArgs& a, const OwnerPlan& pl, hipStream_t st)
+{
+    if (pl.threads == 512)
+        hipLaunchKernelGGL((dcn_backward_input_owner<KT, 512>), dim3((uint32_t)pl.blocks), dim3(512), pl.lds_bytes,
+                           st, a, pl.og);
+    else
+        hipLaunchKernelGGL((dcn_backward_input_owner<KT, 256>), dim3((uint32_t)pl.blocks), dim3(256), pl.lds_bytes,
+                           st, a, pl.og);
+    return launch_status();
+}
+
 template <int LB, int L>
 int backward_variant(const BwdArgs& base, const Call& c, hipStream_t st)
 {
@@ -360,11 +448,21 @@ extern "C" int dcn_core_backward(const void* input, const void* offset, const vo
         return DCN_ERR_UNSUPPORTED;
     }
     hipStream_t st = (hipStream_t)stream;
-    rc = zero_fill((float*)grad_input, (int64_t)N * H * W * G * Cg, st);
-    if (rc != DCN_OK) return rc;
     BwdArgs a{};
     a.input = input; a.offset = offset; a.mask = mask; a.grad_out = grad_output;
     a.grad_input = (float*)grad_input; a.grad_offset = (float*)grad_offset; a.grad_mask = (float*)grad_mask;
+    a.near_m = -1;
+    OwnerPlan op;
+    if (DCN_USE_OWNER && plan_owner(c, grad_output, grad_input, op)) {
+        // owners write every element of grad_input; the gradient kernel
+        // then adds the corners that are not near with atomics
+        a.geo = make_geometry(c, 8);
+        rc = c.K == 3 ? launch_owner<3>(a, op, st) : launch_owner<0>(a, op, st);
+        a.near_m = op.og.M;
+    } else {
+        rc = zero_fill((float*)grad_input, (int64_t)N * H * W * G * Cg, st);
+    }
+    if (rc != DCN_OK) return rc;
     return LB == 16 ? backward_lanes<16>(a, c, st, L) : backward_lanes<4>(a, c, st, L);
 }
 

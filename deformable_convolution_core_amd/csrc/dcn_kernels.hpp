@@ -191,6 +191,8 @@ struct BwdArgs {
     float* grad_input;
     float* grad_offset;
     float* grad_mask;
+    int near_m;                   // >= 0: corners within this many pixels of the sampling
+                                  // base were added by the owner kernel; -1: none were
     Geometry geo;
 };
 
@@ -221,6 +223,7 @@ __device__ __forceinline__ LaneWork lane_work(const Geometry& G)
 // (y0+1,x0), (y0+1,x0+1).
 struct Sample {
     float lx, ly;
+    int x0, y0;                   // floor of the (parked) coordinates
     bool inmap;
     bool v[4];
     uint32_t off[4];
@@ -239,6 +242,8 @@ __device__ __forceinline__ Sample make_sample(const Geometry& G, float bx, float
     s.lx = x - fx;
     s.ly = y - fy;
     const int x0 = (int)fx, y0 = (int)fy;
+    s.x0 = x0;
+    s.y0 = y0;
     const bool vx0 = (uint32_t)x0 < (uint32_t)G.W, vx1 = (uint32_t)(x0 + 1) < (uint32_t)G.W;
     const bool vy0 = (uint32_t)y0 < (uint32_t)G.H, vy1 = (uint32_t)(y0 + 1) < (uint32_t)G.H;
     s.v[0] = vy0 && vx0; s.v[1] = vy0 && vx1; s.v[2] = vy1 && vx0; s.v[3] = vy1 && vx1;
@@ -852,8 +857,9 @@ __global__ __launch_bounds__(kBlock) void dcn_backward_kernel(BwdArgs a)
     float* goff = a.grad_offset + pg * G.P * 2;
     float* gmk = a.grad_mask + pg * G.P;
     char* gin = (char*)a.grad_input + (size_t)lw.n * G.in_image_bytes;
-    const float bx = (float)((int)lw.wo * G.stride - G.pad + G.c0);
-    const float by = (float)((int)lw.ho * G.stride - G.pad + G.c0);
+    const int bxi = (int)lw.wo * G.stride - G.pad + G.c0;
+    const int byi = (int)lw.ho * G.stride - G.pad + G.c0;
+    const float bx = (float)bxi, by = (float)byi;
     const bool leader = (lw.cc & (L - 1)) == 0;
 
     float go[CPL];
@@ -900,7 +906,11 @@ __global__ __launch_bounds__(kBlock) void dcn_backward_kernel(BwdArgs a)
                 gm = fmaf(wb[k], sk, gm);
                 gdx = fmaf(dwx[k], sk, gdx);
                 gdy = fmaf(dwy[k], sk, gdy);
-                if (s.v[k]) {
+                // corners near the sampling base were added by the owner kernel
+                const bool near = a.near_m >= 0 &&
+                                  (uint32_t)(s.x0 + (k & 1) - bxi + a.near_m) <= 2u * (uint32_t)a.near_m &&
+                                  (uint32_t)(s.y0 + (k >> 1) - byi + a.near_m) <= 2u * (uint32_t)a.near_m;
+                if (s.v[k] && !near) {
                     const float mw = m * wb[k];
                     float* dst = (float*)(gin + s.off[k]);
 #pragma unroll
@@ -922,6 +932,244 @@ __global__ __launch_bounds__(kBlock) void dcn_backward_kernel(BwdArgs a)
             const float m = __expf(mk[p] - mx) * inv;
             gmk[p] = m * (gmk[p] - dot);
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// grad_input by owner.  A workgroup owns a TH x TW tile of input pixels and
+// one 128-byte slab of their channels (32 binary32 channels, four lanes of
+// eight channels per pixel).  A corner q of a sample of output pixel o is
+// "near" when |q - b(o)| <= M on both axes, b(o) = o*stride - pad + c0 being
+// the sample's integer base.  The owner visits exactly the output pixels
+// whose base lies within M of its tile, recomputes their samples, adds
+// m*w*g of every near corner that falls in its tile into an LDS copy of the
+// tile, and writes the tile once.  Each near (sample, corner) pair lies in
+// one tile, so grad_input needs neither a zero fill nor global atomics; the
+// rare corners that are not near (offsets beyond the reach M was sized for)
+// are added afterwards, with atomics, by dcn_backward_kernel.
+//
+// LDS keeps the tile pixel by pixel, 32 floats each (channel order); lane
+// chunk `sub` adds into floats [8*sub, 8*sub + 8) of a pixel.
+// Float adds into LDS through compare-and-swap.  On gfx950 an LDS float
+// atomic add (ds_add_f32) retires about one lane every few cycles per CU,
+// while integer LDS atomics run at the rate of plain LDS accesses; a CAS loop
+// uses the latter.  The NV adds of one lane go to slots (c + rot) & 7 of an
+// 8-float chunk and are issued together: read the old values, swap in
+// old + v, and retry only the slots another lane changed in between (each
+// retry follows some lane's successful swap, so the loop ends).
+template <int NV>
+__device__ __forceinline__ void lds_add(uint32_t* chunk, uint32_t rot, const float* v)
+{
+    uint32_t old[NV], got[NV];
+#pragma unroll
+    for (int c = 0; c < NV; ++c)
+        old[c] = __hip_atomic_load(chunk + ((c + rot) & 7u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    bool again = false;
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+        got[c] = old[c];
+        __hip_atomic_compare_exchange_strong(chunk + ((c + rot) & 7u), &got[c],
+                                             __float_as_uint(__uint_as_float(old[c]) + v[c]),
+                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+#pragma unroll
+    for (int c = 0; c < NV; ++c) again |= got[c] != old[c];
+    while (again) {
+        again = false;
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+            if (got[c] != old[c]) {
+                old[c] = got[c];
+                __hip_atomic_compare_exchange_strong(chunk + ((c + rot) & 7u), &got[c],
+                                                     __float_as_uint(__uint_as_float(old[c]) + v[c]),
+                                                     __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                again |= got[c] != old[c];
+            }
+        }
+    }
+}
+
+struct OwnerGeo {
+    int TH, TW, M, Cg;
+    uint32_t tiles_x, tiles_y, slabs;
+    uint32_t off_image_bytes, mask_image_bytes;   // one image of offset / mask
+};
+
+// Output indices o in [0, limit) whose base o*stride - pad + c0 lies in
+// [q0 - M, q0 + len - 1 + M].
+__device__ __forceinline__ void owner_range(const Geometry& G, int M, int q0, int len, int limit, int& lo, int& hi)
+{
+    const int a0 = q0 - M + G.pad - G.c0, a1 = q0 + len - 1 + M + G.pad - G.c0;
+    lo = a0 <= 0 ? 0 : (a0 + G.stride - 1) / G.stride;
+    hi = a1 < 0 ? -1 : a1 / G.stride;
+    hi = hi < limit - 1 ? hi : limit - 1;
+}
+
+template <int KT, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
+void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
+{
+    extern __shared__ float4 owner_tile[];
+    float* acc = (float*)owner_tile;
+    const Geometry& G = a.geo;
+    const int t = threadIdx.x;
+    uint32_t rest = xcd_remap(blockIdx.x, gridDim.x);
+    const uint32_t tx = rest % og.tiles_x;
+    rest /= og.tiles_x;
+    const uint32_t ty = rest % og.tiles_y;
+    rest /= og.tiles_y;
+    const uint32_t slab = rest % og.slabs;
+    const uint32_t n = rest / og.slabs;
+    const int qx0 = (int)tx * og.TW, qy0 = (int)ty * og.TH;
+    const int tw = og.TW < G.W - qx0 ? og.TW : G.W - qx0;     // ragged last column / row of tiles
+    const int th = og.TH < G.H - qy0 ? og.TH : G.H - qy0;
+
+    for (int i = t; i < og.TH * og.TW * 8; i += NT) owner_tile[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+
+    int wlo, whi, hlo, hhi;
+    owner_range(G, og.M, qx0, tw, G.Wo, wlo, whi);
+    owner_range(G, og.M, qy0, th, G.Ho, hlo, hhi);
+    const int EW = whi - wlo + 1;
+    const int E = (EW > 0 && hhi >= hlo) ? EW * (hhi - hlo + 1) : 0;
+
+    const int sub = t & 3;
+    const int ch0 = (int)slab * 32 + sub * 8;
+    const int g = ch0 / og.Cg;
+    const int K = KT > 0 ? KT : G.K;
+    const uint32_t M2 = 2u * (uint32_t)og.M;
+    const __amdgpu_buffer_rsrc_t roff =
+        image_rsrc((const char*)a.offset + (size_t)n * og.off_image_bytes, og.off_image_bytes);
+    const __amdgpu_buffer_rsrc_t rmk =
+        image_rsrc((const char*)a.mask + (size_t)n * og.mask_image_bytes, og.mask_image_bytes);
+
+    // one sample point of output pixel (ho, wo): m*w*g of each near corner in the tile
+    // the pixel slots of a wave start their eight channel adds at different
+    // channels, so one LDS instruction of the wave spreads over all banks
+    const uint32_t rot = ((uint32_t)t >> 2) & 7u;
+    auto point = [&](int i, int j, int bxi, int byi, float2 d, float m, const float* go) {
+        // the coordinates, skip rule and floor of make_sample
+        const float x = fmaf(G.alpha, d.x, fmaf(G.alpha, (float)(i * G.dil - G.c0), (float)bxi));
+        const float y = fmaf(G.alpha, d.y, fmaf(G.alpha, (float)(j * G.dil - G.c0), (float)byi));
+        if (!(x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H)) return;
+        const float fx = floorf(x), fy = floorf(y);
+        const int x0 = (int)fx, y0 = (int)fy;
+        const int rx = x0 - qx0, ry = y0 - qy0;
+        if (rx < -1 || rx >= tw || ry < -1 || ry >= th) return;   // no corner in the tile
+        const float lx = x - fx, ly = y - fy;
+        const float hy = 1.0f - ly, hx = 1.0f - lx;
+        const float wb[4] = {hy * hx, hy * lx, ly * hx, ly * lx};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int cx = rx + (k & 1), cy = ry + (k >> 1);
+            const int qx = x0 + (k & 1), qy = y0 + (k >> 1);
+            const bool mine = (uint32_t)cx < (uint32_t)tw && (uint32_t)cy < (uint32_t)th &&
+                              (uint32_t)(qx - bxi + og.M) <= M2 && (uint32_t)(qy - byi + og.M) <= M2;
+            if (mine) {
+                const float mw = m * wb[k];
+                // 24-bit multiply: a 64-bit multiply-add here reads a register
+                // pair whose upper half may be a load still in flight
+                const uint32_t base = (__umul24((uint32_t)cy, (uint32_t)og.TW) + (uint32_t)cx) * 32u + (uint32_t)sub * 8u;
+                float v[8];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) v[c] = mw * go[c];
+                lds_add<4>((uint32_t*)acc + base, rot, v);
+                lds_add<4>((uint32_t*)acc + base, rot + 4u, v + 4);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Each lane walks the visited output pixels e = t/4, t/4 + NT/4, ...,
+    // fetching a pixel's upstream gradient and whole records at once.  (Holding
+    // the next pixel's fetch in registers as well spills at this register
+    // budget and measured slower.)
+    struct Pending {
+        float4 g0, g1;
+        PointRecord<float, (KT > 0 ? KT * KT : 1)> rec;
+    };
+    auto fetch = [&](int e, Pending& pd) {
+        const int eh = e / EW, ew = e - eh * EW;
+        const int ho = hlo + eh, wo = wlo + ew;
+        const size_t pix = ((size_t)n * G.Ho + ho) * G.Wo + wo;
+        const float4* gp = (const float4*)((const float*)a.grad_out + pix * G.C + ch0);
+        pd.g0 = gp[0];
+        pd.g1 = gp[1];
+        if constexpr (KT > 0) {
+            const uint32_t pg_img = ((uint32_t)ho * (uint32_t)G.Wo + (uint32_t)wo) * (uint32_t)G.groups + (uint32_t)g;
+            load_record<float, KT * KT>(pd.rec, roff, pg_img * (uint32_t)(KT * KT * 8), rmk,
+                                        pg_img * (uint32_t)(KT * KT * 4));
+        }
+    };
+
+    for (int e = t >> 2; e < E; e += NT / 4) {
+        Pending cur;
+        fetch(e, cur);
+        const int eh = e / EW, ew = e - eh * EW;
+        const int ho = hlo + eh, wo = wlo + ew;
+        const int bxi = wo * G.stride - G.pad + G.c0, byi = ho * G.stride - G.pad + G.c0;
+        // this lane's upstream gradient in its add order: go[c] is channel (c + rot) & 7
+        float go[8] = {cur.g0.x, cur.g0.y, cur.g0.z, cur.g0.w, cur.g1.x, cur.g1.y, cur.g1.z, cur.g1.w};
+#pragma unroll
+        for (int b = 1; b < 8; b <<= 1) {
+            float r8[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) r8[c] = (rot & (uint32_t)b) ? go[(c + b) & 7] : go[c];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) go[c] = r8[c];
+        }
+        if constexpr (KT > 0) {
+            constexpr int PK = KT * KT;
+            float mx = 0.f, inv = 1.f;
+            if (G.softmax) {
+                mx = __uint_as_float(cur.rec.mask[0]);
+#pragma unroll
+                for (int q = 1; q < PK; ++q) mx = fmaxf(mx, __uint_as_float(cur.rec.mask[q]));
+                float sum = 0.f;
+#pragma unroll
+                for (int q = 0; q < PK; ++q) sum += __expf(__uint_as_float(cur.rec.mask[q]) - mx);
+                inv = 1.0f / sum;
+            }
+#pragma unroll
+            for (int i = 0; i < KT; ++i)
+#pragma unroll
+                for (int j = 0; j < KT; ++j) {
+                    const int q = i * KT + j;
+                    float m = __uint_as_float(cur.rec.mask[q]);
+                    if (G.softmax) m = __expf(m - mx) * inv;
+                    point(i, j, bxi, byi, record_pair<float, PK>(cur.rec, q), m, go);
+                }
+        } else {
+            const size_t pg = (((size_t)n * G.Ho + ho) * G.Wo + wo) * G.groups + g;
+            const float* off = (const float*)a.offset + pg * G.P * 2;
+            const float* mk = (const float*)a.mask + pg * G.P;
+            float mx = 0.f, inv = 1.f;
+            if (G.softmax) {
+                mx = mk[0];
+                for (int q = 1; q < G.P; ++q) mx = fmaxf(mx, mk[q]);
+                float sum = 0.f;
+                for (int q = 0; q < G.P; ++q) sum += __expf(mk[q] - mx);
+                inv = 1.0f / sum;
+            }
+            for (int i = 0; i < K; ++i)
+                for (int j = 0; j < K; ++j) {
+                    const int q = i * K + j;
+                    float m = mk[q];
+                    if (G.softmax) m = __expf(m - mx) * inv;
+                    point(i, j, bxi, byi, ld2(off + 2 * q), m, go);
+                }
+        }
+    }
+    __syncthreads();
+
+    // write the tile: 16 bytes (4 channels) per lane
+    char* gin = (char*)a.grad_input + (size_t)n * G.in_image_bytes + slab * 128u;
+    for (int i = t; i < th * tw * 8; i += NT) {
+        const int px = i >> 3, q4 = i & 7;
+        const int cy = px / tw, cx = px - cy * tw;
+        const int qx = qx0 + cx, qy = qy0 + cy;
+        *(float4*)(gin + (size_t)qy * G.in_line_bytes + (size_t)qx * G.in_row_bytes + q4 * 16) =
+            owner_tile[(cy * og.TW + cx) * 8 + q4];
     }
 }
 

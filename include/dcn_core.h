@@ -90,10 +90,12 @@ int dcn_core_forward(const void* input, const void* offset, const void* mask, vo
 
 /* Backward of the forward above for an upstream gradient grad_output
  * (N, Ho, Wo, G*Cg).  Writes:
- *   grad_input  (N, H, W, G*Cg): zero-filled on `stream`, then every valid
- *               corner of every sample scatter-adds m_p * w * grad_output
- *               with float atomics, so its summation order (and its last
- *               bits) can vary from run to run;
+ *   grad_input  (N, H, W, G*Cg): for each input pixel, the sum of
+ *               m_p * w * grad_output over every valid corner of every sample
+ *               that lands on it.  The sum is formed in an order that is not
+ *               fixed (adds into on-chip memory and, for corners far from
+ *               their sample's base, float atomics), so its last bits can
+ *               vary from run to run;
  *   grad_offset (N, Ho, Wo, G, P, 2): offset_scale * m_p * sum_c g_c * dB/dx
  *               (and dB/dy), the derivative of the bilinear read taken from
  *               the right where floor() jumps;

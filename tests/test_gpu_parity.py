@@ -294,6 +294,33 @@ def test_backward_sweep(case):
     check_backward(w)
 
 
+# Shapes the owner-tiled grad_input path takes (Cg a multiple of 8, C a
+# multiple of 32): strides, dilation, negative offset_scale, tiles that do not
+# divide the map, and offset spreads that put many corners beyond the owners'
+# reach (those are added by the gradient kernel's atomics).
+OWNER_SWEEP = [  # name, N, H, W, G, Cg, K, stride, pad, dil, alpha, softmax, sigma
+    ("own_s2_d2", 1, 21, 19, 4, 8, 3, 2, 2, 2, 0.75, True, 2.0),
+    ("own_ragged", 2, 37, 29, 4, 8, 3, 1, 1, 1, 1.0, False, 1.5),
+    ("own_neg_alpha", 1, 17, 23, 2, 16, 3, 1, 1, 1, -1.25, False, 2.0),
+    ("own_k1", 1, 15, 14, 4, 8, 1, 1, 0, 1, 1.0, False, 2.0),
+    ("own_k7_s3", 1, 26, 24, 1, 32, 7, 3, 3, 1, 1.0, True, 1.5),
+    ("own_far_6", 1, 19, 21, 2, 16, 3, 1, 1, 1, 1.0, False, 6.0),
+    ("own_far_40", 1, 19, 21, 2, 16, 3, 1, 1, 1, 1.0, True, 40.0),
+    ("own_cg64", 2, 11, 13, 2, 64, 3, 1, 1, 1, 1.0, False, 3.0),
+    ("big_alpha_atomic", 1, 12, 12, 4, 8, 3, 1, 1, 1, 9.0, False, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", OWNER_SWEEP, ids=lambda c: c[0])
+def test_backward_owner_sweep(case):
+    name, N, H, W, G, Cg, K, s, p, d, a, sm, sigma = case
+    Ho, Wo = oracle.out_size(H, K, s, p, d), oracle.out_size(W, K, s, p, d)
+    w = inputs.Workload(name=name, N=N, H=H, W=W, G=G, Cg=Cg, Ho=Ho, Wo=Wo, K=K, stride=s, pad=p,
+                        dilation=d, offset_scale=a, softmax=sm, dtype="f32", offset_sigma=sigma,
+                        mask_sigma=1.0 if sm else 0.5, seed_base=93000 + 37 * len(name), backward=True)
+    check_backward(w)
+
+
 def test_backward_repeat_within_tolerance_and_autograd():
     w = inputs.scaled(inputs.WORKLOADS["c5_dcnv4_f32_56_fwdbwd"], N=2)
     t = {k: v.to(DEV) for k, v in inputs.make(w, with_grad=True).items()}
