@@ -261,7 +261,7 @@ int forward_typed(const FwdArgs& a, const Call& c, hipStream_t st)
 #ifndef DCN_OWNER_REACH
 #define DCN_OWNER_REACH 4     // corners of offsets up to this many pixels are added by owners
 #endif
-constexpr int64_t kMaxOwnerLds = 64 * 1024;
+constexpr int64_t kMaxOwnerLds = 160 * 1024;
 
 struct OwnerPlan {
     OwnerGeo og;
@@ -273,7 +273,7 @@ struct OwnerPlan {
 // The owner kernel applies to binary32 gradients whose 32-byte lane chunks
 // stay inside one group (Cg a multiple of 8) and whose 128-byte slabs tile
 // the channel row (C a multiple of 32), with 16-byte aligned grad_output and
-// grad_input.  Among tiles of at most 512 pixels it picks the one with the
+// grad_input.  Among tiles that fit the LDS it picks the one with the
 // shortest makespan: blocks per CU (256 CUs) times a block's lane slots
 // issued over its visited output pixels (idle lanes of the last pass count)
 // plus its own zero fill and store.  It declines shapes
@@ -292,10 +292,10 @@ bool plan_owner(const Call& c, const void* gout, const void* gin, OwnerPlan& pl)
     const int M = (int)mf;
     const uint32_t slabs = (uint32_t)(C / 32);
     double best = -1.0;
-    for (int nt = 256; nt <= 512; nt *= 2) {
+    for (int nt = 256; nt <= 1024; nt *= 2) {
         for (int tw = 1; tw <= 64 && tw <= c.W; ++tw)
             for (int th = 1; th <= 64 && th <= c.H; ++th) {
-                const int64_t lds = (int64_t)th * tw * 128;
+                const int64_t lds = (int64_t)th * tw * kOwnerStride * 4;
                 if (lds > kMaxOwnerLds) continue;
                 const int per_cu = (int)(160 * 1024 / lds) < 2048 / nt ? (int)(160 * 1024 / lds) : 2048 / nt;
                 const int waves = per_cu * nt / 64;
@@ -333,7 +333,10 @@ bool plan_owner(const Call& c, const void* gout, const void* gin, OwnerPlan& pl)
 template <int KT>
 int launch_owner(const BwdArgs& a, const OwnerPlan& pl, hipStream_t st)
 {
-    if (pl.threads == 512)
+    if (pl.threads == 1024)
+        hipLaunchKernelGGL((dcn_backward_input_owner<KT, 1024>), dim3((uint32_t)pl.blocks), dim3(1024), pl.lds_bytes,
+                           st, a, pl.og);
+    else if (pl.threads == 512)
         hipLaunchKernelGGL((dcn_backward_input_owner<KT, 512>), dim3((uint32_t)pl.blocks), dim3(512), pl.lds_bytes,
                            st, a, pl.og);
     else

@@ -948,46 +948,60 @@ __global__ __launch_bounds__(kBlock) void dcn_backward_kernel(BwdArgs a)
 // rare corners that are not near (offsets beyond the reach M was sized for)
 // are added afterwards, with atomics, by dcn_backward_kernel.
 //
-// LDS keeps the tile pixel by pixel, 32 floats each (channel order); lane
-// chunk `sub` adds into floats [8*sub, 8*sub + 8) of a pixel.
+// LDS keeps the tile pixel by pixel, 32 floats each in channel order, at a
+// stride of 34 floats: the pixels a wave's lanes add into then start on
+// different banks, and a lane's eight channels sit at fixed offsets from one
+// 8-byte aligned address.  Lane chunk `sub` adds into floats [8*sub, 8*sub + 8) of a pixel.
+
 // Float adds into LDS through compare-and-swap.  On gfx950 an LDS float
 // atomic add (ds_add_f32) retires about one lane every few cycles per CU,
 // while integer LDS atomics run at the rate of plain LDS accesses; a CAS loop
-// uses the latter.  The NV adds of one lane go to slots (c + rot) & 7 of an
-// 8-float chunk and are issued together: read the old values, swap in
-// old + v, and retry only the slots another lane changed in between (each
-// retry follows some lane's successful swap, so the loop ends).
-template <int NV>
-__device__ __forceinline__ void lds_add(uint32_t* chunk, uint32_t rot, const float* v)
+// uses the latter, on 64-bit words holding two floats each.  The eight adds
+// of one lane (consecutive floats) go out together as four swaps of
+// old + v; a lane whose swap found another value (another lane added in
+// between) repeats the round for its unfinished words, and finished words
+// then swap a value for itself, which never changes memory.  Each failed
+// swap follows some lane's successful one, so the loop ends.
+__device__ __forceinline__ uint64_t add_pair(uint64_t w, float a, float b)
 {
-    uint32_t old[NV], got[NV];
+    const uint32_t lo = __float_as_uint(__uint_as_float((uint32_t)w) + a);
+    const uint32_t hi = __float_as_uint(__uint_as_float((uint32_t)(w >> 32)) + b);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ void lds_add8(uint64_t* p, const float (&v)[8])
+{
+    uint64_t cur[4], des[4], got[4];
 #pragma unroll
-    for (int c = 0; c < NV; ++c)
-        old[c] = __hip_atomic_load(chunk + ((c + rot) & 7u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    bool again = false;
+    for (int j = 0; j < 4; ++j) cur[j] = __hip_atomic_load(p + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
-    for (int c = 0; c < NV; ++c) {
-        got[c] = old[c];
-        __hip_atomic_compare_exchange_strong(chunk + ((c + rot) & 7u), &got[c],
-                                             __float_as_uint(__uint_as_float(old[c]) + v[c]),
-                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int j = 0; j < 4; ++j) {
+        des[j] = add_pair(cur[j], v[2 * j], v[2 * j + 1]);
+        got[j] = cur[j];
+        __hip_atomic_compare_exchange_strong(p + j, &got[j], des[j], __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_WORKGROUP);
     }
+    uint32_t pend = 0;
 #pragma unroll
-    for (int c = 0; c < NV; ++c) again |= got[c] != old[c];
-    while (again) {
-        again = false;
+    for (int j = 0; j < 4; ++j) pend |= (got[j] != cur[j] ? 1u : 0u) << j;
+    while (pend) {
 #pragma unroll
-        for (int c = 0; c < NV; ++c) {
-            if (got[c] != old[c]) {
-                old[c] = got[c];
-                __hip_atomic_compare_exchange_strong(chunk + ((c + rot) & 7u), &got[c],
-                                                     __float_as_uint(__uint_as_float(old[c]) + v[c]),
-                                                     __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                again |= got[c] != old[c];
-            }
+        for (int j = 0; j < 4; ++j) {
+            const bool retry = (pend >> j) & 1u;
+            cur[j] = retry ? got[j] : des[j];
+            des[j] = retry ? add_pair(got[j], v[2 * j], v[2 * j + 1]) : des[j];
+            got[j] = cur[j];
+            __hip_atomic_compare_exchange_strong(p + j, &got[j], des[j], __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
         }
+        uint32_t again = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) again |= (((pend >> j) & 1u) && got[j] != cur[j] ? 1u : 0u) << j;
+        pend = again;
     }
 }
+
+constexpr int kOwnerStride = 34;   // floats per pixel in the LDS tile (even: 8-byte words)
 
 struct OwnerGeo {
     int TH, TW, M, Cg;
@@ -1009,8 +1023,7 @@ template <int KT, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
 void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
 {
-    extern __shared__ float4 owner_tile[];
-    float* acc = (float*)owner_tile;
+    extern __shared__ float owner_tile[];
     const Geometry& G = a.geo;
     const int t = threadIdx.x;
     uint32_t rest = xcd_remap(blockIdx.x, gridDim.x);
@@ -1024,7 +1037,7 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
     const int tw = og.TW < G.W - qx0 ? og.TW : G.W - qx0;     // ragged last column / row of tiles
     const int th = og.TH < G.H - qy0 ? og.TH : G.H - qy0;
 
-    for (int i = t; i < og.TH * og.TW * 8; i += NT) owner_tile[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = t; i < og.TH * og.TW * kOwnerStride; i += NT) owner_tile[i] = 0.f;
     __syncthreads();
 
     int wlo, whi, hlo, hhi;
@@ -1044,9 +1057,6 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
         image_rsrc((const char*)a.mask + (size_t)n * og.mask_image_bytes, og.mask_image_bytes);
 
     // one sample point of output pixel (ho, wo): m*w*g of each near corner in the tile
-    // the pixel slots of a wave start their eight channel adds at different
-    // channels, so one LDS instruction of the wave spreads over all banks
-    const uint32_t rot = ((uint32_t)t >> 2) & 7u;
     auto point = [&](int i, int j, int bxi, int byi, float2 d, float m, const float* go) {
         // the coordinates, skip rule and floor of make_sample
         const float x = fmaf(G.alpha, d.x, fmaf(G.alpha, (float)(i * G.dil - G.c0), (float)bxi));
@@ -1069,19 +1079,19 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
                 const float mw = m * wb[k];
                 // 24-bit multiply: a 64-bit multiply-add here reads a register
                 // pair whose upper half may be a load still in flight
-                const uint32_t base = (__umul24((uint32_t)cy, (uint32_t)og.TW) + (uint32_t)cx) * 32u + (uint32_t)sub * 8u;
+                const uint32_t base = (__umul24((uint32_t)cy, (uint32_t)og.TW) + (uint32_t)cx) * (uint32_t)kOwnerStride +
+                                      (uint32_t)sub * 8u;
                 float v[8];
 #pragma unroll
                 for (int c = 0; c < 8; ++c) v[c] = mw * go[c];
-                lds_add<4>((uint32_t*)acc + base, rot, v);
-                lds_add<4>((uint32_t*)acc + base, rot + 4u, v + 4);
+                lds_add8((uint64_t*)(owner_tile + base), v);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // Each lane walks the visited output pixels e = t/4, t/4 + NT/4, ...,
-    // fetching a pixel's upstream gradient and whole records at once.  (Holding
+    // Each lane walks the visited output pixels in steps of NT/4, fetching a
+    // pixel's upstream gradient and whole records at once.  (Holding
     // the next pixel's fetch in registers as well spills at this register
     // budget and measured slower.)
     struct Pending {
@@ -1102,22 +1112,16 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
         }
     };
 
-    for (int e = t >> 2; e < E; e += NT / 4) {
+    // The 16 pixel slots of a wave take pixels NT/64 apart, so that two
+    // lanes of one LDS instruction rarely add into the same address.
+    const int e0 = (((t & 63) >> 2) * (NT / 64)) + (t >> 6);
+    for (int e = e0; e < E; e += NT / 4) {
         Pending cur;
         fetch(e, cur);
         const int eh = e / EW, ew = e - eh * EW;
         const int ho = hlo + eh, wo = wlo + ew;
         const int bxi = wo * G.stride - G.pad + G.c0, byi = ho * G.stride - G.pad + G.c0;
-        // this lane's upstream gradient in its add order: go[c] is channel (c + rot) & 7
-        float go[8] = {cur.g0.x, cur.g0.y, cur.g0.z, cur.g0.w, cur.g1.x, cur.g1.y, cur.g1.z, cur.g1.w};
-#pragma unroll
-        for (int b = 1; b < 8; b <<= 1) {
-            float r8[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) r8[c] = (rot & (uint32_t)b) ? go[(c + b) & 7] : go[c];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) go[c] = r8[c];
-        }
+        const float go[8] = {cur.g0.x, cur.g0.y, cur.g0.z, cur.g0.w, cur.g1.x, cur.g1.y, cur.g1.z, cur.g1.w};
         if constexpr (KT > 0) {
             constexpr int PK = KT * KT;
             float mx = 0.f, inv = 1.f;
@@ -1168,8 +1172,9 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
         const int px = i >> 3, q4 = i & 7;
         const int cy = px / tw, cx = px - cy * tw;
         const int qx = qx0 + cx, qy = qy0 + cy;
+        const float* src = owner_tile + (cy * og.TW + cx) * kOwnerStride + q4 * 4;
         *(float4*)(gin + (size_t)qy * G.in_line_bytes + (size_t)qx * G.in_row_bytes + q4 * 16) =
-            owner_tile[(cy * og.TW + cx) * 8 + q4];
+            make_float4(src[0], src[1], src[2], src[3]);
     }
 }
 
