@@ -345,6 +345,31 @@ int launch_owner(const BwdArgs& a, const OwnerPlan& pl, hipStream_t st)
     return launch_status();
 }
 
+#ifndef DCN_USE_GRAD_TILES
+#define DCN_USE_GRAD_TILES 1  // grad_offset / grad_mask from staged input tiles where the shape allows
+#endif
+
+template <int KT, int NT>
+int launch_grad_tiled(const BwdArgs& a, const Call& c, const TilePlan& pl, hipStream_t st)
+{
+    if (c.softmax)
+        hipLaunchKernelGGL((dcn_backward_grad_tiled<KT, NT, true>), dim3((uint32_t)pl.blocks), dim3(NT), pl.lds_bytes,
+                           st, a, pl.tg);
+    else
+        hipLaunchKernelGGL((dcn_backward_grad_tiled<KT, NT, false>), dim3((uint32_t)pl.blocks), dim3(NT), pl.lds_bytes,
+                           st, a, pl.tg);
+    return launch_status();
+}
+
+int backward_grad_tiled(const BwdArgs& base, const Call& c, const TilePlan& pl, hipStream_t st)
+{
+    BwdArgs a = base;
+    a.geo = make_geometry(c, 8);
+    if (pl.threads == 512)
+        return c.K == 3 ? launch_grad_tiled<3, 512>(a, c, pl, st) : launch_grad_tiled<0, 512>(a, c, pl, st);
+    return c.K == 3 ? launch_grad_tiled<3, 256>(a, c, pl, st) : launch_grad_tiled<0, 256>(a, c, pl, st);
+}
+
 template <int LB, int L>
 int backward_variant(const BwdArgs& base, const Call& c, hipStream_t st)
 {
@@ -466,6 +491,8 @@ extern "C" int dcn_core_backward(const void* input, const void* offset, const vo
         rc = zero_fill((float*)grad_input, (int64_t)N * H * W * G * Cg, st);
     }
     if (rc != DCN_OK) return rc;
+    TilePlan tp;
+    if (DCN_USE_GRAD_TILES && plan_tiles(c, input, grad_output, tp)) return backward_grad_tiled(a, c, tp, st);
     return LB == 16 ? backward_lanes<16>(a, c, st, L) : backward_lanes<4>(a, c, st, L);
 }
 

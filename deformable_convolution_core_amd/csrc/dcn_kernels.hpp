@@ -936,6 +936,238 @@ __global__ __launch_bounds__(kBlock) void dcn_backward_kernel(BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Tiled gradient kernel (binary32): grad_offset and grad_mask, plus the
+// atomic adds of corners that are not near their sample's base (the owner
+// kernel has written every near one).  The input region of an output tile is
+// staged in LDS exactly as for the forward; a lane owns 8 channels of one
+// output pixel, reads its corners from the region (or, outside it, from
+// global memory), and the lanes of a group sum their partial dot products
+// with cross-lane shuffles.
+struct GradPoint {
+    uint32_t raw[4][8];
+    float lx, ly;
+    int x0, y0;
+    bool inmap;
+};
+
+__device__ __forceinline__ GradPoint tiled_fetch_grad(const Geometry& G, const TiledLane& L, const char* lds,
+                                                      __amdgpu_buffer_rsrc_t rin, float tapx, float tapy, float2 d)
+{
+    GradPoint pt;
+    const float x = fmaf(G.alpha, d.x, fmaf(G.alpha, tapx, L.bx));
+    const float y = fmaf(G.alpha, d.y, fmaf(G.alpha, tapy, L.by));
+    // the skip rule of the definition (false for NaN)
+    pt.inmap = x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H;
+    const float fx = floorf(x), fy = floorf(y);
+    pt.x0 = (int)fx;
+    pt.y0 = (int)fy;
+    pt.lx = x - fx;
+    pt.ly = y - fy;
+    const uint32_t ix = (uint32_t)(pt.x0 - L.x_lo), iy = (uint32_t)(pt.y0 - L.y_lo);
+    if ((ix < L.xlim) & (iy < L.ylim) & pt.inmap) {
+        const uint32_t a0 = (__umul24(iy, L.RW) + ix) * 128u + L.lane_first;
+        const uint32_t a1 = a0 ^ 16u;
+        const uint32_t ca[4] = {0u, 128u, L.RWB, L.RWB + 128u};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint4 v0 = *(const uint4*)(lds + a0 + ca[k]);
+            const uint4 v1 = *(const uint4*)(lds + a1 + ca[k]);
+            pt.raw[k][0] = v0.x; pt.raw[k][1] = v0.y; pt.raw[k][2] = v0.z; pt.raw[k][3] = v0.w;
+            pt.raw[k][4] = v1.x; pt.raw[k][5] = v1.y; pt.raw[k][6] = v1.z; pt.raw[k][7] = v1.w;
+        }
+    } else {
+        const int x0 = pt.inmap ? pt.x0 : -2, y0 = pt.inmap ? pt.y0 : -2;
+        const bool vx0 = (uint32_t)x0 < (uint32_t)G.W, vx1 = (uint32_t)(x0 + 1) < (uint32_t)G.W;
+        const bool vy0 = (uint32_t)y0 < (uint32_t)G.H, vy1 = (uint32_t)(y0 + 1) < (uint32_t)G.H;
+        const bool vk[4] = {vy0 && vx0, vy0 && vx1, vy1 && vx0, vy1 && vx1};
+        const uint32_t a00 = (uint32_t)y0 * G.in_line_bytes + (uint32_t)x0 * G.in_row_bytes;
+        const uint32_t ck[4] = {0u, G.in_row_bytes, G.in_line_bytes, G.in_line_bytes + G.in_row_bytes};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t o0 = vk[k] ? a00 + ck[k] + L.gl_first : kOOB;
+            const uint32_t o1 = vk[k] ? a00 + ck[k] + L.gl_second : kOOB;
+            const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rin, o0, 0, 0);
+            const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rin, o1, 0, 0);
+            pt.raw[k][0] = v0[0]; pt.raw[k][1] = v0[1]; pt.raw[k][2] = v0[2]; pt.raw[k][3] = v0[3];
+            pt.raw[k][4] = v1[0]; pt.raw[k][5] = v1[1]; pt.raw[k][6] = v1[2]; pt.raw[k][7] = v1[3];
+        }
+    }
+    return pt;
+}
+
+template <int KT, int NT, bool SOFTMAX>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DCN_TILE_WAVES_PER_EU)))
+void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
+{
+    extern __shared__ uint4 region[];
+    const Geometry& G = a.geo;
+    const int t = threadIdx.x;
+    const TileCoord cur = tile_coord(G, tg, xcd_remap(blockIdx.x, gridDim.x));
+    stage_rows<NT>(G, tg, a.input, cur, region, 0, tg.RH, t);
+
+    const int p = t >> 2, sub = t & 3;
+    const int py = p / tg.TW, px = p - py * tg.TW;
+    const int P = KT > 0 ? KT * KT : G.P;
+    const int swp = p & 1;
+    TiledLane L;
+    L.xlim = (uint32_t)(tg.RW - 1);
+    L.ylim = (uint32_t)(tg.RH - 1);
+    L.lane_first = (uint32_t)sub * 32u + (uint32_t)swp * 16u;
+    L.RW = (uint32_t)tg.RW;
+    L.RWB = (uint32_t)tg.RW * 128u;
+    const int ho = cur.ho0 + py, wo = cur.wo0 + px;
+    const bool active = p < tg.TH * tg.TW && ho < G.Ho && wo < G.Wo;
+    const uint32_t g = cur.slab * (4u >> tg.gshift) + ((uint32_t)sub >> tg.gshift);
+    const bool leader = (sub & ((1 << tg.gshift) - 1)) == 0;
+    const uint32_t pg_img = active ? ((uint32_t)ho * (uint32_t)G.Wo + (uint32_t)wo) * (uint32_t)G.groups + g : 0u;
+    const __amdgpu_buffer_rsrc_t rin =
+        image_rsrc((const char*)a.input + (size_t)cur.n * G.in_image_bytes, G.in_image_bytes);
+    const __amdgpu_buffer_rsrc_t roff =
+        image_rsrc((const char*)a.offset + (size_t)cur.n * tg.off_image_bytes, tg.off_image_bytes);
+    const __amdgpu_buffer_rsrc_t rmk =
+        image_rsrc((const char*)a.mask + (size_t)cur.n * tg.mask_image_bytes, tg.mask_image_bytes);
+    const uint32_t voff = pg_img * (uint32_t)(P * 8);
+    const uint32_t vmk = pg_img * (uint32_t)(P * 4);
+    const int bxi = wo * G.stride - G.pad + G.c0, byi = ho * G.stride - G.pad + G.c0;
+    L.bx = (float)bxi;
+    L.by = (float)byi;
+    L.x_lo = cur.x_lo;
+    L.y_lo = cur.y_lo;
+    L.gl_first = cur.slab * 128u + L.lane_first;
+    L.gl_second = L.gl_first ^ 16u;
+    const uint32_t M2 = 2u * (uint32_t)a.near_m;
+
+    // upstream gradient of this lane's channels, in the order its corner reads arrive
+    float go[8];
+    const size_t pix = ((size_t)cur.n * G.Ho + (size_t)ho) * G.Wo + wo;
+    char* gin = (char*)a.grad_input + (size_t)cur.n * G.in_image_bytes;
+    float* goff = a.grad_offset + ((size_t)cur.n * G.Ho * G.Wo * G.groups + pg_img) * P * 2;
+    float* gmk = a.grad_mask + ((size_t)cur.n * G.Ho * G.Wo * G.groups + pg_img) * P;
+    if (active) {
+        const char* gp = (const char*)a.grad_out + pix * G.C * 4 + cur.slab * 128u + (uint32_t)sub * 32u;
+        const float4 h0 = *(const float4*)(gp + swp * 16), h1 = *(const float4*)(gp + (swp ^ 1) * 16);
+        go[0] = h0.x; go[1] = h0.y; go[2] = h0.z; go[3] = h0.w;
+        go[4] = h1.x; go[5] = h1.y; go[6] = h1.z; go[7] = h1.w;
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) go[c] = 0.f;
+    }
+
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const char* lds = (const char*)region;
+
+    // one point: returns gm, and writes grad_offset; far corners go to grad_input
+    auto point = [&](int q, float2 d, float m) -> float {
+        const GradPoint pt = tiled_fetch_grad(G, L, lds, rin, tg.tap_x[q], tg.tap_y[q], d);
+        float sk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float acc = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc = fmaf(go[c], __uint_as_float(pt.raw[k][c]), acc);
+            sk[k] = acc;
+        }
+        const float hy = 1.0f - pt.ly, hx = 1.0f - pt.lx;
+        const float wb[4] = {hy * hx, hy * pt.lx, pt.ly * hx, pt.ly * pt.lx};
+        float gm = wb[0] * sk[0] + wb[1] * sk[1] + wb[2] * sk[2] + wb[3] * sk[3];
+        float gdx = hy * (sk[1] - sk[0]) + pt.ly * (sk[3] - sk[2]);
+        float gdy = hx * (sk[2] - sk[0]) + pt.lx * (sk[3] - sk[1]);
+        if (tg.gshift >= 1) {
+            gm += __shfl_xor(gm, 1);
+            gdx += __shfl_xor(gdx, 1);
+            gdy += __shfl_xor(gdy, 1);
+        }
+        if (tg.gshift >= 2) {
+            gm += __shfl_xor(gm, 2);
+            gdx += __shfl_xor(gdx, 2);
+            gdy += __shfl_xor(gdy, 2);
+        }
+        if (!pt.inmap) { gm = 0.f; gdx = 0.f; gdy = 0.f; }
+        if (active && leader) *(float2*)(goff + 2 * q) = make_float2(G.alpha * m * gdx, G.alpha * m * gdy);
+        // corners beyond the owners' reach
+        if (active && pt.inmap) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int qx = pt.x0 + (k & 1), qy = pt.y0 + (k >> 1);
+                const bool valid = (uint32_t)qx < (uint32_t)G.W && (uint32_t)qy < (uint32_t)G.H;
+                const bool near = a.near_m >= 0 && (uint32_t)(qx - bxi + a.near_m) <= M2 &&
+                                  (uint32_t)(qy - byi + a.near_m) <= M2;
+                if (valid && !near) {
+                    const float mw = m * wb[k];
+                    float* dst = (float*)(gin + (size_t)qy * G.in_line_bytes + (size_t)qx * G.in_row_bytes + L.gl_first);
+                    float* dst2 = (float*)(gin + (size_t)qy * G.in_line_bytes + (size_t)qx * G.in_row_bytes + L.gl_second);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) atomicAdd(dst + c, mw * go[c]);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) atomicAdd(dst2 + c, mw * go[4 + c]);
+                }
+            }
+        }
+        return gm;
+    };
+
+    if constexpr (KT > 0) {
+        constexpr int PK = KT * KT;
+        PointRecord<float, PK> rec;
+        load_record<float, PK>(rec, roff, voff, rmk, vmk);
+        float mx = 0.f, inv = 1.f;
+        if constexpr (SOFTMAX) {
+            mx = __uint_as_float(rec.mask[0]);
+#pragma unroll
+            for (int q = 1; q < PK; ++q) mx = fmaxf(mx, __uint_as_float(rec.mask[q]));
+            float sum = 0.f;
+#pragma unroll
+            for (int q = 0; q < PK; ++q) sum += __expf(__uint_as_float(rec.mask[q]) - mx);
+            inv = 1.0f / sum;
+        }
+        float gms[PK];
+        float dot = 0.f;
+#pragma unroll
+        for (int q = 0; q < PK; ++q) {
+            float m = __uint_as_float(rec.mask[q]);
+            if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
+            gms[q] = point(q, record_pair<float, PK>(rec, q), m);
+            dot = fmaf(m, gms[q], dot);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (active && leader) {
+#pragma unroll
+            for (int q = 0; q < PK; ++q) {
+                float v = gms[q];
+                if constexpr (SOFTMAX) v = __expf(__uint_as_float(rec.mask[q]) - mx) * inv * (v - dot);
+                gmk[q] = v;
+            }
+        }
+    } else {
+        float mx = 0.f, inv = 1.f;
+        if constexpr (SOFTMAX) {
+            mx = load_mask_value<float>(rmk, vmk, 0);
+            for (int q = 1; q < P; ++q) mx = fmaxf(mx, load_mask_value<float>(rmk, vmk, q));
+            float sum = 0.f;
+            for (int q = 0; q < P; ++q) sum += __expf(load_mask_value<float>(rmk, vmk, q) - mx);
+            inv = 1.0f / sum;
+        }
+        float dot = 0.f;
+        for (int q = 0; q < P; ++q) {
+            float m = load_mask_value<float>(rmk, vmk, q);
+            if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
+            const float gm = point(q, load_offset_pair<float>(roff, voff, q), m);
+            dot = fmaf(m, gm, dot);
+            if (active && leader) gmk[q] = gm;
+        }
+        if constexpr (SOFTMAX) {
+            if (active && leader) {
+                for (int q = 0; q < P; ++q) {
+                    const float m = __expf(load_mask_value<float>(rmk, vmk, q) - mx) * inv;
+                    gmk[q] = m * (gmk[q] - dot);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // grad_input by owner.  A workgroup owns a TH x TW tile of input pixels and
 // one 128-byte slab of their channels (32 binary32 channels, four lanes of
 // eight channels per pixel).  A corner q of a sample of output pixel o is
