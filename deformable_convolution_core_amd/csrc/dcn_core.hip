@@ -191,28 +191,11 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan)
     return true;
 }
 
-#ifndef DCN_TILE_PERSIST
-#define DCN_TILE_PERSIST 0    // 1: persistent double-buffered workgroups where two regions fit in LDS
-#endif
-
 template <typename T, int KT, int NT, bool SM>
 int launch_tiled(const FwdArgs& a, const TilePlan& pl, hipStream_t st)
 {
-    uint32_t grid = (uint32_t)pl.blocks, per_block = 1, lds = pl.lds_bytes;
-    int cus = 0, dev = 0;
-    if (DCN_TILE_PERSIST && 2 * pl.lds_bytes <= 160 * 1024 && hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0 &&
-        pl.blocks > (uint64_t)cus) {
-        per_block = (uint32_t)((pl.blocks + cus - 1) / cus);
-        grid = (uint32_t)((pl.blocks + per_block - 1) / per_block);
-        lds = 2 * pl.lds_bytes;
-    }
-    if (per_block > 1)
-        hipLaunchKernelGGL((dcn_forward_tiled<T, KT, NT, SM, true>), dim3(grid), dim3(NT), lds, st, a, pl.tg,
-                           (uint32_t)pl.blocks, per_block);
-    else
-        hipLaunchKernelGGL((dcn_forward_tiled<T, KT, NT, SM, false>), dim3(grid), dim3(NT), lds, st, a, pl.tg,
-                           (uint32_t)pl.blocks, per_block);
+    hipLaunchKernelGGL((dcn_forward_tiled<T, KT, NT, SM>), dim3((uint32_t)pl.blocks), dim3(NT), pl.lds_bytes, st, a,
+                       pl.tg);
     return launch_status();
 }
 

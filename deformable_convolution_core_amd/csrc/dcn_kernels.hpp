@@ -651,16 +651,13 @@ __device__ __forceinline__ void stage_rows(const Geometry& G, const TileGeo& tg,
     }
 }
 
-// Persistent tiled forward: a workgroup walks the contiguous tile range
-// [first, first + count).  With two LDS buffers, tile k is computed from one
-// while tile k+1's region streams into the other; the next tile's rows are
-// issued in slices between points so that waits on a point's own loads never
-// have to drain a whole region's worth of earlier loads (vector memory
-// counters retire in order).  With one buffer (count == 1) it stages, waits
-// and computes.
-template <typename T, int KT, int NT, bool SOFTMAX, bool PERSIST>
+// Tiled forward: a workgroup stages the input region of one output tile into
+// LDS, then each lane accumulates 32 bytes of channels of one output pixel.
+// The lane's offset/mask record is requested before the wait for the region,
+// so the two memory latencies overlap.
+template <typename T, int KT, int NT, bool SOFTMAX>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DCN_TILE_WAVES_PER_EU)))
-void dcn_forward_tiled(FwdArgs a, TileGeo tg, uint32_t tiles_total, uint32_t tiles_per_block)
+void dcn_forward_tiled(FwdArgs a, TileGeo tg)
 {
     constexpr int EB = Elem<T>::bytes;
     constexpr int CPL = 32 / EB;        // channels per lane
@@ -668,18 +665,11 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg, uint32_t tiles_total, uint32_t til
     extern __shared__ uint4 region[];
     const Geometry& G = a.geo;
     const int t = threadIdx.x;
-    const uint32_t region_elems = (uint32_t)(tg.RH * tg.RW * 8);
 
-    const uint32_t first = xcd_remap(blockIdx.x, gridDim.x) * tiles_per_block;
-    if (first >= tiles_total) return;                       // whole workgroup
-    const uint32_t last = first + tiles_per_block < tiles_total ? first + tiles_per_block : tiles_total;
-
-    TileCoord cur = tile_coord(G, tg, first);
+    const TileCoord cur = tile_coord(G, tg, xcd_remap(blockIdx.x, gridDim.x));
     stage_rows<NT>(G, tg, a.input, cur, region, 0, tg.RH, t);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
 
-    // ---- this lane: 32 bytes of channels of one output pixel of each tile
+    // ---- this lane: 32 bytes of channels of one output pixel of the tile
     const int p = t >> 2, sub = t & 3;
     const int py = p / tg.TW, px = p - py * tg.TW;
     const int P = KT > 0 ? KT * KT : G.P;
@@ -690,133 +680,116 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg, uint32_t tiles_total, uint32_t til
     L.lane_first = (uint32_t)sub * 32u + (uint32_t)swp * 16u;
     L.RW = (uint32_t)tg.RW;
     L.RWB = (uint32_t)tg.RW * 128u;
+    const int ho = cur.ho0 + py, wo = cur.wo0 + px;
+    const bool active = p < tg.TH * tg.TW && ho < G.Ho && wo < G.Wo;
+    const uint32_t g = cur.slab * (4u >> tg.gshift) + ((uint32_t)sub >> tg.gshift);
+    const uint32_t pg_img = active ? ((uint32_t)ho * (uint32_t)G.Wo + (uint32_t)wo) * (uint32_t)G.groups + g : 0u;
+    const __amdgpu_buffer_rsrc_t rin =
+        image_rsrc((const char*)a.input + (size_t)cur.n * G.in_image_bytes, G.in_image_bytes);
+    const __amdgpu_buffer_rsrc_t roff =
+        image_rsrc((const char*)a.offset + (size_t)cur.n * tg.off_image_bytes, tg.off_image_bytes);
+    const __amdgpu_buffer_rsrc_t rmk =
+        image_rsrc((const char*)a.mask + (size_t)cur.n * tg.mask_image_bytes, tg.mask_image_bytes);
+    const uint32_t voff = pg_img * (uint32_t)(P * 2 * EB);
+    const uint32_t vmk = pg_img * (uint32_t)(P * EB);
+    L.bx = (float)(wo * G.stride - G.pad + G.c0);
+    L.by = (float)(ho * G.stride - G.pad + G.c0);
+    L.x_lo = cur.x_lo;
+    L.y_lo = cur.y_lo;
+    L.gl_first = cur.slab * 128u + L.lane_first;
+    L.gl_second = L.gl_first ^ 16u;
+    const char* lds = (const char*)region;
 
-    for (uint32_t tile = first; tile < last; ++tile) {
-        const uint32_t k = tile - first;
-        uint4* buf = region + (k & 1u) * region_elems;
-        uint4* nbuf = region + ((k + 1u) & 1u) * region_elems;
-        const bool has_next = PERSIST && tile + 1 < last;
-        const TileCoord nxt = tile_coord(G, tg, has_next ? tile + 1 : tile);
+    auto mval = [&](uint32_t raw) {
+        return Elem<T>::bytes == 4 ? __uint_as_float(raw) : Elem<T>::widen(raw);
+    };
+    float acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
 
-        const int ho = cur.ho0 + py, wo = cur.wo0 + px;
-        const bool active = p < tg.TH * tg.TW && ho < G.Ho && wo < G.Wo;
-        const uint32_t g = cur.slab * (4u >> tg.gshift) + ((uint32_t)sub >> tg.gshift);
-        const uint32_t pg_img = active ? ((uint32_t)ho * (uint32_t)G.Wo + (uint32_t)wo) * (uint32_t)G.groups + g : 0u;
-        const __amdgpu_buffer_rsrc_t rin =
-            image_rsrc((const char*)a.input + (size_t)cur.n * G.in_image_bytes, G.in_image_bytes);
-        const __amdgpu_buffer_rsrc_t roff =
-            image_rsrc((const char*)a.offset + (size_t)cur.n * tg.off_image_bytes, tg.off_image_bytes);
-        const __amdgpu_buffer_rsrc_t rmk =
-            image_rsrc((const char*)a.mask + (size_t)cur.n * tg.mask_image_bytes, tg.mask_image_bytes);
-        const uint32_t voff = pg_img * (uint32_t)(P * 2 * EB);
-        const uint32_t vmk = pg_img * (uint32_t)(P * EB);
-        L.bx = (float)(wo * G.stride - G.pad + G.c0);
-        L.by = (float)(ho * G.stride - G.pad + G.c0);
-        L.x_lo = cur.x_lo;
-        L.y_lo = cur.y_lo;
-        L.gl_first = cur.slab * 128u + L.lane_first;
-        L.gl_second = L.gl_first ^ 16u;
-        const char* lds = (const char*)buf;
-
-        auto mval = [&](uint32_t raw) {
-            return Elem<T>::bytes == 4 ? __uint_as_float(raw) : Elem<T>::widen(raw);
-        };
-        float acc[CPL];
+    if constexpr (KT > 0) {
+        // K fixed: the (pixel, group)'s offset and mask records come in once
+        // (a per-point load would re-touch the same cache lines P times)
+        // and the points are unrolled so the record stays in registers.
+        constexpr int PK = KT * KT;
+        PointRecord<T, PK> rec;
+        load_record<T, PK>(rec, roff, voff, rmk, vmk);
+        __builtin_amdgcn_s_waitcnt(0);   // the region (and the record) have landed
+        __syncthreads();
+        float mx = 0.f, inv = 1.f;
+        if constexpr (SOFTMAX) {
+            mx = mval(rec.mask[0]);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
-
-        if constexpr (KT > 0) {
-            // K fixed: the (pixel, group)'s offset and mask records come in once
-            // (a per-point load would re-touch the same cache lines P times)
-            // and the points are unrolled so the record stays in registers.
-            constexpr int PK = KT * KT;
-            PointRecord<T, PK> rec;
-            load_record<T, PK>(rec, roff, voff, rmk, vmk);
-            float mx = 0.f, inv = 1.f;
-            if constexpr (SOFTMAX) {
-                mx = mval(rec.mask[0]);
+            for (int q = 1; q < PK; ++q) mx = fmaxf(mx, mval(rec.mask[q]));
+            float sum = 0.f;
 #pragma unroll
-                for (int q = 1; q < PK; ++q) mx = fmaxf(mx, mval(rec.mask[q]));
-                float sum = 0.f;
+            for (int q = 0; q < PK; ++q) sum += __expf(mval(rec.mask[q]) - mx);
+            inv = 1.0f / sum;
+        }
 #pragma unroll
-                for (int q = 0; q < PK; ++q) sum += __expf(mval(rec.mask[q]) - mx);
-                inv = 1.0f / sum;
-            }
-#pragma unroll
-            for (int q = 0; q < PK; ++q) {
-                if (active) {
-                    float m = mval(rec.mask[q]);
-                    if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
-                    const TiledPoint pt = tiled_fetch<T>(G, L, lds, rin, tg.tap_x[q], tg.tap_y[q], record_pair<T, PK>(rec, q), m);
-                    tiled_accumulate<T, CPL>(pt, acc);
-                }
-                if constexpr (PERSIST)
-                    if (has_next) stage_rows<NT>(G, tg, a.input, nxt, nbuf, (q * tg.RH) / PK, ((q + 1) * tg.RH) / PK, t);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        } else {
-            float mx = 0.f, inv = 1.f;
-            if constexpr (SOFTMAX) {
-                mx = load_mask_value<T>(rmk, vmk, 0);
-                for (int q = 1; q < P; ++q) mx = fmaxf(mx, load_mask_value<T>(rmk, vmk, q));
-                float sum = 0.f;
-                for (int q = 0; q < P; ++q) sum += __expf(load_mask_value<T>(rmk, vmk, q) - mx);
-                inv = 1.0f / sum;
-            }
-            auto fetch = [&](int q, const RawPair<T>& d, uint32_t mraw) {
-                float m = mval(mraw);
+        for (int q = 0; q < PK; ++q) {
+            if (active) {
+                float m = mval(rec.mask[q]);
                 if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
-                return tiled_fetch<T>(G, L, lds, rin, tg.tap_x[q], tg.tap_y[q], widen_pair<T>(d), m);
-            };
-
-            // Software pipeline over the points, two per (rolled) iteration: the
-            // corner reads of point q+1 are in flight while point q accumulates,
-            // and each point's offsets and mask are requested two points ahead.
-            // Rolled, the compiler cannot hoist further points' reads and run
-            // out of registers.
-            RawPair<T> dA, dB;
-            uint32_t mA = 0u, mB = 0u;
-            dA = load_offset_raw<T>(roff, voff, 0);
-            mA = load_mask_raw<T>(rmk, vmk, 0);
-            if (P > 1) { dB = load_offset_raw<T>(roff, voff, 1); mB = load_mask_raw<T>(rmk, vmk, 1); }
-            TiledPoint ptA, ptB;
-            if (active) ptA = fetch(0, dA, mA);
-            if (P > 2) { dA = load_offset_raw<T>(roff, voff, 2); mA = load_mask_raw<T>(rmk, vmk, 2); }
-            int q = 0;
-            DCN_UNROLL(1)
-            for (; q + 1 < P; q += 2) {
-                // here: ptA = point q (reads issued), dB = point q+1, dA = point q+2
-                if (active) ptB = fetch(q + 1, dB, mB);
-                if (q + 3 < P) { dB = load_offset_raw<T>(roff, voff, q + 3); mB = load_mask_raw<T>(rmk, vmk, q + 3); }
-                if (active) tiled_accumulate<T, CPL>(ptA, acc);
-                if constexpr (PERSIST)
-                    if (has_next) stage_rows<NT>(G, tg, a.input, nxt, nbuf, (q * tg.RH) / P, ((q + 1) * tg.RH) / P, t);
-                if (q + 2 < P) {
-                    if (active) ptA = fetch(q + 2, dA, mA);
-                    if (q + 4 < P) { dA = load_offset_raw<T>(roff, voff, q + 4); mA = load_mask_raw<T>(rmk, vmk, q + 4); }
-                }
-                if (active) tiled_accumulate<T, CPL>(ptB, acc);
-                if constexpr (PERSIST)
-                    if (has_next)
-                        stage_rows<NT>(G, tg, a.input, nxt, nbuf, ((q + 1) * tg.RH) / P, ((q + 2) * tg.RH) / P, t);
+                const TiledPoint pt = tiled_fetch<T>(G, L, lds, rin, tg.tap_x[q], tg.tap_y[q], record_pair<T, PK>(rec, q), m);
+                tiled_accumulate<T, CPL>(pt, acc);
             }
-            if (q < P) {   // odd number of points: the last one is in ptA
-                if (active) tiled_accumulate<T, CPL>(ptA, acc);
-                if constexpr (PERSIST)
-                    if (has_next) stage_rows<NT>(G, tg, a.input, nxt, nbuf, (q * tg.RH) / P, tg.RH, t);
-            }
+            __builtin_amdgcn_sched_barrier(0);
         }
+    } else {
+        __builtin_amdgcn_s_waitcnt(0);   // the region has landed
+        __syncthreads();
+        float mx = 0.f, inv = 1.f;
+        if constexpr (SOFTMAX) {
+            mx = load_mask_value<T>(rmk, vmk, 0);
+            for (int q = 1; q < P; ++q) mx = fmaxf(mx, load_mask_value<T>(rmk, vmk, q));
+            float sum = 0.f;
+            for (int q = 0; q < P; ++q) sum += __expf(load_mask_value<T>(rmk, vmk, q) - mx);
+            inv = 1.0f / sum;
+        }
+        auto fetch = [&](int q, const RawPair<T>& d, uint32_t mraw) {
+            float m = mval(mraw);
+            if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
+            return tiled_fetch<T>(G, L, lds, rin, tg.tap_x[q], tg.tap_y[q], widen_pair<T>(d), m);
+        };
 
-        if (active) {
-            // store the lane's 32 bytes, undoing the half swap
-            char* out = (char*)a.output + ((size_t)cur.n * G.Ho * G.Wo + (size_t)ho * G.Wo + wo) * G.C * EB +
-                        cur.slab * 128u + (uint32_t)sub * 32u;
-            store<T, 16>(out + swp * 16, &acc[0]);
-            store<T, 16>(out + (swp ^ 1) * 16, &acc[EPR]);
+        // Software pipeline over the points, two per (rolled) iteration: the
+        // corner reads of point q+1 are in flight while point q accumulates,
+        // and each point's offsets and mask are requested two points ahead.
+        // Rolled, the compiler cannot hoist further points' reads and run
+        // out of registers.
+        RawPair<T> dA, dB;
+        uint32_t mA = 0u, mB = 0u;
+        dA = load_offset_raw<T>(roff, voff, 0);
+        mA = load_mask_raw<T>(rmk, vmk, 0);
+        if (P > 1) { dB = load_offset_raw<T>(roff, voff, 1); mB = load_mask_raw<T>(rmk, vmk, 1); }
+        TiledPoint ptA, ptB;
+        if (active) ptA = fetch(0, dA, mA);
+        if (P > 2) { dA = load_offset_raw<T>(roff, voff, 2); mA = load_mask_raw<T>(rmk, vmk, 2); }
+        int q = 0;
+        DCN_UNROLL(1)
+        for (; q + 1 < P; q += 2) {
+            // here: ptA = point q (reads issued), dB = point q+1, dA = point q+2
+            if (active) ptB = fetch(q + 1, dB, mB);
+            if (q + 3 < P) { dB = load_offset_raw<T>(roff, voff, q + 3); mB = load_mask_raw<T>(rmk, vmk, q + 3); }
+            if (active) tiled_accumulate<T, CPL>(ptA, acc);
+            if (q + 2 < P) {
+                if (active) ptA = fetch(q + 2, dA, mA);
+                if (q + 4 < P) { dA = load_offset_raw<T>(roff, voff, q + 4); mA = load_mask_raw<T>(rmk, vmk, q + 4); }
+            }
+            if (active) tiled_accumulate<T, CPL>(ptB, acc);
         }
-        __builtin_amdgcn_s_waitcnt(0);   // the next region has landed
-        __syncthreads();                 // and nobody still reads this one
-        cur = nxt;
+        if (q < P) {   // odd number of points: the last one is in ptA
+            if (active) tiled_accumulate<T, CPL>(ptA, acc);
+        }
+    }
+
+    if (active) {
+        // store the lane's 32 bytes, undoing the half swap
+        char* out = (char*)a.output + ((size_t)cur.n * G.Ho * G.Wo + (size_t)ho * G.Wo + wo) * G.C * EB +
+                    cur.slab * 128u + (uint32_t)sub * 32u;
+        store<T, 16>(out + swp * 16, &acc[0]);
+        store<T, 16>(out + (swp ^ 1) * 16, &acc[EPR]);
     }
 }
 
@@ -995,6 +968,16 @@ __device__ __forceinline__ GradPoint tiled_fetch_grad(const Geometry& G, const T
     return pt;
 }
 
+// Sums over lanes l ^ 1 and l ^ 2 within a quad of lanes (DPP quad permutes).
+__device__ __forceinline__ float quad_xor1(float v)
+{
+    return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float v)
+{
+    return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
 template <int KT, int NT, bool SOFTMAX>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DCN_TILE_WAVES_PER_EU)))
 void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
@@ -1053,7 +1036,9 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
         for (int c = 0; c < 8; ++c) go[c] = 0.f;
     }
 
-    __builtin_amdgcn_s_waitcnt(0);
+    PointRecord<float, (KT > 0 ? KT * KT : 1)> rec;
+    if constexpr (KT > 0) load_record<float, KT * KT>(rec, roff, voff, rmk, vmk);
+    __builtin_amdgcn_s_waitcnt(0);     // region, upstream gradient and record have landed
     __syncthreads();
     const char* lds = (const char*)region;
 
@@ -1074,14 +1059,14 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
         float gdx = hy * (sk[1] - sk[0]) + pt.ly * (sk[3] - sk[2]);
         float gdy = hx * (sk[2] - sk[0]) + pt.lx * (sk[3] - sk[1]);
         if (tg.gshift >= 1) {
-            gm += __shfl_xor(gm, 1);
-            gdx += __shfl_xor(gdx, 1);
-            gdy += __shfl_xor(gdy, 1);
+            gm = quad_xor1(gm);
+            gdx = quad_xor1(gdx);
+            gdy = quad_xor1(gdy);
         }
         if (tg.gshift >= 2) {
-            gm += __shfl_xor(gm, 2);
-            gdx += __shfl_xor(gdx, 2);
-            gdy += __shfl_xor(gdy, 2);
+            gm = quad_xor2(gm);
+            gdx = quad_xor2(gdx);
+            gdy = quad_xor2(gdy);
         }
         if (!pt.inmap) { gm = 0.f; gdx = 0.f; gdy = 0.f; }
         if (active && leader) *(float2*)(goff + 2 * q) = make_float2(G.alpha * m * gdx, G.alpha * m * gdy);
@@ -1109,8 +1094,6 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
 
     if constexpr (KT > 0) {
         constexpr int PK = KT * KT;
-        PointRecord<float, PK> rec;
-        load_record<float, PK>(rec, roff, voff, rmk, vmk);
         float mx = 0.f, inv = 1.f;
         if constexpr (SOFTMAX) {
             mx = __uint_as_float(rec.mask[0]);

@@ -113,7 +113,30 @@ def test_tiled_offset_spread(sigma):
     check_forward(w)
 
 
-@pytest.mark.parametrize("case", SWEEP, ids=lambda c: c[0])
+@pytest.mark.parametrize("sigma", [0.25, 6.0, 40.0])
+def test_tall_offset_spread(sigma):
+    """The same on a taller map with several tiles in each direction."""
+    w = inputs.Workload(name="spread_tall", N=1, H=40, W=32, G=4, Cg=16, Ho=40, Wo=32, dtype="f16",
+                        offset_sigma=sigma, mask_sigma=0.5, seed_base=93500 + int(sigma * 10))
+    check_forward(w)
+
+
+# taller maps (32 rows or more, several tiles in each direction): ragged
+# tiles, runtime K, every group width, dilation, negative offset_scale
+TALL_SWEEP = [  # name, N, H, W, G, Cg, K, stride, pad, dil, alpha, softmax, dtype
+    ("tall_f16_ragged", 2, 37, 57, 4, 16, 3, 1, 1, 1, 1.0, False, "f16"),
+    ("tall_bf16_k5", 1, 40, 33, 8, 16, 5, 1, 2, 1, 0.8, True, "bf16"),
+    ("tall_f32_cg16", 1, 48, 30, 4, 16, 3, 1, 1, 1, 1.0, True, "f32"),
+    ("tall_f32_cg8", 1, 33, 26, 8, 8, 3, 1, 1, 1, 1.0, False, "f32"),
+    ("tall_bf16_cg64", 1, 35, 28, 2, 64, 3, 1, 1, 1, 1.0, False, "bf16"),
+    ("tall_f16_k1", 1, 32, 40, 4, 16, 1, 1, 0, 1, 1.0, False, "f16"),
+    ("tall_bf16_d2", 1, 44, 36, 4, 16, 3, 1, 2, 2, 1.0, True, "bf16"),
+    ("tall_neg_alpha", 1, 34, 31, 4, 16, 3, 1, 1, 1, -1.1, False, "f16"),
+    ("tall_f16_k7", 1, 40, 30, 4, 16, 7, 1, 3, 1, 1.0, False, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP + TALL_SWEEP, ids=lambda c: c[0])
 def test_geometry_sweep(case):
     name, N, H, W, G, Cg, K, s, p, d, a, sm, dt = case
     Ho, Wo = oracle.out_size(H, K, s, p, d), oracle.out_size(W, K, s, p, d)
@@ -221,6 +244,22 @@ def test_nan_input_does_not_leak_tiled(dtype):
                       kernel_size=1, pad=0, group=G).cpu()
     nan_pix = torch.isnan(out.float()).any(-1)
     assert nan_pix[0, 0, 11] and nan_pix.sum() == 1
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nan_input_does_not_leak_tall(dtype):
+    """Same check on a taller map with several tiles."""
+    N, H, W, G, Cg = 1, 32, 32, 4, 16
+    T = inputs.DTYPES[dtype]
+    x = torch.randn(N, H, W, G * Cg, generator=torch.Generator().manual_seed(3)).to(T)
+    x[0, 0, 31] = float("nan")
+    off = torch.zeros(N, H, W, G, 2)
+    off[..., 0] = -0.5
+    m = torch.ones(N, H, W, G)
+    out = dcn.forward(x.to(DEV), off.reshape(N, H, W, -1).to(T).to(DEV), m.reshape(N, H, W, -1).to(T).to(DEV),
+                      kernel_size=1, pad=0, group=G).cpu()
+    nan_pix = torch.isnan(out.float()).any(-1)
+    assert nan_pix[0, 0, 31] and nan_pix.sum() == 1
 
 
 def test_nan_input_does_not_leak_to_other_pixels():
