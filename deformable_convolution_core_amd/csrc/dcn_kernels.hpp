@@ -523,15 +523,16 @@ struct TiledLane {
 
 // Coordinates, weights and corner reads of one point: from the staged region
 // when all four corners lie inside it, else gathered from global memory with
-// the untiled kernel's off-map rules.
+// the untiled kernel's off-map rules.  xt, yt: the tap's part of the
+// coordinates, fmaf(alpha, tap, base).
 template <typename T>
 __device__ __forceinline__ TiledPoint tiled_fetch(const Geometry& G, const TiledLane& L, const char* lds,
-                                                  __amdgpu_buffer_rsrc_t rin, float tapx, float tapy,
+                                                  __amdgpu_buffer_rsrc_t rin, float xt, float yt,
                                                   float2 d, float m)
 {
     TiledPoint pt;
-    const float x = fmaf(G.alpha, d.x, fmaf(G.alpha, tapx, L.bx));
-    const float y = fmaf(G.alpha, d.y, fmaf(G.alpha, tapy, L.by));
+    const float x = fmaf(G.alpha, d.x, xt);
+    const float y = fmaf(G.alpha, d.y, yt);
     // Floor and fraction come from the absolute coordinate (x - x_lo is not
     // exact when x_lo < 0); the region test is on the integer floor.
     // cvt_flr saturates +-Inf to out-of-range values; NaN is rejected by the
@@ -628,7 +629,9 @@ __device__ __forceinline__ TileCoord tile_coord(const Geometry& G, const TileGeo
 // (asynchronous, no registers): lane t copies 16-byte chunk e of each row;
 // the 64 lanes of a wave fill 1 KB of LDS contiguously (lane l at base +
 // 16*l).  Off-image pixels get an out-of-range offset and are written as
-// zeros, which is the zero padding of the definition.
+// zeros, which is the zero padding of the definition.  Rows above and below
+// the image (a range every lane shares) use that offset outright; on image
+// rows a lane steps its offset by one image row.
 template <int NT>
 __device__ __forceinline__ void stage_rows(const Geometry& G, const TileGeo& tg, const void* input,
                                            const TileCoord& c, uint4* buf, int r0, int r1, int t)
@@ -636,18 +639,28 @@ __device__ __forceinline__ void stage_rows(const Geometry& G, const TileGeo& tg,
     const int RW8 = tg.RW * 8;
     const __amdgpu_buffer_rsrc_t rin =
         image_rsrc((const char*)input + (size_t)c.n * G.in_image_bytes, G.in_image_bytes);
+    // image rows are region rows [ra, rb)
+    const int ra = -c.y_lo < r0 ? r0 : (-c.y_lo > r1 ? r1 : -c.y_lo);
+    const int rb = G.H - c.y_lo < ra ? ra : (G.H - c.y_lo > r1 ? r1 : G.H - c.y_lo);
     for (int e = t; e < RW8; e += NT) {
         const int gx = c.x_lo + (e >> 3);
         const bool col_ok = (uint32_t)gx < (uint32_t)G.W;
-        const uint32_t col_off = (uint32_t)gx * G.in_row_bytes + c.slab * 128u + (uint32_t)(e & 7) * 16u;
         uint4* wave_dst = buf + (e & ~63);
-        for (int ry = r0; ry < r1; ++ry) {
-            const int gy = c.y_lo + ry;
-            const bool ok = col_ok && (uint32_t)gy < (uint32_t)G.H;
-            const uint32_t off = ok ? (uint32_t)gy * G.in_line_bytes + col_off : kOOB;
+        for (int ry = r0; ry < ra; ++ry)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rin, (__attribute__((address_space(3))) void*)(wave_dst + ry * RW8), 16, kOOB, 0, 0, 0);
+        uint32_t off = col_ok ? (uint32_t)(c.y_lo + ra) * G.in_line_bytes + (uint32_t)gx * G.in_row_bytes +
+                                    c.slab * 128u + (uint32_t)(e & 7) * 16u
+                              : kOOB;
+        const uint32_t step = col_ok ? G.in_line_bytes : 0u;
+        for (int ry = ra; ry < rb; ++ry) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rin, (__attribute__((address_space(3))) void*)(wave_dst + ry * RW8), 16, off, 0, 0, 0);
+            off += step;
         }
+        for (int ry = rb; ry < r1; ++ry)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rin, (__attribute__((address_space(3))) void*)(wave_dst + ry * RW8), 16, kOOB, 0, 0, 0);
     }
 }
 
@@ -726,12 +739,20 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
             for (int q = 0; q < PK; ++q) sum += __expf(mval(rec.mask[q]) - mx);
             inv = 1.0f / sum;
         }
+        // the taps' part of the coordinates, once per column and row of taps
+        float xt[KT], yt[KT];
+#pragma unroll
+        for (int i = 0; i < KT; ++i) {
+            xt[i] = fmaf(G.alpha, tg.tap_x[i * KT], L.bx);
+            yt[i] = fmaf(G.alpha, tg.tap_y[i], L.by);
+        }
 #pragma unroll
         for (int q = 0; q < PK; ++q) {
             if (active) {
                 float m = mval(rec.mask[q]);
                 if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
-                const TiledPoint pt = tiled_fetch<T>(G, L, lds, rin, tg.tap_x[q], tg.tap_y[q], record_pair<T, PK>(rec, q), m);
+                const TiledPoint pt =
+                    tiled_fetch<T>(G, L, lds, rin, xt[q / KT], yt[q % KT], record_pair<T, PK>(rec, q), m);
                 tiled_accumulate<T, CPL>(pt, acc);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -750,7 +771,8 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
         auto fetch = [&](int q, const RawPair<T>& d, uint32_t mraw) {
             float m = mval(mraw);
             if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
-            return tiled_fetch<T>(G, L, lds, rin, tg.tap_x[q], tg.tap_y[q], widen_pair<T>(d), m);
+            return tiled_fetch<T>(G, L, lds, rin, fmaf(G.alpha, tg.tap_x[q], L.bx), fmaf(G.alpha, tg.tap_y[q], L.by),
+                                  widen_pair<T>(d), m);
         };
 
         // Software pipeline over the points, two per (rolled) iteration: the
