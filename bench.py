@@ -283,6 +283,17 @@ def main():
                                  GBps=round(w5.min_bytes_backward() / (bms * 1e-3) / 1e9, 1),
                                  frac_hbm=round(w5.min_bytes_backward() / (bms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4))
         log(f"backward c5: {extra['backward']['us']} us")
+        # the same shape in half precision (binary32 arithmetic, half storage)
+        halves = []
+        for dt in ("f16", "bf16"):
+            wh = inputs.scaled(w5, dtype=dt)
+            hms, heager, _ = time_launches(wh, max(20, args.steps // 4), min(args.warmup, 10), backward=True)
+            halves.append(dict(workload=f"{w5.name} ({dt})", dtype=dt, us=round(hms * 1e3, 3),
+                               eager_us=round(heager * 1e3, 3), min_bytes=wh.min_bytes_backward(),
+                               GBps=round(wh.min_bytes_backward() / (hms * 1e-3) / 1e9, 1),
+                               frac_hbm=round(wh.min_bytes_backward() / (hms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)))
+            log(f"backward c5 {dt}: {halves[-1]['us']} us")
+        extra["backward_half"] = halves
 
     cpu = None
     if not args.quick and not args.no_cpu_baseline:

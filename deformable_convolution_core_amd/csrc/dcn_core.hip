@@ -134,7 +134,8 @@ struct TilePlan {
 // multiple of 128, 16-byte aligned input and output.  Among tile shapes with
 // at most 128 pixels it picks the cheapest by a simple cost model: lane slots
 // issued (idle lanes of ragged tiles count) plus region chunks staged.
-bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan)
+bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan, int min_waves = 12,
+                int64_t max_lds = kMaxTileLds)
 {
     const int eb = c.ebytes, rowg = c.Cg * eb, rowc = c.G * c.Cg * eb;
     if (!(rowg == 32 || rowg == 64 || rowg == 128) || rowc % 128 != 0) return false;
@@ -157,7 +158,7 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan)
             if (DCN_TILE_FORCE_TW && (tw != DCN_TILE_FORCE_TW || th != DCN_TILE_FORCE_TH)) continue;
             const int rh = (th - 1) * c.stride + 2 * ml + 2, rw = (tw - 1) * c.stride + 2 * ml + 2;
             const int64_t lds = (int64_t)rh * rw * 128;
-            if (lds > kMaxTileLds) continue;
+            if (lds > max_lds) continue;
             const uint64_t tx = (uint64_t)((c.Wo + tw - 1) / tw), ty = (uint64_t)((c.Ho + th - 1) / th);
             const uint64_t tiles = tx * ty * slabs * (uint64_t)c.N;
             const int lanes = ((th * tw * 4 + 63) / 64) * 64;
@@ -165,7 +166,7 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan)
             // waves per CU the latency of the corner reads shows
             const int per_cu = (int)(160 * 1024 / lds) < 2048 / nt ? (int)(160 * 1024 / lds) : 2048 / nt;
             const int waves = per_cu * nt / 64;
-            if (waves < 12) continue;   // too few resident waves: the untiled kernel does better
+            if (waves < min_waves) continue;   // too few resident waves: the untiled kernel does better
             const double occ_penalty = waves >= 16 ? 1.0 : 16.0 / (double)waves;
             const double cost = (double)tiles * ((double)lanes * 900.0 * occ_penalty + (double)rh * rw * 8 * 3.0);
             if (best < 0 || cost < best) {
@@ -253,15 +254,13 @@ struct OwnerPlan {
     uint64_t blocks;
 };
 
-// The owner kernel applies to binary32 gradients whose 32-byte lane chunks
-// stay inside one group (Cg a multiple of 8) and whose 128-byte slabs tile
-// the channel row (C a multiple of 32), with 16-byte aligned grad_output and
-// grad_input.  Among tiles that fit the LDS it picks the one with the
+// The owner kernel applies where a lane's 8 channels stay inside one group
+// (Cg a multiple of 8) and slabs of 32 channels tile the channel row (C a
+// multiple of 32), with 16-byte aligned grad_output and grad_input.  Among tiles that fit the LDS it picks the one with the
 // shortest makespan: blocks per CU (256 CUs) times a block's lane slots
 // issued over its visited output pixels (idle lanes of the last pass count)
-// plus its own zero fill and store.  It declines shapes
-// where the visited area is many times the output (a very large
-// offset_scale makes every output pixel near every tile).
+// plus its own zero fill and store, among tiles whose visited area stays
+// within 8x the output.
 bool plan_owner(const Call& c, const void* gout, const void* gin, OwnerPlan& pl)
 {
     const int C = c.G * c.Cg;
@@ -287,6 +286,10 @@ bool plan_owner(const Call& c, const void* gout, const void* gin, OwnerPlan& pl)
                 int64_t ew = (tw - 1 + 2 * M) / c.stride + 1, eh = (th - 1 + 2 * M) / c.stride + 1;
                 if (ew > c.Wo) ew = c.Wo;
                 if (eh > c.Ho) eh = c.Ho;
+                // visited output pixels over output pixels: beyond 8x the
+                // atomic scatter is cheaper (a very large offset_scale makes
+                // every output pixel near every tile)
+                if ((double)(tx * ty) * (double)(ew * eh) > 8.0 * (double)c.Ho * c.Wo) continue;
                 const int64_t passes = (ew * eh * 4 + nt - 1) / nt;
                 const double occ = waves >= 16 ? 1.0 : 16.0 / (double)waves;
                 // makespan: the busiest CU runs ceil(blocks / CUs) blocks
@@ -303,27 +306,24 @@ bool plan_owner(const Call& c, const void* gout, const void* gin, OwnerPlan& pl)
             }
     }
     if (best < 0 || pl.blocks >= (1ull << 31)) return false;
-    const int64_t off_img = (int64_t)c.Ho * c.Wo * c.G * c.K * c.K * 2 * 4;
+    const int64_t off_img = (int64_t)c.Ho * c.Wo * c.G * c.K * c.K * 2 * c.ebytes;
     if (off_img >= (1ll << 31)) return false;
     pl.og.off_image_bytes = (uint32_t)off_img;
     pl.og.mask_image_bytes = (uint32_t)(off_img / 2);
-    // visited output pixels per output pixel: beyond 8x the atomic scatter is cheaper
-    const double visits = (double)pl.og.tiles_x * pl.og.tiles_y *
-                          (double)((pl.og.TW - 1 + 2 * M) / c.stride + 1) * ((pl.og.TH - 1 + 2 * M) / c.stride + 1);
-    return visits <= 8.0 * (double)c.Ho * c.Wo;
+    return true;
 }
 
-template <int KT>
+template <typename T, int KT>
 int launch_owner(const BwdArgs& a, const OwnerPlan& pl, hipStream_t st)
 {
     if (pl.threads == 1024)
-        hipLaunchKernelGGL((dcn_backward_input_owner<KT, 1024>), dim3((uint32_t)pl.blocks), dim3(1024), pl.lds_bytes,
-                           st, a, pl.og);
+        hipLaunchKernelGGL((dcn_backward_input_owner<T, KT, 1024>), dim3((uint32_t)pl.blocks), dim3(1024),
+                           pl.lds_bytes, st, a, pl.og);
     else if (pl.threads == 512)
-        hipLaunchKernelGGL((dcn_backward_input_owner<KT, 512>), dim3((uint32_t)pl.blocks), dim3(512), pl.lds_bytes,
+        hipLaunchKernelGGL((dcn_backward_input_owner<T, KT, 512>), dim3((uint32_t)pl.blocks), dim3(512), pl.lds_bytes,
                            st, a, pl.og);
     else
-        hipLaunchKernelGGL((dcn_backward_input_owner<KT, 256>), dim3((uint32_t)pl.blocks), dim3(256), pl.lds_bytes,
+        hipLaunchKernelGGL((dcn_backward_input_owner<T, KT, 256>), dim3((uint32_t)pl.blocks), dim3(256), pl.lds_bytes,
                            st, a, pl.og);
     return launch_status();
 }
@@ -332,25 +332,45 @@ int launch_owner(const BwdArgs& a, const OwnerPlan& pl, hipStream_t st)
 #define DCN_USE_GRAD_TILES 1  // grad_offset / grad_mask from staged input tiles where the shape allows
 #endif
 
-template <int KT, int NT>
+template <typename T, int KT, int NT>
 int launch_grad_tiled(const BwdArgs& a, const Call& c, const TilePlan& pl, hipStream_t st)
 {
     if (c.softmax)
-        hipLaunchKernelGGL((dcn_backward_grad_tiled<KT, NT, true>), dim3((uint32_t)pl.blocks), dim3(NT), pl.lds_bytes,
-                           st, a, pl.tg);
+        hipLaunchKernelGGL((dcn_backward_grad_tiled<T, KT, NT, true>), dim3((uint32_t)pl.blocks), dim3(NT),
+                           pl.lds_bytes, st, a, pl.tg);
     else
-        hipLaunchKernelGGL((dcn_backward_grad_tiled<KT, NT, false>), dim3((uint32_t)pl.blocks), dim3(NT), pl.lds_bytes,
-                           st, a, pl.tg);
+        hipLaunchKernelGGL((dcn_backward_grad_tiled<T, KT, NT, false>), dim3((uint32_t)pl.blocks), dim3(NT),
+                           pl.lds_bytes, st, a, pl.tg);
     return launch_status();
 }
 
+template <typename T>
 int backward_grad_tiled(const BwdArgs& base, const Call& c, const TilePlan& pl, hipStream_t st)
 {
     BwdArgs a = base;
-    a.geo = make_geometry(c, 8);
+    a.geo = make_geometry(c, 32 / (int)sizeof(T));
     if (pl.threads == 512)
-        return c.K == 3 ? launch_grad_tiled<3, 512>(a, c, pl, st) : launch_grad_tiled<0, 512>(a, c, pl, st);
-    return c.K == 3 ? launch_grad_tiled<3, 256>(a, c, pl, st) : launch_grad_tiled<0, 256>(a, c, pl, st);
+        return c.K == 3 ? launch_grad_tiled<T, 3, 512>(a, c, pl, st) : launch_grad_tiled<T, 0, 512>(a, c, pl, st);
+    return c.K == 3 ? launch_grad_tiled<T, 3, 256>(a, c, pl, st) : launch_grad_tiled<T, 0, 256>(a, c, pl, st);
+}
+
+// Half precision: the owner kernel writes grad_input (binary32 sums rounded
+// once) and the tiled gradient kernel does the rest; shapes outside what the
+// two kernels cover are not supported.
+template <typename T>
+int backward_half(BwdArgs a, const Call& c, hipStream_t st)
+{
+    OwnerPlan op;
+    TilePlan tp;
+    // there is no untiled half-precision gradient kernel to fall back on, so
+    // any tile that fits the LDS will do
+    if (!plan_owner(c, a.grad_out, a.grad_input, op) || !plan_tiles(c, a.input, a.grad_out, tp, 1, 160 * 1024))
+        return DCN_ERR_UNSUPPORTED;
+    a.geo = make_geometry(c, 8);
+    int rc = c.K == 3 ? launch_owner<T, 3>(a, op, st) : launch_owner<T, 0>(a, op, st);
+    if (rc != DCN_OK) return rc;
+    a.near_m = op.og.M;
+    return backward_grad_tiled<T>(a, c, tp, st);
 }
 
 template <int LB, int L>
@@ -443,13 +463,21 @@ extern "C" int dcn_core_backward(const void* input, const void* offset, const vo
     Call c;
     int rc = validate(c, N, H, W, G, Cg, K, stride, pad, dilation, offset_scale, softmax_flag, dtype);
     if (rc != DCN_OK) return rc;
-    if (dtype != DCN_F32) return DCN_ERR_UNSUPPORTED;
     if (N == 0) return DCN_OK;
     if (!input || !offset || !mask || !grad_output || !grad_input || !grad_offset || !grad_mask)
         return DCN_ERR_INVALID_ARG;
-    if (!aligned(input, 4) || !aligned(grad_output, 4) || !aligned(grad_input, 4) ||
-        !aligned(offset, 8) || !aligned(grad_offset, 8) || !aligned(mask, 4) || !aligned(grad_mask, 4))
+    const uintptr_t eb = (uintptr_t)c.ebytes;
+    if (!aligned(input, eb) || !aligned(grad_output, eb) || !aligned(grad_input, eb) || !aligned(offset, 2 * eb) ||
+        !aligned(grad_offset, 2 * eb) || !aligned(mask, eb) || !aligned(grad_mask, eb))
         return DCN_ERR_INVALID_ARG;
+    if (dtype != DCN_F32) {
+        BwdArgs a{};
+        a.input = input; a.offset = offset; a.mask = mask; a.grad_out = grad_output;
+        a.grad_input = grad_input; a.grad_offset = grad_offset; a.grad_mask = grad_mask;
+        a.near_m = -1;
+        return dtype == DCN_F16 ? backward_half<_Float16>(a, c, (hipStream_t)stream)
+                                : backward_half<__bf16>(a, c, (hipStream_t)stream);
+    }
     int LB, L;
     if (Cg % 4 == 0 && pow2(Cg / 4) && Cg / 4 <= 64 && aligned(input, 16) && aligned(grad_input, 16)) {
         LB = 16; L = Cg / 4;
@@ -461,21 +489,21 @@ extern "C" int dcn_core_backward(const void* input, const void* offset, const vo
     hipStream_t st = (hipStream_t)stream;
     BwdArgs a{};
     a.input = input; a.offset = offset; a.mask = mask; a.grad_out = grad_output;
-    a.grad_input = (float*)grad_input; a.grad_offset = (float*)grad_offset; a.grad_mask = (float*)grad_mask;
+    a.grad_input = grad_input; a.grad_offset = grad_offset; a.grad_mask = grad_mask;
     a.near_m = -1;
     OwnerPlan op;
     if (DCN_USE_OWNER && plan_owner(c, grad_output, grad_input, op)) {
         // owners write every element of grad_input; the gradient kernel
         // then adds the corners that are not near with atomics
         a.geo = make_geometry(c, 8);
-        rc = c.K == 3 ? launch_owner<3>(a, op, st) : launch_owner<0>(a, op, st);
+        rc = c.K == 3 ? launch_owner<float, 3>(a, op, st) : launch_owner<float, 0>(a, op, st);
         a.near_m = op.og.M;
     } else {
         rc = zero_fill((float*)grad_input, (int64_t)N * H * W * G * Cg, st);
     }
     if (rc != DCN_OK) return rc;
     TilePlan tp;
-    if (DCN_USE_GRAD_TILES && plan_tiles(c, input, grad_output, tp)) return backward_grad_tiled(a, c, tp, st);
+    if (DCN_USE_GRAD_TILES && plan_tiles(c, input, grad_output, tp)) return backward_grad_tiled<float>(a, c, tp, st);
     return LB == 16 ? backward_lanes<16>(a, c, st, L) : backward_lanes<4>(a, c, st, L);
 }
 

@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace dcn {
 
 constexpr int kBlock = 256;
@@ -188,9 +190,9 @@ struct BwdArgs {
     const void* offset;
     const void* mask;
     const void* grad_out;
-    float* grad_input;
-    float* grad_offset;
-    float* grad_mask;
+    void* grad_input;             // all three in the call's dtype
+    void* grad_offset;
+    void* grad_mask;
     int near_m;                   // >= 0: corners within this many pixels of the sampling
                                   // base were added by the owner kernel; -1: none were
     Geometry geo;
@@ -849,8 +851,8 @@ __global__ __launch_bounds__(kBlock) void dcn_backward_kernel(BwdArgs a)
     const size_t pg = pix_global * G.groups + lw.g;
     const float* off = (const float*)a.offset + pg * G.P * 2;
     const float* mk = (const float*)a.mask + pg * G.P;
-    float* goff = a.grad_offset + pg * G.P * 2;
-    float* gmk = a.grad_mask + pg * G.P;
+    float* goff = (float*)a.grad_offset + pg * G.P * 2;
+    float* gmk = (float*)a.grad_mask + pg * G.P;
     char* gin = (char*)a.grad_input + (size_t)lw.n * G.in_image_bytes;
     const int bxi = (int)lw.wo * G.stride - G.pad + G.c0;
     const int byi = (int)lw.ho * G.stride - G.pad + G.c0;
@@ -1000,10 +1002,28 @@ __device__ __forceinline__ float quad_xor2(float v)
     return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
 }
 
-template <int KT, int NT, bool SOFTMAX>
+// Packed atomic add of two adjacent half-precision elements (each add rounds
+// once to the dtype).
+template <typename T>
+__device__ __forceinline__ void atomic_add_pair(void* p, float x, float y)
+{
+    if constexpr (std::is_same<T, _Float16>::value) {
+        typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+        const v2 v = {(_Float16)x, (_Float16)y};
+        __builtin_amdgcn_global_atomic_fadd_v2f16((__attribute__((address_space(1))) v2*)p, v);
+    } else {
+        typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+        const v2 v = {(__bf16)x, (__bf16)y};
+        __builtin_amdgcn_global_atomic_fadd_v2bf16((__attribute__((address_space(1))) v2*)p, v);
+    }
+}
+
+template <typename T, int KT, int NT, bool SOFTMAX>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DCN_TILE_WAVES_PER_EU)))
 void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
 {
+    constexpr int EB = Elem<T>::bytes;
+    constexpr int CPL = 32 / EB;        // channels per lane
     extern __shared__ uint4 region[];
     const Geometry& G = a.geo;
     const int t = threadIdx.x;
@@ -1031,8 +1051,8 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
         image_rsrc((const char*)a.offset + (size_t)cur.n * tg.off_image_bytes, tg.off_image_bytes);
     const __amdgpu_buffer_rsrc_t rmk =
         image_rsrc((const char*)a.mask + (size_t)cur.n * tg.mask_image_bytes, tg.mask_image_bytes);
-    const uint32_t voff = pg_img * (uint32_t)(P * 8);
-    const uint32_t vmk = pg_img * (uint32_t)(P * 4);
+    const uint32_t voff = pg_img * (uint32_t)(P * 2 * EB);
+    const uint32_t vmk = pg_img * (uint32_t)(P * EB);
     const int bxi = wo * G.stride - G.pad + G.c0, byi = ho * G.stride - G.pad + G.c0;
     L.bx = (float)bxi;
     L.by = (float)byi;
@@ -1043,23 +1063,34 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
     const uint32_t M2 = 2u * (uint32_t)a.near_m;
 
     // upstream gradient of this lane's channels, in the order its corner reads arrive
-    float go[8];
+    float go[CPL];
     const size_t pix = ((size_t)cur.n * G.Ho + (size_t)ho) * G.Wo + wo;
     char* gin = (char*)a.grad_input + (size_t)cur.n * G.in_image_bytes;
-    float* goff = a.grad_offset + ((size_t)cur.n * G.Ho * G.Wo * G.groups + pg_img) * P * 2;
-    float* gmk = a.grad_mask + ((size_t)cur.n * G.Ho * G.Wo * G.groups + pg_img) * P;
+    T* goff = (T*)a.grad_offset + ((size_t)cur.n * G.Ho * G.Wo * G.groups + pg_img) * P * 2;
+    T* gmk = (T*)a.grad_mask + ((size_t)cur.n * G.Ho * G.Wo * G.groups + pg_img) * P;
     if (active) {
-        const char* gp = (const char*)a.grad_out + pix * G.C * 4 + cur.slab * 128u + (uint32_t)sub * 32u;
-        const float4 h0 = *(const float4*)(gp + swp * 16), h1 = *(const float4*)(gp + (swp ^ 1) * 16);
-        go[0] = h0.x; go[1] = h0.y; go[2] = h0.z; go[3] = h0.w;
-        go[4] = h1.x; go[5] = h1.y; go[6] = h1.z; go[7] = h1.w;
+        const char* gp = (const char*)a.grad_out + pix * G.C * EB + cur.slab * 128u + (uint32_t)sub * 32u;
+        const uint4 h0 = *(const uint4*)(gp + swp * 16), h1 = *(const uint4*)(gp + (swp ^ 1) * 16);
+        const uint32_t w[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            if constexpr (EB == 4) {
+                go[c] = __uint_as_float(w[c]);
+            } else {
+                go[2 * c] = Elem<T>::widen(w[c] & 0xffffu);
+                go[2 * c + 1] = Elem<T>::widen(w[c] >> 16);
+            }
+        }
     } else {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) go[c] = 0.f;
+        for (int c = 0; c < CPL; ++c) go[c] = 0.f;
     }
+    auto mval = [&](uint32_t raw) {
+        return EB == 4 ? __uint_as_float(raw) : Elem<T>::widen(raw);
+    };
 
-    PointRecord<float, (KT > 0 ? KT * KT : 1)> rec;
-    if constexpr (KT > 0) load_record<float, KT * KT>(rec, roff, voff, rmk, vmk);
+    PointRecord<T, (KT > 0 ? KT * KT : 1)> rec;
+    if constexpr (KT > 0) load_record<T, KT * KT>(rec, roff, voff, rmk, vmk);
     __builtin_amdgcn_s_waitcnt(0);     // region, upstream gradient and record have landed
     __syncthreads();
     const char* lds = (const char*)region;
@@ -1072,7 +1103,14 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
         for (int k = 0; k < 4; ++k) {
             float acc = 0.f;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) acc = fmaf(go[c], __uint_as_float(pt.raw[k][c]), acc);
+            for (int c = 0; c < 8; ++c) {
+                if constexpr (EB == 4) {
+                    acc = fmaf(go[c], __uint_as_float(pt.raw[k][c]), acc);
+                } else {
+                    acc = fmaf(go[2 * c], Elem<T>::widen(pt.raw[k][c] & 0xffffu), acc);
+                    acc = fmaf(go[2 * c + 1], Elem<T>::widen(pt.raw[k][c] >> 16), acc);
+                }
+            }
             sk[k] = acc;
         }
         const float hy = 1.0f - pt.ly, hx = 1.0f - pt.lx;
@@ -1091,7 +1129,10 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
             gdy = quad_xor2(gdy);
         }
         if (!pt.inmap) { gm = 0.f; gdx = 0.f; gdy = 0.f; }
-        if (active && leader) *(float2*)(goff + 2 * q) = make_float2(G.alpha * m * gdx, G.alpha * m * gdy);
+        if (active && leader) {
+            const float gd[2] = {G.alpha * m * gdx, G.alpha * m * gdy};
+            store<T, 2 * EB>(goff + 2 * q, gd);
+        }
         // corners beyond the owners' reach
         if (active && pt.inmap) {
 #pragma unroll
@@ -1102,12 +1143,20 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
                                   (uint32_t)(qy - byi + a.near_m) <= M2;
                 if (valid && !near) {
                     const float mw = m * wb[k];
-                    float* dst = (float*)(gin + (size_t)qy * G.in_line_bytes + (size_t)qx * G.in_row_bytes + L.gl_first);
-                    float* dst2 = (float*)(gin + (size_t)qy * G.in_line_bytes + (size_t)qx * G.in_row_bytes + L.gl_second);
+                    char* px0 = gin + (size_t)qy * G.in_line_bytes + (size_t)qx * G.in_row_bytes;
+                    if constexpr (EB == 4) {
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) atomicAdd(dst + c, mw * go[c]);
+                        for (int c = 0; c < 4; ++c) atomicAdd((float*)(px0 + L.gl_first) + c, mw * go[c]);
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) atomicAdd(dst2 + c, mw * go[4 + c]);
+                        for (int c = 0; c < 4; ++c) atomicAdd((float*)(px0 + L.gl_second) + c, mw * go[4 + c]);
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            atomic_add_pair<T>(px0 + L.gl_first + 4 * c, mw * go[2 * c], mw * go[2 * c + 1]);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            atomic_add_pair<T>(px0 + L.gl_second + 4 * c, mw * go[8 + 2 * c], mw * go[9 + 2 * c]);
+                    }
                 }
             }
         }
@@ -1118,21 +1167,21 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
         constexpr int PK = KT * KT;
         float mx = 0.f, inv = 1.f;
         if constexpr (SOFTMAX) {
-            mx = __uint_as_float(rec.mask[0]);
+            mx = mval(rec.mask[0]);
 #pragma unroll
-            for (int q = 1; q < PK; ++q) mx = fmaxf(mx, __uint_as_float(rec.mask[q]));
+            for (int q = 1; q < PK; ++q) mx = fmaxf(mx, mval(rec.mask[q]));
             float sum = 0.f;
 #pragma unroll
-            for (int q = 0; q < PK; ++q) sum += __expf(__uint_as_float(rec.mask[q]) - mx);
+            for (int q = 0; q < PK; ++q) sum += __expf(mval(rec.mask[q]) - mx);
             inv = 1.0f / sum;
         }
         float gms[PK];
         float dot = 0.f;
 #pragma unroll
         for (int q = 0; q < PK; ++q) {
-            float m = __uint_as_float(rec.mask[q]);
+            float m = mval(rec.mask[q]);
             if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
-            gms[q] = point(q, record_pair<float, PK>(rec, q), m);
+            gms[q] = point(q, record_pair<T, PK>(rec, q), m);
             dot = fmaf(m, gms[q], dot);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1140,33 +1189,35 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
 #pragma unroll
             for (int q = 0; q < PK; ++q) {
                 float v = gms[q];
-                if constexpr (SOFTMAX) v = __expf(__uint_as_float(rec.mask[q]) - mx) * inv * (v - dot);
-                gmk[q] = v;
+                if constexpr (SOFTMAX) v = __expf(mval(rec.mask[q]) - mx) * inv * (v - dot);
+                store<T, EB>(gmk + q, &v);
             }
         }
     } else {
+        // runtime K: the mask gradients wait in a binary32 array (private
+        // memory: the index is not known at compile time) for the softmax
+        // Jacobian's dot product
         float mx = 0.f, inv = 1.f;
         if constexpr (SOFTMAX) {
-            mx = load_mask_value<float>(rmk, vmk, 0);
-            for (int q = 1; q < P; ++q) mx = fmaxf(mx, load_mask_value<float>(rmk, vmk, q));
+            mx = load_mask_value<T>(rmk, vmk, 0);
+            for (int q = 1; q < P; ++q) mx = fmaxf(mx, load_mask_value<T>(rmk, vmk, q));
             float sum = 0.f;
-            for (int q = 0; q < P; ++q) sum += __expf(load_mask_value<float>(rmk, vmk, q) - mx);
+            for (int q = 0; q < P; ++q) sum += __expf(load_mask_value<T>(rmk, vmk, q) - mx);
             inv = 1.0f / sum;
         }
+        float gms[kMaxTiledTaps];
         float dot = 0.f;
         for (int q = 0; q < P; ++q) {
-            float m = load_mask_value<float>(rmk, vmk, q);
+            float m = load_mask_value<T>(rmk, vmk, q);
             if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
-            const float gm = point(q, load_offset_pair<float>(roff, voff, q), m);
-            dot = fmaf(m, gm, dot);
-            if (active && leader) gmk[q] = gm;
+            gms[q] = point(q, load_offset_pair<T>(roff, voff, q), m);
+            dot = fmaf(m, gms[q], dot);
         }
-        if constexpr (SOFTMAX) {
-            if (active && leader) {
-                for (int q = 0; q < P; ++q) {
-                    const float m = __expf(load_mask_value<float>(rmk, vmk, q) - mx) * inv;
-                    gmk[q] = m * (gmk[q] - dot);
-                }
+        if (active && leader) {
+            for (int q = 0; q < P; ++q) {
+                float v = gms[q];
+                if constexpr (SOFTMAX) v = __expf(load_mask_value<T>(rmk, vmk, q) - mx) * inv * (v - dot);
+                store<T, EB>(gmk + q, &v);
             }
         }
     }
@@ -1174,21 +1225,22 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
 
 // ---------------------------------------------------------------------------
 // grad_input by owner.  A workgroup owns a TH x TW tile of input pixels and
-// one 128-byte slab of their channels (32 binary32 channels, four lanes of
-// eight channels per pixel).  A corner q of a sample of output pixel o is
-// "near" when |q - b(o)| <= M on both axes, b(o) = o*stride - pad + c0 being
-// the sample's integer base.  The owner visits exactly the output pixels
-// whose base lies within M of its tile, recomputes their samples, adds
-// m*w*g of every near corner that falls in its tile into an LDS copy of the
-// tile, and writes the tile once.  Each near (sample, corner) pair lies in
-// one tile, so grad_input needs neither a zero fill nor global atomics; the
-// rare corners that are not near (offsets beyond the reach M was sized for)
-// are added afterwards, with atomics, by dcn_backward_kernel.
+// one slab of 32 of their channels (four lanes of eight channels per pixel).
+// A corner q of a sample of output pixel o is "near" when |q - b(o)| <= M on
+// both axes, b(o) = o*stride - pad + c0 being the sample's integer base.  The
+// owner visits exactly the output pixels whose base lies within M of its
+// tile, recomputes their samples, adds m*w*g of every near corner that falls
+// in its tile into an LDS copy of the tile (binary32), and writes the tile
+// once, rounded to the dtype.  Each near (sample, corner) pair lies in one
+// tile, so grad_input needs neither a zero fill nor global atomics; the rare
+// corners that are not near (offsets beyond the reach M was sized for) are
+// added afterwards, with atomics, by the gradient kernel.
 //
 // LDS keeps the tile pixel by pixel, 32 floats each in channel order, at a
 // stride of 34 floats: the pixels a wave's lanes add into then start on
 // different banks, and a lane's eight channels sit at fixed offsets from one
-// 8-byte aligned address.  Lane chunk `sub` adds into floats [8*sub, 8*sub + 8) of a pixel.
+// 8-byte aligned address.  Lane chunk `sub` adds into floats [8*sub, 8*sub + 8)
+// of a pixel.
 
 // Float adds into LDS through compare-and-swap.  On gfx950 an LDS float
 // atomic add (ds_add_f32) retires about one lane every few cycles per CU,
@@ -1256,10 +1308,11 @@ __device__ __forceinline__ void owner_range(const Geometry& G, int M, int q0, in
     hi = hi < limit - 1 ? hi : limit - 1;
 }
 
-template <int KT, int NT>
+template <typename T, int KT, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
 void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
 {
+    constexpr int EB = Elem<T>::bytes;
     extern __shared__ float owner_tile[];
     const Geometry& G = a.geo;
     const int t = threadIdx.x;
@@ -1332,21 +1385,27 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
     // the next pixel's fetch in registers as well spills at this register
     // budget and measured slower.)
     struct Pending {
-        float4 g0, g1;
-        PointRecord<float, (KT > 0 ? KT * KT : 1)> rec;
+        uint32_t gw[2 * EB];                  // the lane's 8 upstream-gradient elements
+        PointRecord<T, (KT > 0 ? KT * KT : 1)> rec;
     };
     auto fetch = [&](int e, Pending& pd) {
         const int eh = e / EW, ew = e - eh * EW;
         const int ho = hlo + eh, wo = wlo + ew;
         const size_t pix = ((size_t)n * G.Ho + ho) * G.Wo + wo;
-        const float4* gp = (const float4*)((const float*)a.grad_out + pix * G.C + ch0);
-        pd.g0 = gp[0];
-        pd.g1 = gp[1];
+        const uint4* gp = (const uint4*)((const char*)a.grad_out + (pix * G.C + ch0) * EB);
+#pragma unroll
+        for (int h = 0; h < EB / 2; ++h) {
+            const uint4 v = gp[h];
+            pd.gw[4 * h] = v.x; pd.gw[4 * h + 1] = v.y; pd.gw[4 * h + 2] = v.z; pd.gw[4 * h + 3] = v.w;
+        }
         if constexpr (KT > 0) {
             const uint32_t pg_img = ((uint32_t)ho * (uint32_t)G.Wo + (uint32_t)wo) * (uint32_t)G.groups + (uint32_t)g;
-            load_record<float, KT * KT>(pd.rec, roff, pg_img * (uint32_t)(KT * KT * 8), rmk,
-                                        pg_img * (uint32_t)(KT * KT * 4));
+            load_record<T, KT * KT>(pd.rec, roff, pg_img * (uint32_t)(KT * KT * 2 * EB), rmk,
+                                    pg_img * (uint32_t)(KT * KT * EB));
         }
+    };
+    auto mval = [&](uint32_t raw) {
+        return EB == 4 ? __uint_as_float(raw) : Elem<T>::widen(raw);
     };
 
     // The 16 pixel slots of a wave take pixels NT/64 apart, so that two
@@ -1358,17 +1417,22 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
         const int eh = e / EW, ew = e - eh * EW;
         const int ho = hlo + eh, wo = wlo + ew;
         const int bxi = wo * G.stride - G.pad + G.c0, byi = ho * G.stride - G.pad + G.c0;
-        const float go[8] = {cur.g0.x, cur.g0.y, cur.g0.z, cur.g0.w, cur.g1.x, cur.g1.y, cur.g1.z, cur.g1.w};
+        float go[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            if constexpr (EB == 4) go[c] = __uint_as_float(cur.gw[c]);
+            else go[c] = Elem<T>::widen((c & 1) ? cur.gw[c >> 1] >> 16 : cur.gw[c >> 1] & 0xffffu);
+        }
         if constexpr (KT > 0) {
             constexpr int PK = KT * KT;
             float mx = 0.f, inv = 1.f;
             if (G.softmax) {
-                mx = __uint_as_float(cur.rec.mask[0]);
+                mx = mval(cur.rec.mask[0]);
 #pragma unroll
-                for (int q = 1; q < PK; ++q) mx = fmaxf(mx, __uint_as_float(cur.rec.mask[q]));
+                for (int q = 1; q < PK; ++q) mx = fmaxf(mx, mval(cur.rec.mask[q]));
                 float sum = 0.f;
 #pragma unroll
-                for (int q = 0; q < PK; ++q) sum += __expf(__uint_as_float(cur.rec.mask[q]) - mx);
+                for (int q = 0; q < PK; ++q) sum += __expf(mval(cur.rec.mask[q]) - mx);
                 inv = 1.0f / sum;
             }
 #pragma unroll
@@ -1376,26 +1440,26 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
 #pragma unroll
                 for (int j = 0; j < KT; ++j) {
                     const int q = i * KT + j;
-                    float m = __uint_as_float(cur.rec.mask[q]);
+                    float m = mval(cur.rec.mask[q]);
                     if (G.softmax) m = __expf(m - mx) * inv;
-                    point(i, j, bxi, byi, record_pair<float, PK>(cur.rec, q), m, go);
+                    point(i, j, bxi, byi, record_pair<T, PK>(cur.rec, q), m, go);
                 }
         } else {
             const size_t pg = (((size_t)n * G.Ho + ho) * G.Wo + wo) * G.groups + g;
-            const float* off = (const float*)a.offset + pg * G.P * 2;
-            const float* mk = (const float*)a.mask + pg * G.P;
+            const T* off = (const T*)a.offset + pg * G.P * 2;
+            const T* mk = (const T*)a.mask + pg * G.P;
             float mx = 0.f, inv = 1.f;
             if (G.softmax) {
-                mx = mk[0];
-                for (int q = 1; q < G.P; ++q) mx = fmaxf(mx, mk[q]);
+                mx = ld1(mk);
+                for (int q = 1; q < G.P; ++q) mx = fmaxf(mx, ld1(mk + q));
                 float sum = 0.f;
-                for (int q = 0; q < G.P; ++q) sum += __expf(mk[q] - mx);
+                for (int q = 0; q < G.P; ++q) sum += __expf(ld1(mk + q) - mx);
                 inv = 1.0f / sum;
             }
             for (int i = 0; i < K; ++i)
                 for (int j = 0; j < K; ++j) {
                     const int q = i * K + j;
-                    float m = mk[q];
+                    float m = ld1(mk + q);
                     if (G.softmax) m = __expf(m - mx) * inv;
                     point(i, j, bxi, byi, ld2(off + 2 * q), m, go);
                 }
@@ -1403,15 +1467,15 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
     }
     __syncthreads();
 
-    // write the tile: 16 bytes (4 channels) per lane
-    char* gin = (char*)a.grad_input + (size_t)n * G.in_image_bytes + slab * 128u;
+    // write the tile, 4 channels per lane, rounded once to the dtype
+    char* gin = (char*)a.grad_input + (size_t)n * G.in_image_bytes + slab * (32u * EB);
     for (int i = t; i < th * tw * 8; i += NT) {
         const int px = i >> 3, q4 = i & 7;
         const int cy = px / tw, cx = px - cy * tw;
         const int qx = qx0 + cx, qy = qy0 + cy;
         const float* src = owner_tile + (cy * og.TW + cx) * kOwnerStride + q4 * 4;
-        *(float4*)(gin + (size_t)qy * G.in_line_bytes + (size_t)qx * G.in_row_bytes + q4 * 16) =
-            make_float4(src[0], src[1], src[2], src[3]);
+        const float v[4] = {src[0], src[1], src[2], src[3]};
+        store<T, 4 * EB>(gin + (size_t)qy * G.in_line_bytes + (size_t)qx * G.in_row_bytes + q4 * (4 * EB), v);
     }
 }
 

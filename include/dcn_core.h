@@ -105,8 +105,14 @@ int dcn_core_forward(const void* input, const void* offset, const void* mask, vo
  * Samples that contribute nothing to the forward get zero gradients.  The
  * three outputs are overwritten, never accumulated into.  The pages print
  * no gradient formulas; these are the derivatives of the definition.
- * Same arguments and errors as dcn_core_forward; dtype must be DCN_F32
- * (half precision returns DCN_ERR_UNSUPPORTED). */
+ * Same arguments and errors as dcn_core_forward.  The arithmetic is binary32
+ * for every dtype; each gradient is rounded once to the dtype, except that in
+ * half precision a grad_input element that also receives corners far from
+ * their sample's base (offsets beyond about 4 pixels times offset_scale) gets
+ * them through half-precision atomic adds, one rounding each.  Half precision
+ * needs group rows of 32, 64 or 128 bytes, channel rows a multiple of 128
+ * bytes, 16-byte aligned input, grad_output and grad_input, stride <= 4 and
+ * K <= 7; other half-precision calls return DCN_ERR_UNSUPPORTED. */
 int dcn_core_backward(const void* input, const void* offset, const void* mask,
                       const void* grad_output, void* grad_input, void* grad_offset,
                       void* grad_mask, int N, int H, int W, int G, int Cg, int K, int stride,

@@ -26,15 +26,24 @@ RTOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
 ATOL = {"f32": 0.0, "f16": 2.0 ** -24, "bf16": 0.0}
 
 
-def bound(ref, S, n_terms, dtype, slack=32):
-    return RTOL[dtype] * np.abs(ref) + (np.asarray(n_terms, np.float64) + slack) * U * S + ATOL[dtype]
+# unit roundoff of the storage formats (a result rounded to one of them, or
+# summed by atomics in it, carries this relative error per rounding)
+U_STORE = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
 
 
-def compare(gpu, ref, S, n_terms, dtype, slack=32):
+def bound(ref, S, n_terms, dtype, slack=32, store_roundings=0):
+    """store_roundings: how many times a partial sum of magnitude <= S may be
+    rounded to the storage format besides the final rounding (half-precision
+    atomics add that many)."""
+    return (RTOL[dtype] * np.abs(ref) + (np.asarray(n_terms, np.float64) + slack) * U * S + ATOL[dtype]
+            + store_roundings * U_STORE[dtype] * S)
+
+
+def compare(gpu, ref, S, n_terms, dtype, slack=32, store_roundings=0):
     """Returns a dict of statistics; 'ok' is True when every element is within bound."""
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
-    b = bound(ref, S, n_terms, dtype, slack)
+    b = bound(ref, S, n_terms, dtype, slack, store_roundings)
     err = np.abs(gpu - ref)
     finite = np.isfinite(gpu)
     ratio = np.where(b > 0, err / np.where(b > 0, b, 1.0), np.where(err > 0, np.inf, 0.0))
