@@ -6,9 +6,11 @@ bytes per launch / launch time), as a fraction of the 8 TB/s HBM3E peak, and
 Gsamples/s, on the FlashInternImage-T stage-1 shape (DCNv4, fp16 with fp32
 accumulation, N=64, 56x56, C=64, G=4, K=3).  One step = one forward launch
 over the whole batch.  Beside it, in the same JSON line: the bf16 sweep over
-the four FlashInternImage-T stage shapes, the DCNv3 large-channel stage at
-stride 1 and 2, the fp32 forward + backward, and the CPU oracle timed on the
-host cores.
+the four FlashInternImage-T stage shapes, the core op of a whole
+FlashInternImage-T forward (the stage shapes at their depths, 30 launches),
+the DCNv3 large-channel stage at stride 1 and 2, the fp32 forward +
+backward, the half-precision backward, and the CPU oracle timed on the host
+cores.
 
 Inputs are seeded synthetic tensors (no dataset, no weights).  Timing uses
 R rotating copies of every tensor (R * bytes > 512 MB, twice the 256 MB
@@ -161,6 +163,55 @@ def forward_record(w, steps, warmup):
                 Gsamples_s=round(w.samples() / (ms * 1e-3) / 1e9, 3), rotating_sets=R)
 
 
+FII_T_DEPTHS = (4, 4, 18, 4)   # DCN layers per FlashInternImage-T stage (the T config's depths)
+
+
+def fii_t_sweep(steps, warmup):
+    """The core op of one FlashInternImage-T forward over a batch of 64: the
+    four bf16 stage shapes at their depths (30 launches, each layer on its
+    own tensors), captured in one graph and replayed.  Reports the core-op
+    time per batch and per image."""
+    layers = []
+    for depth, name in zip(FII_T_DEPTHS, inputs.BF16_SWEEP):
+        w = inputs.WORKLOADS[name]
+        host = inputs.make(w, with_grad=False)
+        for _ in range(depth):
+            d = {k: v.to("cuda") for k, v in host.items()}
+            d["out"] = torch.empty(w.shapes()["output"], dtype=d["input"].dtype, device="cuda")
+            layers.append((w, launcher(w), d))
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        h = stream.cuda_stream
+        for _ in range(warmup):
+            for w, launch, d in layers:
+                launch(d, h)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        h = torch.cuda.current_stream().cuda_stream
+        for w, launch, d in layers:
+            launch(d, h)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = sum(w.min_bytes_forward() for w, _, _ in layers)
+    n_img = layers[0][0].N
+    del g, layers
+    torch.cuda.empty_cache()
+    return dict(depths=list(FII_T_DEPTHS), launches=sum(FII_T_DEPTHS), batch=n_img,
+                us_per_batch=round(ms * 1e3, 2), us_per_image=round(ms * 1e3 / n_img, 3),
+                images_per_s_core_op=round(n_img / (ms * 1e-3), 1), min_bytes=nbytes,
+                GBps=round(nbytes / (ms * 1e-3) / 1e9, 1))
+
+
 def cpu_baseline(w):
     """The oracle as it stands, on the host cores, over whole batches of the
     headline workload, repeated until at least ~10 s of wall time."""
@@ -294,6 +345,10 @@ def main():
                                frac_hbm=round(wh.min_bytes_backward() / (hms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)))
             log(f"backward c5 {dt}: {halves[-1]['us']} us")
         extra["backward_half"] = halves
+        fii = fii_t_sweep(max(5, args.steps // 20), 2)
+        extra["fii_t_core_op"] = fii
+        log(f"FlashInternImage-T core op: {fii['us_per_batch']} us per batch of {fii['batch']}, "
+            f"{fii['us_per_image']} us per image")
 
     cpu = None
     if not args.quick and not args.no_cpu_baseline:
