@@ -156,7 +156,16 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan, 
             if (th > c.Ho) th = c.Ho;
             if (th < 1) continue;
             if (DCN_TILE_FORCE_TW && (tw != DCN_TILE_FORCE_TW || th != DCN_TILE_FORCE_TH)) continue;
-            const int rh = (th - 1) * c.stride + 2 * ml + 2, rw = (tw - 1) * c.stride + 2 * ml + 2;
+            // A region never needs more than the map and a one-pixel border
+            // (tile_coord starts it no earlier than -1).  When that is all of
+            // it on both axes the kernel reads no memory outside the region;
+            // one more zero row then gives off-map samples a 2x2 block of
+            // zeros to read.
+            int rh = (th - 1) * c.stride + 2 * ml + 2, rw = (tw - 1) * c.stride + 2 * ml + 2;
+            const bool whole = rh >= c.H + 2 && rw >= c.W + 2;
+            if (rh > c.H + 2) rh = c.H + 2;
+            if (rw > c.W + 2) rw = c.W + 2;
+            if (whole) rh = c.H + 3;
             const int64_t lds = (int64_t)rh * rw * 128;
             if (lds > max_lds) continue;
             const uint64_t tx = (uint64_t)((c.Wo + tw - 1) / tw), ty = (uint64_t)((c.Ho + th - 1) / th);
@@ -171,7 +180,7 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan, 
             const double cost = (double)tiles * ((double)lanes * 900.0 * occ_penalty + (double)rh * rw * 8 * 3.0);
             if (best < 0 || cost < best) {
                 best = cost;
-                plan.tg = TileGeo{th, tw, rh, rw, ml, 0, (uint32_t)tx, (uint32_t)ty, slabs};
+                plan.tg = TileGeo{th, tw, rh, rw, ml, 0, whole ? 1 : 0, (uint32_t)tx, (uint32_t)ty, slabs};
                 plan.threads = nt;
                 plan.lds_bytes = (uint32_t)lds;
                 plan.blocks = tiles;
@@ -195,8 +204,12 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan, 
 template <typename T, int KT, int NT, bool SM>
 int launch_tiled(const FwdArgs& a, const TilePlan& pl, hipStream_t st)
 {
-    hipLaunchKernelGGL((dcn_forward_tiled<T, KT, NT, SM>), dim3((uint32_t)pl.blocks), dim3(NT), pl.lds_bytes, st, a,
-                       pl.tg);
+    if (pl.tg.whole)
+        hipLaunchKernelGGL((dcn_forward_tiled<T, KT, NT, SM, true>), dim3((uint32_t)pl.blocks), dim3(NT), pl.lds_bytes,
+                           st, a, pl.tg);
+    else
+        hipLaunchKernelGGL((dcn_forward_tiled<T, KT, NT, SM, false>), dim3((uint32_t)pl.blocks), dim3(NT),
+                           pl.lds_bytes, st, a, pl.tg);
     return launch_status();
 }
 

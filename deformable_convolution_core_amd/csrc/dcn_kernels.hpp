@@ -376,6 +376,7 @@ struct TileGeo {
     int RH, RW;              // staged input region, pixels
     int ML;                  // region origin = first tile centre - ML (both axes)
     int gshift;              // log2(Cg * elem_bytes / 32): lanes per group = 1 << gshift
+    int whole;               // 1: the region is the whole map plus a one-pixel border
     uint32_t tiles_x, tiles_y, slabs;
     uint32_t off_image_bytes, mask_image_bytes;   // one image of offset / mask
     float tap_x[kMaxTiledTaps];                   // (float)(i*dilation - c0) of point p
@@ -555,6 +556,8 @@ __device__ __forceinline__ TiledPoint tiled_fetch(const Geometry& G, const Tiled
             pt.raw[k][4] = v1.x; pt.raw[k][5] = v1.y; pt.raw[k][6] = v1.z; pt.raw[k][7] = v1.w;
         }
     } else {
+        // outside the staged region: gather from memory, or nothing at all
+        // for a sample with no corner on the map (or a NaN coordinate)
         float fx = floorf(x), fy = floorf(y);
         lx = x - fx;
         ly = y - fy;
@@ -566,19 +569,61 @@ __device__ __forceinline__ TiledPoint tiled_fetch(const Geometry& G, const Tiled
         const bool vk[4] = {vy0 && vx0, vy0 && vx1, vy1 && vx0, vy1 && vx1};
         const uint32_t a00 = (uint32_t)y0 * G.in_line_bytes + (uint32_t)x0 * G.in_row_bytes;
         const uint32_t ck[4] = {0u, G.in_row_bytes, G.in_line_bytes, G.in_line_bytes + G.in_row_bytes};
+        if (inmap) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t o0 = vk[k] ? a00 + ck[k] + L.gl_first : kOOB;
-            const uint32_t o1 = vk[k] ? a00 + ck[k] + L.gl_second : kOOB;
-            const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rin, o0, 0, 0);
-            const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rin, o1, 0, 0);
-            pt.raw[k][0] = v0[0]; pt.raw[k][1] = v0[1]; pt.raw[k][2] = v0[2]; pt.raw[k][3] = v0[3];
-            pt.raw[k][4] = v1[0]; pt.raw[k][5] = v1[1]; pt.raw[k][6] = v1[2]; pt.raw[k][7] = v1[3];
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t o0 = vk[k] ? a00 + ck[k] + L.gl_first : kOOB;
+                const uint32_t o1 = vk[k] ? a00 + ck[k] + L.gl_second : kOOB;
+                const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rin, o0, 0, 0);
+                const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rin, o1, 0, 0);
+                pt.raw[k][0] = v0[0]; pt.raw[k][1] = v0[1]; pt.raw[k][2] = v0[2]; pt.raw[k][3] = v0[3];
+                pt.raw[k][4] = v1[0]; pt.raw[k][5] = v1[1]; pt.raw[k][6] = v1[2]; pt.raw[k][7] = v1[3];
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) pt.raw[k][c] = 0u;
         }
     }
     // bilinear weights with the modulation folded in; each is formed with
     // relative error <= 2 ulp (the one-minus factors are fused, so a weight
     // near zero is not the difference of two rounded values)
+    const float mly = mm * ly, mhy = fmaf(-mm, ly, mm);
+    pt.w[0] = fmaf(-mhy, lx, mhy);
+    pt.w[1] = mhy * lx;
+    pt.w[2] = fmaf(-mly, lx, mly);
+    pt.w[3] = mly * lx;
+    return pt;
+}
+
+// tiled_fetch for a region holding the whole map, a one-pixel zero border
+// and one more zero row (origin -1, -1; rows H and H + 1 are zero): every
+// sample with a corner on the map is inside it, and any other sample (or a
+// NaN coordinate) reads the 2x2 block of zeros at the bottom-left with zero
+// weights.  No branch, no gather from memory.
+template <typename T>
+__device__ __forceinline__ TiledPoint whole_fetch(const Geometry& G, const TiledLane& L, const char* lds, float xt,
+                                                  float yt, float2 d, float m)
+{
+    TiledPoint pt;
+    const float x = fmaf(G.alpha, d.x, xt);
+    const float y = fmaf(G.alpha, d.y, yt);
+    const bool inmap = x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H;
+    const uint32_t ix = inmap ? (uint32_t)(cvt_flr(x) + 1) : 0u;
+    const uint32_t iy = inmap ? (uint32_t)(cvt_flr(y) + 1) : (uint32_t)(G.H + 1);
+    const float lx = inmap ? __builtin_amdgcn_fractf(x) : 0.f, ly = inmap ? __builtin_amdgcn_fractf(y) : 0.f;
+    const float mm = inmap ? m : 0.f;
+    const uint32_t a0 = (__umul24(iy, L.RW) + ix) * 128u + L.lane_first;
+    const uint32_t a1 = a0 ^ 16u;
+    const uint32_t ca[4] = {0u, 128u, L.RWB, L.RWB + 128u};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint4 v0 = *(const uint4*)(lds + a0 + ca[k]);
+        const uint4 v1 = *(const uint4*)(lds + a1 + ca[k]);
+        pt.raw[k][0] = v0.x; pt.raw[k][1] = v0.y; pt.raw[k][2] = v0.z; pt.raw[k][3] = v0.w;
+        pt.raw[k][4] = v1.x; pt.raw[k][5] = v1.y; pt.raw[k][6] = v1.z; pt.raw[k][7] = v1.w;
+    }
     const float mly = mm * ly, mhy = fmaf(-mm, ly, mm);
     pt.w[0] = fmaf(-mhy, lx, mhy);
     pt.w[1] = mhy * lx;
@@ -622,8 +667,13 @@ __device__ __forceinline__ TileCoord tile_coord(const Geometry& G, const TileGeo
     c.n = rest / tg.slabs;
     c.ho0 = (int)ty * tg.TH;
     c.wo0 = (int)tx * tg.TW;
-    c.y_lo = c.ho0 * G.stride - G.pad + G.c0 - tg.ML;
-    c.x_lo = c.wo0 * G.stride - G.pad + G.c0 - tg.ML;
+    // A region cut down to the map and a one-pixel border starts no earlier
+    // than -1: rows and columns before it hold nothing a sample on the map
+    // can read.
+    const int y_lo = c.ho0 * G.stride - G.pad + G.c0 - tg.ML;
+    const int x_lo = c.wo0 * G.stride - G.pad + G.c0 - tg.ML;
+    c.y_lo = tg.whole ? -1 : ((tg.RH == G.H + 2 && y_lo < -1) ? -1 : y_lo);   // whole: RH = H + 3
+    c.x_lo = tg.whole ? -1 : ((tg.RW == G.W + 2 && x_lo < -1) ? -1 : x_lo);
     return c;
 }
 
@@ -670,7 +720,7 @@ __device__ __forceinline__ void stage_rows(const Geometry& G, const TileGeo& tg,
 // LDS, then each lane accumulates 32 bytes of channels of one output pixel.
 // The lane's offset/mask record is requested before the wait for the region,
 // so the two memory latencies overlap.
-template <typename T, int KT, int NT, bool SOFTMAX>
+template <typename T, int KT, int NT, bool SOFTMAX, bool WHOLE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DCN_TILE_WAVES_PER_EU)))
 void dcn_forward_tiled(FwdArgs a, TileGeo tg)
 {
@@ -754,7 +804,8 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
                 float m = mval(rec.mask[q]);
                 if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
                 const TiledPoint pt =
-                    tiled_fetch<T>(G, L, lds, rin, xt[q / KT], yt[q % KT], record_pair<T, PK>(rec, q), m);
+                    WHOLE ? whole_fetch<T>(G, L, lds, xt[q / KT], yt[q % KT], record_pair<T, PK>(rec, q), m)
+                          : tiled_fetch<T>(G, L, lds, rin, xt[q / KT], yt[q % KT], record_pair<T, PK>(rec, q), m);
                 tiled_accumulate<T, CPL>(pt, acc);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -773,8 +824,9 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
         auto fetch = [&](int q, const RawPair<T>& d, uint32_t mraw) {
             float m = mval(mraw);
             if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
-            return tiled_fetch<T>(G, L, lds, rin, fmaf(G.alpha, tg.tap_x[q], L.bx), fmaf(G.alpha, tg.tap_y[q], L.by),
-                                  widen_pair<T>(d), m);
+            const float xt = fmaf(G.alpha, tg.tap_x[q], L.bx), yt = fmaf(G.alpha, tg.tap_y[q], L.by);
+            return WHOLE ? whole_fetch<T>(G, L, lds, xt, yt, widen_pair<T>(d), m)
+                         : tiled_fetch<T>(G, L, lds, rin, xt, yt, widen_pair<T>(d), m);
         };
 
         // Software pipeline over the points, two per (rolled) iteration: the

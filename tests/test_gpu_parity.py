@@ -262,6 +262,25 @@ def test_nan_input_does_not_leak_tall(dtype):
     assert nan_pix[0, 0, 31] and nan_pix.sum() == 1
 
 
+@pytest.mark.parametrize("shape", [(14, 14, 16), (7, 7, 32), (28, 28, 8)])
+def test_off_map_samples_never_read_nan(shape):
+    """Small maps (the staged region is the whole map plus its border):
+    samples that miss the map read nothing, even with NaN in every corner
+    pixel of the map; samples that land on it see the NaN."""
+    H, W, G = shape
+    Cg, N = 16, 2
+    x = torch.randn(N, H, W, G * Cg, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16)
+    for yy, xx in ((0, 0), (0, W - 1), (H - 1, 0), (H - 1, W - 1)):
+        x[:, yy, xx] = float("nan")
+    off = torch.full((N, H, W, G, 9, 2), -60.0)   # every sample far off the map
+    off[1] = 0.0                                    # image 1: every sample on the map
+    m = torch.ones(N, H, W, G, 9)
+    out = dcn.forward(x.to(DEV), off.reshape(N, H, W, -1).to(torch.bfloat16).to(DEV),
+                      m.reshape(N, H, W, -1).to(torch.bfloat16).to(DEV), group=G).cpu().float()
+    assert torch.all(out[0] == 0)
+    assert torch.isnan(out[1]).any()
+
+
 def test_nan_input_does_not_leak_to_other_pixels():
     """A NaN at one pixel reaches only outputs whose sample has a corner on
     that pixel; an off-map corner whose address would wrap onto it reads 0."""
