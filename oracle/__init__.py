@@ -53,9 +53,9 @@ def _open(path):
     lib.oracle_out_size.restype = i
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i
-    lib.oracle_forward.argtypes = [dp, dp, dp, dp, dp] + [i] * 9 + [d, i, i]
+    lib.oracle_forward.argtypes = [dp, dp, dp, dp, dp] + [i] * 9 + [d, i, i, i]
     lib.oracle_forward.restype = i
-    lib.oracle_backward.argtypes = [dp] * 11 + [i] * 9 + [d, i, i]
+    lib.oracle_backward.argtypes = [dp] * 11 + [i] * 9 + [d, i, i, i]
     lib.oracle_backward.restype = i
     return lib
 
@@ -112,41 +112,44 @@ def _geometry(input, K, stride, pad, dilation):
 
 
 def forward(input, offset, mask, *, K, stride, pad, dilation, offset_scale,
-            softmax, group, coord_mode=COORD_BINARY32, with_absum=True):
+            softmax, group, coord_mode=COORD_BINARY32, with_absum=True, remove_center=False):
     """Reference forward.
 
     input (N,H,W,G*Cg); offset (N,Ho,Wo,G*P*2) or (N,Ho,Wo,G,P,2) as (dx,dy)
-    pixel offsets; mask (N,Ho,Wo,G*P).  Values are read as float64 (pass the
-    already dtype-rounded tensors).  Returns (out, absum) as float64 arrays of
-    shape (N,Ho,Wo,G*Cg); absum is None unless with_absum.
+    pixel offsets; mask (N,Ho,Wo,G*P).  P = K*K, or K*K - 1 with
+    remove_center (odd K; the centre tap is left out, the other taps keep
+    their order).  Values are read as float64 (pass the already dtype-rounded
+    tensors).  Returns (out, absum) as float64 arrays of shape
+    (N,Ho,Wo,G*Cg); absum is None unless with_absum.
     """
     x = _f64(input)
     N, H, W, C, Ho, Wo = _geometry(x, K, stride, pad, dilation)
     G = int(group)
     if C % G:
         raise ValueError("channels not divisible by group")
-    Cg, P = C // G, K * K
+    Cg, P = C // G, K * K - (1 if remove_center else 0)
     off = _f64(offset).reshape(N, Ho, Wo, G * P * 2)
     msk = _f64(mask).reshape(N, Ho, Wo, G * P)
     out = np.empty((N, Ho, Wo, C), np.float64)
     absum = np.empty_like(out) if with_absum else None
     rc = _load().oracle_forward(_ptr(x), _ptr(off), _ptr(msk), _ptr(out), _ptr(absum),
                                 N, H, W, G, Cg, K, stride, pad, dilation,
-                                float(offset_scale), int(bool(softmax)), int(coord_mode))
+                                float(offset_scale), int(bool(softmax)), int(coord_mode),
+                                int(bool(remove_center)))
     if rc != 0:
         raise ValueError("oracle_forward rejected the sizes")
     return out, absum
 
 
 def backward(input, offset, mask, grad_out, *, K, stride, pad, dilation, offset_scale,
-             softmax, group, coord_mode=COORD_BINARY32, with_scales=True):
+             softmax, group, coord_mode=COORD_BINARY32, with_scales=True, remove_center=False):
     """Reference backward.  Returns a dict with grad_input, grad_offset,
     grad_mask (float64, shaped like input / offset / mask as passed) and, when
     with_scales, gi_abs, gi_cnt, goff_abs, gmask_abs error scales."""
     x = _f64(input)
     N, H, W, C, Ho, Wo = _geometry(x, K, stride, pad, dilation)
     G = int(group)
-    Cg, P = C // G, K * K
+    Cg, P = C // G, K * K - (1 if remove_center else 0)
     off_shape, msk_shape = np.shape(offset), np.shape(mask)
     off = _f64(offset).reshape(N, Ho, Wo, G * P * 2)
     msk = _f64(mask).reshape(N, Ho, Wo, G * P)
@@ -163,7 +166,7 @@ def backward(input, offset, mask, grad_out, *, K, stride, pad, dilation, offset_
         _ptr(sc.get("gi_abs")), _ptr(sc.get("gi_cnt")), _ptr(sc.get("goff_abs")),
         _ptr(sc.get("gmask_abs")),
         N, H, W, G, Cg, K, stride, pad, dilation,
-        float(offset_scale), int(bool(softmax)), int(coord_mode))
+        float(offset_scale), int(bool(softmax)), int(coord_mode), int(bool(remove_center)))
     if rc != 0:
         raise ValueError("oracle_backward rejected the sizes")
     res = dict(grad_input=gi, grad_offset=goff.reshape(off_shape),

@@ -88,6 +88,17 @@ static double coord(int o, int s, int pad, int c0, int tap, int d, double alpha,
     return (double)(o * s - pad + c0) + alpha * ((double)(tap * d - c0) + delta);
 }
 
+/* Index of tap (i, j) among the P points of a (pixel, group): p = i*K + j,
+ * or, with remove_center (DCNv4 option, odd K), the same order with the
+ * centre tap left out (P = K*K - 1).  Returns -1 for the removed tap. */
+static int point_index(int i, int j, int K, int remove_center)
+{
+    int p = i * K + j, centre = (K * K - 1) / 2;
+    if (!remove_center) return p;
+    if (p == centre) return -1;
+    return p < centre ? p : p - 1;
+}
+
 /* Mask values of one (pixel, group): raw, or softmax over P in binary64. */
 static void modulation(const double* logits, int P, int softmax, double* m)
 {
@@ -120,12 +131,13 @@ static int sample_touches_map(double x, double y, int H, int W)
 int oracle_forward(const double* input, const double* offset, const double* mask,
                    double* out, double* absum,
                    int N, int H, int W, int G, int Cg, int K, int stride, int pad,
-                   int dil, double alpha, int softmax, int coord_mode)
+                   int dil, double alpha, int softmax, int coord_mode, int remove_center)
 {
     int Ho = oracle_out_size(H, K, stride, pad, dil);
     int Wo = oracle_out_size(W, K, stride, pad, dil);
     if (N <= 0 || G <= 0 || Cg <= 0 || Ho <= 0 || Wo <= 0) return -1;
-    const int P = K * K, C = G * Cg, c0 = dil * (K - 1) / 2;
+    if (remove_center && (K % 2 == 0 || K < 3)) return -1;
+    const int P = K * K - (remove_center ? 1 : 0), C = G * Cg, c0 = dil * (K - 1) / 2;
 
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (int n = 0; n < N; ++n)
@@ -142,7 +154,8 @@ int oracle_forward(const double* input, const double* offset, const double* mask
 
             for (int i = 0; i < K; ++i)
             for (int j = 0; j < K; ++j) {
-                int p = i * K + j;
+                int p = point_index(i, j, K, remove_center);
+                if (p < 0) continue;
                 double x = coord(wo, stride, pad, c0, i, dil, alpha, off[2 * p], coord_mode);
                 double y = coord(ho, stride, pad, c0, j, dil, alpha, off[2 * p + 1], coord_mode);
                 if (!sample_touches_map(x, y, H, W)) continue;
@@ -192,12 +205,13 @@ int oracle_backward(const double* input, const double* offset, const double* mas
                     double* grad_input, double* grad_offset, double* grad_mask,
                     double* gi_abs, double* gi_cnt, double* goff_abs, double* gmask_abs,
                     int N, int H, int W, int G, int Cg, int K, int stride, int pad,
-                    int dil, double alpha, int softmax, int coord_mode)
+                    int dil, double alpha, int softmax, int coord_mode, int remove_center)
 {
     int Ho = oracle_out_size(H, K, stride, pad, dil);
     int Wo = oracle_out_size(W, K, stride, pad, dil);
     if (N <= 0 || G <= 0 || Cg <= 0 || Ho <= 0 || Wo <= 0) return -1;
-    const int P = K * K, C = G * Cg, c0 = dil * (K - 1) / 2;
+    if (remove_center && (K % 2 == 0 || K < 3)) return -1;
+    const int P = K * K - (remove_center ? 1 : 0), C = G * Cg, c0 = dil * (K - 1) / 2;
     long in_elems = (long)N * H * W * C;
     memset(grad_input, 0, sizeof(double) * in_elems);
     if (gi_abs) memset(gi_abs, 0, sizeof(double) * in_elems);
@@ -219,7 +233,8 @@ int oracle_backward(const double* input, const double* offset, const double* mas
 
             for (int i = 0; i < K; ++i)
             for (int j = 0; j < K; ++j) {
-                int p = i * K + j;
+                int p = point_index(i, j, K, remove_center);
+                if (p < 0) continue;
                 double gdx = 0.0, gdy = 0.0, adx = 0.0, ady = 0.0;
                 gm[p] = 0.0; gm_abs[p] = 0.0;
                 double x = coord(wo, stride, pad, c0, i, dil, alpha, off[2 * p], coord_mode);

@@ -45,11 +45,16 @@ def _bilinear_padded(img, u_pix, v_pix):
     return val
 
 
-def brute_force(inp, off, mask, K, s, pad, d, alpha, softmax, G):
-    """inp (N,H,W,C) float64; off (N,Ho,Wo,G*P*2); mask (N,Ho,Wo,G*P)."""
+def brute_force(inp, off, mask, K, s, pad, d, alpha, softmax, G, remove_center=False):
+    """inp (N,H,W,C) float64; off (N,Ho,Wo,G*P*2); mask (N,Ho,Wo,G*P).
+    remove_center: the K*K taps without the middle one, in the same order."""
     inp = np.asarray(inp, np.float64)
     N, H, W, C = inp.shape
-    Cg, P = C // G, K * K
+    Cg = C // G
+    taps = [(i, j) for i in range(K) for j in range(K)]      # kernel column i -> x, row j -> y
+    if remove_center:
+        taps.remove(((K - 1) // 2, (K - 1) // 2))
+    P = len(taps)
     Ho, Wo = conv_out(H, K, s, pad, d), conv_out(W, K, s, pad, d)
     off = np.asarray(off, np.float64).reshape(N, Ho, Wo, G, P, 2)
     mask = np.asarray(mask, np.float64).reshape(N, Ho, Wo, G, P)
@@ -67,21 +72,19 @@ def brute_force(inp, off, mask, K, s, pad, d, alpha, softmax, G):
                     if softmax:
                         e = [math.exp(v - max(m)) for v in m]
                         m = np.array(e) / sum(e)
-                    for i in range(K):          # kernel column -> x
-                        for j in range(K):      # kernel row -> y
-                            p = i * K + j
-                            gx = (-half + i * d) / Wp
-                            gy = (-half + j * d) / Hp
-                            lx = ref_x + gx * alpha + off[n, ho, wo, g, p, 0] * alpha / Wp
-                            ly = ref_y + gy * alpha + off[n, ho, wo, g, p, 1] * alpha / Hp
-                            u = 2.0 * lx - 1.0
-                            v = 2.0 * ly - 1.0
-                            u_pix = ((u + 1.0) * Wp - 1.0) / 2.0
-                            v_pix = ((v + 1.0) * Hp - 1.0) / 2.0
-                            for c in range(Cg):
-                                ch = g * Cg + c
-                                out[n, ho, wo, ch] += m[p] * _bilinear_padded(
-                                    padded[n, :, :, ch], u_pix, v_pix)
+                    for p, (i, j) in enumerate(taps):
+                        gx = (-half + i * d) / Wp
+                        gy = (-half + j * d) / Hp
+                        lx = ref_x + gx * alpha + off[n, ho, wo, g, p, 0] * alpha / Wp
+                        ly = ref_y + gy * alpha + off[n, ho, wo, g, p, 1] * alpha / Hp
+                        u = 2.0 * lx - 1.0
+                        v = 2.0 * ly - 1.0
+                        u_pix = ((u + 1.0) * Wp - 1.0) / 2.0
+                        v_pix = ((v + 1.0) * Hp - 1.0) / 2.0
+                        for c in range(Cg):
+                            ch = g * Cg + c
+                            out[n, ho, wo, ch] += m[p] * _bilinear_padded(
+                                padded[n, :, :, ch], u_pix, v_pix)
     return out
 
 

@@ -31,8 +31,10 @@ MUTANTS = {
     "skip_rule_too_strict": ("return x > -1.0 && x < (double)W && y > -1.0 && y < (double)H;",
                              "return x >= 0.0 && x < (double)W && y > -1.0 && y < (double)H;"),
     "softmax_unnormalised": ("for (int p = 0; p < P; ++p) m[p] /= sum;", ""),
-    "point_order_transposed": ("int p = i * K + j;\n                double x = coord(wo, stride, pad, c0, i, dil, alpha, off[2 * p], coord_mode);",
-                               "int p = j * K + i;\n                double x = coord(wo, stride, pad, c0, i, dil, alpha, off[2 * p], coord_mode);"),
+    "point_order_transposed": ("int p = i * K + j, centre = (K * K - 1) / 2;",
+                               "int p = j * K + i, centre = (K * K - 1) / 2;"),
+    "removed_tap_not_centre": ("int p = i * K + j, centre = (K * K - 1) / 2;",
+                               "int p = i * K + j, centre = (K * K - 1) / 2 + 1;"),
     "right_edge_off_by_one": ("if (yy < 0 || yy >= H || xx < 0 || xx >= W) continue;\n                    double w =",
                               "if (yy < 0 || yy >= H || xx < 0 || xx > W) continue;\n                    double w ="),
     "offset_pair_swapped": ("alpha, off[2 * p], coord_mode);\n                double y = coord(ho, stride, pad, c0, j, dil, alpha, off[2 * p + 1], coord_mode);\n                if (!sample",
@@ -49,6 +51,9 @@ MUTANTS = {
 def battery():
     """All pins, as zero-argument callables."""
     checks = []
+    for geom in tp.RC_GEOMS:
+        checks.append(lambda g=geom: tp.test_bruteforce_remove_center(g))
+        checks.append(lambda g=geom: tp.test_remove_center_is_full_grid_without_centre(g))
     for geom in tp.GEOMS:
         checks.append(lambda g=geom: tp.test_bruteforce_normalised_form_exact_coords(g))
         checks.append(lambda g=geom: tp.test_bruteforce_binary32_coords_dyadic(g))

@@ -19,9 +19,9 @@ from tests import independent as ind
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
 
 
-def rand_case(rng, N, H, W, G, Cg, K, s, p, d, off_sigma=1.5, mask_sigma=1.0, dyadic=False):
+def rand_case(rng, N, H, W, G, Cg, K, s, p, d, off_sigma=1.5, mask_sigma=1.0, dyadic=False, rc=False):
     Ho, Wo = ind.conv_out(H, K, s, p, d), ind.conv_out(W, K, s, p, d)
-    P = K * K
+    P = K * K - (1 if rc else 0)
     x = rng.standard_normal((N, H, W, G * Cg))
     off = rng.standard_normal((N, Ho, Wo, G * P * 2)) * off_sigma
     if dyadic:  # exactly representable in binary32 -> binary32 coordinates are exact
@@ -30,9 +30,9 @@ def rand_case(rng, N, H, W, G, Cg, K, s, p, d, off_sigma=1.5, mask_sigma=1.0, dy
     return x, off, m
 
 
-def fwd(x, off, m, K, s, p, d, a, sm, G, mode=oracle.COORD_EXACT):
+def fwd(x, off, m, K, s, p, d, a, sm, G, mode=oracle.COORD_EXACT, rc=False):
     out, _ = oracle.forward(x, off, m, K=K, stride=s, pad=p, dilation=d, offset_scale=a,
-                            softmax=sm, group=G, coord_mode=mode, with_absum=False)
+                            softmax=sm, group=G, coord_mode=mode, with_absum=False, remove_center=rc)
     return out
 
 
@@ -69,6 +69,43 @@ def test_bruteforce_binary32_coords_dyadic(geom):
     ref = ind.brute_force(x, off, m, K, s, p, d, a, sm, G)
     got = fwd(x, off, m, K, s, p, d, a, sm, G, mode=oracle.COORD_BINARY32)
     assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+RC_GEOMS = [  # N, H, W, G, Cg, K, s, pad, d, alpha, softmax  (odd K: remove_center)
+    (1, 6, 7, 2, 2, 3, 1, 1, 1, 1.0, True),
+    (2, 7, 6, 1, 3, 3, 2, 1, 1, 0.75, False),
+    (1, 8, 7, 1, 2, 5, 1, 2, 1, 1.25, False),
+    (1, 9, 8, 2, 1, 3, 1, 2, 2, 1.0, True),
+]
+
+
+@pytest.mark.parametrize("geom", RC_GEOMS)
+def test_bruteforce_remove_center(geom):
+    """remove_center (DCNv4 option): the oracle against the brute force
+    written from the normalised-grid form with the middle tap left out."""
+    N, H, W, G, Cg, K, s, p, d, a, sm = geom
+    rng = np.random.default_rng(31 + K + 5 * s)
+    x, off, m = rand_case(rng, N, H, W, G, Cg, K, s, p, d, rc=True)
+    ref = ind.brute_force(x, off, m, K, s, p, d, a, sm, G, remove_center=True)
+    got = fwd(x, off, m, K, s, p, d, a, sm, G, rc=True)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("geom", RC_GEOMS)
+def test_remove_center_is_full_grid_without_centre(geom):
+    """Leaving the centre tap out equals the full grid with the centre's
+    weight at zero: a raw mask of 0 there, or a softmax logit of -inf (whose
+    exponential is 0, so the other taps normalise over the same P - 1)."""
+    N, H, W, G, Cg, K, s, p, d, a, sm = geom
+    rng = np.random.default_rng(37 + K)
+    x, off, m = rand_case(rng, N, H, W, G, Cg, K, s, p, d, rc=True)
+    Ho, Wo = off.shape[1], off.shape[2]
+    P, c = K * K - 1, (K * K - 1) // 2
+    off_full = np.insert(off.reshape(N, Ho, Wo, G, P, 2), c, 0.0, axis=4).reshape(N, Ho, Wo, -1)
+    m_full = np.insert(m.reshape(N, Ho, Wo, G, P), c, -np.inf if sm else 0.0, axis=4).reshape(N, Ho, Wo, -1)
+    got = fwd(x, off, m, K, s, p, d, a, sm, G, rc=True)
+    full = fwd(x, off_full, m_full, K, s, p, d, a, sm, G)
+    assert np.max(np.abs(got - full)) <= 1e-13 * max(1.0, np.max(np.abs(full)))
 
 
 def test_binary32_coords_close_for_general_offsets():
