@@ -13,8 +13,11 @@ section): for every output pixel and channel group, sample the group's
 channels bilinearly (zero outside the map) at K*K offset positions around the
 pixel and sum them weighted by the per-point mask, softmax-normalised for
 DCNv3 and raw for DCNv4.  Tensors are channels-last:
-input (N,H,W,G*Cg), offset (N,Ho,Wo,G*K*K*2) as (dx,dy) pixel pairs,
-mask (N,Ho,Wo,G*K*K), output (N,Ho,Wo,G*Cg).
+input (N,H,W,G*Cg), offset (N,Ho,Wo,G*P*2) as (dx,dy) pixel pairs,
+mask (N,Ho,Wo,G*P), output (N,Ho,Wo,G*Cg), with P = K*K points, or K*K - 1
+with ``remove_center`` (odd K; the centre tap is left out).  DCNv4's single
+offset-and-weight tensor is (N,Ho,Wo,G*3P): per (pixel, group) the 2P
+offsets, then the P mask values (``forward_packed`` / ``backward_packed``).
 """
 from __future__ import annotations
 
@@ -23,8 +26,9 @@ import os
 
 import torch
 
-__all__ = ["forward", "backward", "out_size", "dcn_core", "DCNCoreFunction", "DCNError",
-           "library_path", "load_library"]
+__all__ = ["forward", "backward", "forward_packed", "backward_packed", "out_size", "dcn_core",
+           "dcnv4_core", "DCNCoreFunction", "DCNv4CoreFunction", "DCNError", "library_path",
+           "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libdcn_core.so")
@@ -32,7 +36,9 @@ _lib = None
 
 DCN_F32, DCN_F16, DCN_BF16 = 0, 1, 2
 _DTYPE = {torch.float32: DCN_F32, torch.float16: DCN_F16, torch.bfloat16: DCN_BF16}
-EXPORTED = ("dcn_core_out_size", "dcn_core_forward", "dcn_core_backward", "dcn_status_string")
+EXPORTED = ("dcn_core_out_size", "dcn_core_forward", "dcn_core_backward", "dcn_core_forward_ex",
+            "dcn_core_backward_ex", "dcn_status_string")
+FLAG_SOFTMAX, FLAG_REMOVE_CENTER, FLAG_PACKED = 1, 2, 4
 
 
 class DCNError(RuntimeError):
@@ -61,6 +67,10 @@ def load_library(path: str | None = None):
     lib.dcn_core_forward.restype = i
     lib.dcn_core_backward.argtypes = [vp] * 7 + [i] * 9 + [f, i, i, vp]
     lib.dcn_core_backward.restype = i
+    lib.dcn_core_forward_ex.argtypes = [vp] * 4 + [i] * 9 + [f, i, i, vp]
+    lib.dcn_core_forward_ex.restype = i
+    lib.dcn_core_backward_ex.argtypes = [vp] * 7 + [i] * 9 + [f, i, i, vp]
+    lib.dcn_core_backward_ex.restype = i
     lib.dcn_status_string.argtypes = [i]
     lib.dcn_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -87,68 +97,127 @@ def _stream(dev: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def _geometry(input, offset, mask, kernel_size, stride, pad, dilation, group):
+def points(kernel_size: int, remove_center: bool = False) -> int:
+    """Sampling points per (pixel, group): K*K, less the centre tap if removed."""
+    return kernel_size * kernel_size - (1 if remove_center else 0)
+
+
+def _flags(softmax, remove_center, packed):
+    return ((FLAG_SOFTMAX if softmax else 0) | (FLAG_REMOVE_CENTER if remove_center else 0)
+            | (FLAG_PACKED if packed else 0))
+
+
+def _check_tensor(name, t, ref):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (channels-last NHWC)")
+    if t.dtype != ref.dtype or t.device != ref.device:
+        raise ValueError(f"{name} must share input's dtype and device")
+
+
+def _geometry(input, offset, mask, kernel_size, stride, pad, dilation, group, remove_center=False):
+    """Shapes of a call; mask None means the packed layout (offset holds the records)."""
     if input.dim() != 4:
         raise ValueError("input must be (N, H, W, G*Cg)")
     N, H, W, C = input.shape
     if group < 1 or C % group:
         raise ValueError(f"channels {C} not divisible by group {group}")
+    if remove_center and (kernel_size % 2 == 0 or kernel_size < 3):
+        raise ValueError("remove_center needs an odd kernel_size >= 3")
     Ho = out_size(H, kernel_size, stride, pad, dilation)
     Wo = out_size(W, kernel_size, stride, pad, dilation)
     if Ho <= 0 or Wo <= 0:
         raise ValueError("empty output grid for this geometry")
-    P = kernel_size * kernel_size
-    if tuple(offset.shape) != (N, Ho, Wo, group * P * 2):
-        raise ValueError(f"offset must be {(N, Ho, Wo, group * P * 2)}, got {tuple(offset.shape)}")
-    if tuple(mask.shape) != (N, Ho, Wo, group * P):
-        raise ValueError(f"mask must be {(N, Ho, Wo, group * P)}, got {tuple(mask.shape)}")
-    for name, t in (("input", input), ("offset", offset), ("mask", mask)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous (channels-last NHWC)")
-        if t.dtype != input.dtype or t.device != input.device:
-            raise ValueError(f"{name} must share input's dtype and device")
+    P = points(kernel_size, remove_center)
+    if mask is None:
+        if tuple(offset.shape) != (N, Ho, Wo, group * P * 3):
+            raise ValueError(f"offset_mask must be {(N, Ho, Wo, group * P * 3)}, got {tuple(offset.shape)}")
+        tensors = (("input", input), ("offset_mask", offset))
+    else:
+        if tuple(offset.shape) != (N, Ho, Wo, group * P * 2):
+            raise ValueError(f"offset must be {(N, Ho, Wo, group * P * 2)}, got {tuple(offset.shape)}")
+        if tuple(mask.shape) != (N, Ho, Wo, group * P):
+            raise ValueError(f"mask must be {(N, Ho, Wo, group * P)}, got {tuple(mask.shape)}")
+        tensors = (("input", input), ("offset", offset), ("mask", mask))
+    for name, t in tensors:
+        _check_tensor(name, t, input)
     if input.dtype not in _DTYPE:
         raise ValueError(f"unsupported dtype {input.dtype}")
     return N, H, W, C, C // group, Ho, Wo
 
 
-def forward(input, offset, mask, *, kernel_size=3, stride=1, pad=1, dilation=1,
-            offset_scale=1.0, softmax=False, group=1, out=None) -> torch.Tensor:
-    """Forward sampling core on input.device, on torch's current stream."""
-    N, H, W, C, Cg, Ho, Wo = _geometry(input, offset, mask, kernel_size, stride, pad, dilation, group)
+def _forward(input, offset, mask, kernel_size, stride, pad, dilation, offset_scale, softmax, group,
+             remove_center, out):
+    N, H, W, C, Cg, Ho, Wo = _geometry(input, offset, mask, kernel_size, stride, pad, dilation, group,
+                                       remove_center)
     if out is None:
         out = torch.empty((N, Ho, Wo, C), dtype=input.dtype, device=input.device)
     elif tuple(out.shape) != (N, Ho, Wo, C) or out.dtype != input.dtype or not out.is_contiguous() \
             or out.device != input.device:
         raise ValueError("out has the wrong shape, dtype, device or layout")
+    flags = _flags(softmax, remove_center, mask is None)
     with torch.cuda.device(input.device):
-        rc = load_library().dcn_core_forward(
-            _ptr(input), _ptr(offset), _ptr(mask), _ptr(out), N, H, W, group, Cg, kernel_size,
-            stride, pad, dilation, float(offset_scale), int(bool(softmax)), _DTYPE[input.dtype],
+        rc = load_library().dcn_core_forward_ex(
+            _ptr(input), _ptr(offset), None if mask is None else _ptr(mask), _ptr(out), N, H, W, group,
+            Cg, kernel_size, stride, pad, dilation, float(offset_scale), flags, _DTYPE[input.dtype],
             _stream(input.device))
-    _check(rc, "dcn_core_forward")
+    _check(rc, "dcn_core_forward_ex")
     return out
 
 
-def backward(input, offset, mask, grad_output, *, kernel_size=3, stride=1, pad=1, dilation=1,
-             offset_scale=1.0, softmax=False, group=1):
-    """Gradients (grad_input, grad_offset, grad_mask) for grad_output."""
-    N, H, W, C, Cg, Ho, Wo = _geometry(input, offset, mask, kernel_size, stride, pad, dilation, group)
+def _backward(input, offset, mask, grad_output, kernel_size, stride, pad, dilation, offset_scale, softmax,
+              group, remove_center):
+    N, H, W, C, Cg, Ho, Wo = _geometry(input, offset, mask, kernel_size, stride, pad, dilation, group,
+                                       remove_center)
     if tuple(grad_output.shape) != (N, Ho, Wo, C) or grad_output.dtype != input.dtype \
             or not grad_output.is_contiguous() or grad_output.device != input.device:
         raise ValueError("grad_output has the wrong shape, dtype, device or layout")
     gi = torch.empty_like(input)
     goff = torch.empty_like(offset)
-    gm = torch.empty_like(mask)
+    gm = None if mask is None else torch.empty_like(mask)
+    flags = _flags(softmax, remove_center, mask is None)
     with torch.cuda.device(input.device):
-        rc = load_library().dcn_core_backward(
-            _ptr(input), _ptr(offset), _ptr(mask), _ptr(grad_output), _ptr(gi), _ptr(goff), _ptr(gm),
-            N, H, W, group, Cg, kernel_size, stride, pad, dilation, float(offset_scale),
-            int(bool(softmax)), _DTYPE[input.dtype], _stream(input.device))
-    _check(rc, "dcn_core_backward")
+        rc = load_library().dcn_core_backward_ex(
+            _ptr(input), _ptr(offset), None if mask is None else _ptr(mask), _ptr(grad_output), _ptr(gi),
+            _ptr(goff), None if gm is None else _ptr(gm), N, H, W, group, Cg, kernel_size, stride, pad,
+            dilation, float(offset_scale), flags, _DTYPE[input.dtype], _stream(input.device))
+    _check(rc, "dcn_core_backward_ex")
     return gi, goff, gm
+
+
+def forward(input, offset, mask, *, kernel_size=3, stride=1, pad=1, dilation=1,
+            offset_scale=1.0, softmax=False, group=1, remove_center=False, out=None) -> torch.Tensor:
+    """Forward sampling core on input.device, on torch's current stream."""
+    if mask is None:
+        raise ValueError("mask is required (forward_packed takes the packed layout)")
+    return _forward(input, offset, mask, kernel_size, stride, pad, dilation, offset_scale, softmax, group,
+                    remove_center, out)
+
+
+def backward(input, offset, mask, grad_output, *, kernel_size=3, stride=1, pad=1, dilation=1,
+             offset_scale=1.0, softmax=False, group=1, remove_center=False):
+    """Gradients (grad_input, grad_offset, grad_mask) for grad_output."""
+    if mask is None:
+        raise ValueError("mask is required (backward_packed takes the packed layout)")
+    return _backward(input, offset, mask, grad_output, kernel_size, stride, pad, dilation, offset_scale,
+                     softmax, group, remove_center)
+
+
+def forward_packed(input, offset_mask, *, kernel_size=3, stride=1, pad=1, dilation=1,
+                   offset_scale=1.0, softmax=False, group=1, remove_center=False, out=None) -> torch.Tensor:
+    """Forward with DCNv4's single offset-and-mask tensor (N, Ho, Wo, G*3P)."""
+    return _forward(input, offset_mask, None, kernel_size, stride, pad, dilation, offset_scale, softmax,
+                    group, remove_center, out)
+
+
+def backward_packed(input, offset_mask, grad_output, *, kernel_size=3, stride=1, pad=1, dilation=1,
+                    offset_scale=1.0, softmax=False, group=1, remove_center=False):
+    """Gradients (grad_input, grad_offset_mask) of forward_packed; the second
+    has the packed record layout of offset_mask."""
+    gi, gom, _ = _backward(input, offset_mask, None, grad_output, kernel_size, stride, pad, dilation,
+                           offset_scale, softmax, group, remove_center)
+    return gi, gom
 
 
 class DCNCoreFunction(torch.autograd.Function):
@@ -157,21 +226,48 @@ class DCNCoreFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, input, offset, mask, kernel_size, stride, pad, dilation, offset_scale,
-                softmax, group):
+                softmax, group, remove_center=False):
         ctx.save_for_backward(input, offset, mask)
         ctx.cfg = dict(kernel_size=kernel_size, stride=stride, pad=pad, dilation=dilation,
-                       offset_scale=offset_scale, softmax=softmax, group=group)
+                       offset_scale=offset_scale, softmax=softmax, group=group,
+                       remove_center=remove_center)
         return forward(input, offset, mask, **ctx.cfg)
 
     @staticmethod
     def backward(ctx, grad_out):
         input, offset, mask = ctx.saved_tensors
         gi, goff, gm = backward(input, offset, mask, grad_out.contiguous(), **ctx.cfg)
-        return gi, goff, gm, None, None, None, None, None, None, None
+        return gi, goff, gm, None, None, None, None, None, None, None, None
+
+
+class DCNv4CoreFunction(torch.autograd.Function):
+    """Autograd wrapper of the packed (DCNv4) layout."""
+
+    @staticmethod
+    def forward(ctx, input, offset_mask, kernel_size, stride, pad, dilation, offset_scale, group,
+                remove_center=False):
+        ctx.save_for_backward(input, offset_mask)
+        ctx.cfg = dict(kernel_size=kernel_size, stride=stride, pad=pad, dilation=dilation,
+                       offset_scale=offset_scale, softmax=False, group=group,
+                       remove_center=remove_center)
+        return forward_packed(input, offset_mask, **ctx.cfg)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        input, offset_mask = ctx.saved_tensors
+        gi, gom = backward_packed(input, offset_mask, grad_out.contiguous(), **ctx.cfg)
+        return gi, gom, None, None, None, None, None, None, None
 
 
 def dcn_core(input, offset, mask, kernel_size=3, stride=1, pad=1, dilation=1, offset_scale=1.0,
-             softmax=False, group=1):
+             softmax=False, group=1, remove_center=False):
     """Differentiable entry point (forward + analytic backward in HIP)."""
     return DCNCoreFunction.apply(input, offset, mask, kernel_size, stride, pad, dilation,
-                                 offset_scale, softmax, group)
+                                 offset_scale, softmax, group, remove_center)
+
+
+def dcnv4_core(input, offset_mask, kernel_size=3, stride=1, pad=1, dilation=1, offset_scale=1.0,
+               group=1, remove_center=False):
+    """Differentiable DCNv4 core: raw mask, offsets and mask in one packed tensor."""
+    return DCNv4CoreFunction.apply(input, offset_mask, kernel_size, stride, pad, dilation,
+                                   offset_scale, group, remove_center)

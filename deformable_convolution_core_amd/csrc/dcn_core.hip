@@ -32,6 +32,13 @@ struct Call {
     int N, H, W, G, Cg, K, stride, pad, dil, Ho, Wo;
     float alpha;
     int softmax, dtype, ebytes;
+    int rc;              // remove_center: the centre tap is left out
+    int packed;          // offsets and mask share one record of 3P values per (pixel, group)
+    int P;               // points per (pixel, group): K*K - rc
+    int off_stride;      // elements per (pixel, group) record of the offset tensor
+    int mask_stride;     // ... of the mask tensor (the packed record for both when packed)
+    // The K = 3 specialisations index the full 3 x 3 grid at compile time.
+    bool k3() const { return K == 3 && !rc; }
 };
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -47,24 +54,30 @@ int elem_bytes(int dtype)
 }
 
 // Host validation shared by forward and backward; touches no device state.
+// remove_center needs an odd K >= 3; packed selects the one-record layout.
 int validate(Call& c, int N, int H, int W, int G, int Cg, int K, int stride, int pad, int dil,
-             float alpha, int softmax, int dtype)
+             float alpha, int softmax, int dtype, int remove_center = 0, int packed = 0)
 {
-    c = Call{N, H, W, G, Cg, K, stride, pad, dil, 0, 0, alpha, softmax, dtype, elem_bytes(dtype)};
+    c = Call{N, H, W, G, Cg, K, stride, pad, dil, 0, 0, alpha, softmax, dtype, elem_bytes(dtype),
+             remove_center, packed, 0, 0, 0};
     if (c.ebytes == 0) return DCN_ERR_INVALID_ARG;
     if (N < 0 || H < 1 || W < 1 || G < 1 || Cg < 1 || K < 1 || stride < 1 || dil < 1 || pad < 0)
         return DCN_ERR_INVALID_ARG;
     if (softmax != 0 && softmax != 1) return DCN_ERR_INVALID_ARG;
+    if (remove_center != 0 && remove_center != 1) return DCN_ERR_INVALID_ARG;
+    if (remove_center && (K % 2 == 0 || K < 3)) return DCN_ERR_INVALID_ARG;
+    c.P = K * K - remove_center;
+    c.off_stride = packed ? 3 * c.P : 2 * c.P;
+    c.mask_stride = packed ? 3 * c.P : c.P;
     if (!(alpha == alpha) || alpha - alpha != 0.0f) return DCN_ERR_INVALID_ARG;   // NaN or Inf
     c.Ho = dcn_core_out_size(H, K, stride, pad, dil);
     c.Wo = dcn_core_out_size(W, K, stride, pad, dil);
     if (c.Ho <= 0 || c.Wo <= 0) return DCN_ERR_INVALID_ARG;
     if (K > 16) return DCN_ERR_UNSUPPORTED;
     const int64_t C = (int64_t)G * Cg;
-    const int64_t P = (int64_t)K * K;
     if (C >= (1ll << 31)) return DCN_ERR_UNSUPPORTED;
     const int64_t in_img = (int64_t)H * W * C, out_img = (int64_t)c.Ho * c.Wo * C;
-    const int64_t off_img = (int64_t)c.Ho * c.Wo * G * P * 2;
+    const int64_t off_img = (int64_t)c.Ho * c.Wo * G * c.off_stride;
     if (in_img * c.ebytes > kMaxImageBytes || out_img >= (1ll << 31) || off_img >= (1ll << 31))
         return DCN_ERR_UNSUPPORTED;
     return DCN_OK;
@@ -74,8 +87,11 @@ Geometry make_geometry(const Call& c, int cpl)
 {
     Geometry g{};
     g.H = c.H; g.W = c.W; g.C = c.G * c.Cg; g.groups = c.G; g.Ho = c.Ho; g.Wo = c.Wo;
-    g.K = c.K; g.P = c.K * c.K; g.stride = c.stride; g.pad = c.pad; g.dil = c.dil;
+    g.K = c.K; g.P = c.P; g.stride = c.stride; g.pad = c.pad; g.dil = c.dil;
     g.c0 = c.dil * (c.K - 1) / 2;
+    g.rc = c.rc;
+    g.off_stride = c.off_stride;
+    g.mask_stride = c.mask_stride;
     g.alpha = c.alpha;
     g.softmax = c.softmax;
     g.in_row_bytes = (uint32_t)(g.C * c.ebytes);
@@ -103,7 +119,7 @@ int forward_variant(const FwdArgs& base, const Call& c, hipStream_t st)
     a.geo = make_geometry(c, CPL);
     const uint64_t blocks = (uint64_t)c.N * a.geo.blocks_per_image;
     if (blocks >= (1ull << 31)) return DCN_ERR_UNSUPPORTED;
-    if (c.K == 3)
+    if (c.k3())
         hipLaunchKernelGGL((dcn_forward_kernel<T, LB, NL, 3>), dim3((uint32_t)blocks), dim3(kBlock), 0, st, a);
     else
         hipLaunchKernelGGL((dcn_forward_kernel<T, LB, NL, 0>), dim3((uint32_t)blocks), dim3(kBlock), 0, st, a);
@@ -141,8 +157,9 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan, 
     if (!(rowg == 32 || rowg == 64 || rowg == 128) || rowc % 128 != 0) return false;
     if (!aligned(in, 16) || !aligned(out, 16)) return false;
     if (c.stride > 4 || c.K * c.K > kMaxTiledTaps) return false;
-    const int64_t off_img = (int64_t)c.Ho * c.Wo * c.G * c.K * c.K * 2 * eb;
-    if (off_img >= (1ll << 31)) return false;
+    const int64_t off_img = (int64_t)c.Ho * c.Wo * c.G * c.off_stride * eb;
+    const int64_t mask_img = (int64_t)c.Ho * c.Wo * c.G * c.mask_stride * eb;
+    if (off_img >= (1ll << 31) || mask_img >= (1ll << 31)) return false;
     const float a = c.alpha < 0 ? -c.alpha : c.alpha;
     const int c0 = c.dil * (c.K - 1) / 2;
     const int span = c0 > c.dil * (c.K - 1) - c0 ? c0 : c.dil * (c.K - 1) - c0;
@@ -192,11 +209,13 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan, 
     while ((32 << gs) < rowg) ++gs;
     plan.tg.gshift = gs;
     plan.tg.off_image_bytes = (uint32_t)off_img;
-    plan.tg.mask_image_bytes = (uint32_t)(off_img / 2);
-    for (int i = 0; i < c.K; ++i)
+    plan.tg.mask_image_bytes = (uint32_t)mask_img;
+    for (int i = 0, q = 0; i < c.K; ++i)
         for (int j = 0; j < c.K; ++j) {
-            plan.tg.tap_x[i * c.K + j] = (float)(i * c.dil - c0);
-            plan.tg.tap_y[i * c.K + j] = (float)(j * c.dil - c0);
+            if (c.rc && i * c.K + j == (c.K * c.K - 1) / 2) continue;   // the left-out centre
+            plan.tg.tap_x[q] = (float)(i * c.dil - c0);
+            plan.tg.tap_y[q] = (float)(j * c.dil - c0);
+            ++q;
         }
     return true;
 }
@@ -216,7 +235,7 @@ int launch_tiled(const FwdArgs& a, const TilePlan& pl, hipStream_t st)
 template <typename T, int NT, bool SM>
 int forward_tiled_k(const FwdArgs& a, const Call& c, const TilePlan& pl, hipStream_t st)
 {
-    return c.K == 3 ? launch_tiled<T, 3, NT, SM>(a, pl, st) : launch_tiled<T, 0, NT, SM>(a, pl, st);
+    return c.k3() ? launch_tiled<T, 3, NT, SM>(a, pl, st) : launch_tiled<T, 0, NT, SM>(a, pl, st);
 }
 
 template <typename T>
@@ -319,10 +338,11 @@ bool plan_owner(const Call& c, const void* gout, const void* gin, OwnerPlan& pl)
             }
     }
     if (best < 0 || pl.blocks >= (1ull << 31)) return false;
-    const int64_t off_img = (int64_t)c.Ho * c.Wo * c.G * c.K * c.K * 2 * c.ebytes;
-    if (off_img >= (1ll << 31)) return false;
+    const int64_t off_img = (int64_t)c.Ho * c.Wo * c.G * c.off_stride * c.ebytes;
+    const int64_t mask_img = (int64_t)c.Ho * c.Wo * c.G * c.mask_stride * c.ebytes;
+    if (off_img >= (1ll << 31) || mask_img >= (1ll << 31)) return false;
     pl.og.off_image_bytes = (uint32_t)off_img;
-    pl.og.mask_image_bytes = (uint32_t)(off_img / 2);
+    pl.og.mask_image_bytes = (uint32_t)mask_img;
     return true;
 }
 
@@ -363,8 +383,8 @@ int backward_grad_tiled(const BwdArgs& base, const Call& c, const TilePlan& pl, 
     BwdArgs a = base;
     a.geo = make_geometry(c, 32 / (int)sizeof(T));
     if (pl.threads == 512)
-        return c.K == 3 ? launch_grad_tiled<T, 3, 512>(a, c, pl, st) : launch_grad_tiled<T, 0, 512>(a, c, pl, st);
-    return c.K == 3 ? launch_grad_tiled<T, 3, 256>(a, c, pl, st) : launch_grad_tiled<T, 0, 256>(a, c, pl, st);
+        return c.k3() ? launch_grad_tiled<T, 3, 512>(a, c, pl, st) : launch_grad_tiled<T, 0, 512>(a, c, pl, st);
+    return c.k3() ? launch_grad_tiled<T, 3, 256>(a, c, pl, st) : launch_grad_tiled<T, 0, 256>(a, c, pl, st);
 }
 
 // Half precision: the owner kernel writes grad_input (binary32 sums rounded
@@ -380,7 +400,7 @@ int backward_half(BwdArgs a, const Call& c, hipStream_t st)
     if (!plan_owner(c, a.grad_out, a.grad_input, op) || !plan_tiles(c, a.input, a.grad_out, tp, 1, 160 * 1024))
         return DCN_ERR_UNSUPPORTED;
     a.geo = make_geometry(c, 8);
-    int rc = c.K == 3 ? launch_owner<T, 3>(a, op, st) : launch_owner<T, 0>(a, op, st);
+    int rc = c.k3() ? launch_owner<T, 3>(a, op, st) : launch_owner<T, 0>(a, op, st);
     if (rc != DCN_OK) return rc;
     a.near_m = op.og.M;
     return backward_grad_tiled<T>(a, c, tp, st);
@@ -393,7 +413,7 @@ int backward_variant(const BwdArgs& base, const Call& c, hipStream_t st)
     a.geo = make_geometry(c, LB / 4);
     const uint64_t blocks = (uint64_t)c.N * a.geo.blocks_per_image;
     if (blocks >= (1ll << 31)) return DCN_ERR_UNSUPPORTED;
-    if (c.K == 3)
+    if (c.k3())
         hipLaunchKernelGGL((dcn_backward_kernel<LB, L, 3>), dim3((uint32_t)blocks), dim3(kBlock), 0, st, a);
     else
         hipLaunchKernelGGL((dcn_backward_kernel<LB, L, 0>), dim3((uint32_t)blocks), dim3(kBlock), 0, st, a);
@@ -446,43 +466,72 @@ extern "C" int dcn_core_out_size(int in, int K, int stride, int pad, int dilatio
     return out < (1ll << 31) ? (int)out : 0;
 }
 
-extern "C" int dcn_core_forward(const void* input, const void* offset, const void* mask, void* output,
-                                int N, int H, int W, int G, int Cg, int K, int stride, int pad,
-                                int dilation, float offset_scale, int softmax_flag, int dtype,
-                                void* stream)
+namespace {
+
+// Flags of the _ex entry points -> validated call.
+int validate_ex(Call& c, int N, int H, int W, int G, int Cg, int K, int stride, int pad, int dil,
+                float alpha, int flags, int dtype)
 {
-    Call c;
-    int rc = validate(c, N, H, W, G, Cg, K, stride, pad, dilation, offset_scale, softmax_flag, dtype);
-    if (rc != DCN_OK) return rc;
-    if (N == 0) return DCN_OK;
-    if (!input || !offset || !mask || !output) return DCN_ERR_INVALID_ARG;
-    if (!aligned(offset, 2 * c.ebytes) || !aligned(mask, c.ebytes)) return DCN_ERR_INVALID_ARG;
+    if (flags & ~(DCN_FLAG_SOFTMAX | DCN_FLAG_REMOVE_CENTER | DCN_FLAG_PACKED)) return DCN_ERR_INVALID_ARG;
+    return validate(c, N, H, W, G, Cg, K, stride, pad, dil, alpha, (flags & DCN_FLAG_SOFTMAX) ? 1 : 0, dtype,
+                    (flags & DCN_FLAG_REMOVE_CENTER) ? 1 : 0, (flags & DCN_FLAG_PACKED) ? 1 : 0);
+}
+
+// Pointer checks shared by both layouts.  A split offset record is a whole
+// number of (dx, dy) pairs, so its base needs pair alignment; a packed record
+// (3P values) only needs the tensor to start on a 4-byte boundary, the kernels
+// realign records that fall on 2-byte boundaries.  The mask of a packed call
+// is the record's tail, 2P elements in.
+int resolve_records(const Call& c, const void* offset, const void* mask, const void** offset_out,
+                    const void** mask_out)
+{
+    const uintptr_t eb = (uintptr_t)c.ebytes;
+    if (c.packed) {
+        if (mask || !aligned(offset, 4)) return DCN_ERR_INVALID_ARG;
+        *offset_out = offset;
+        *mask_out = (const char*)offset + (size_t)2 * c.P * c.ebytes;
+    } else {
+        if (!mask || !aligned(offset, 2 * eb) || !aligned(mask, eb)) return DCN_ERR_INVALID_ARG;
+        *offset_out = offset;
+        *mask_out = mask;
+    }
+    return DCN_OK;
+}
+
+int forward_call(const Call& c, const void* input, const void* offset, const void* mask, void* output,
+                 void* stream)
+{
+    if (c.N == 0) return DCN_OK;
+    if (!input || !offset || !output) return DCN_ERR_INVALID_ARG;
     FwdArgs a{};
-    a.input = input; a.offset = offset; a.mask = mask; a.output = output;
+    const int rc = resolve_records(c, offset, mask, &a.offset, &a.mask);
+    if (rc != DCN_OK) return rc;
+    a.input = input; a.output = output;
     hipStream_t st = (hipStream_t)stream;
-    switch (dtype) {
+    switch (c.dtype) {
     case DCN_F32: return forward_typed<float>(a, c, st);
     case DCN_F16: return forward_typed<_Float16>(a, c, st);
     default: return forward_typed<__bf16>(a, c, st);
     }
 }
 
-extern "C" int dcn_core_backward(const void* input, const void* offset, const void* mask,
-                                 const void* grad_output, void* grad_input, void* grad_offset,
-                                 void* grad_mask, int N, int H, int W, int G, int Cg, int K, int stride,
-                                 int pad, int dilation, float offset_scale, int softmax_flag, int dtype,
-                                 void* stream)
+int backward_call(const Call& c, const void* input, const void* offset_in, const void* mask_in,
+                  const void* grad_output, void* grad_input, void* grad_offset_in, void* grad_mask_in,
+                  void* stream)
 {
-    Call c;
-    int rc = validate(c, N, H, W, G, Cg, K, stride, pad, dilation, offset_scale, softmax_flag, dtype);
-    if (rc != DCN_OK) return rc;
+    const int N = c.N, H = c.H, W = c.W, G = c.G, Cg = c.Cg;
     if (N == 0) return DCN_OK;
-    if (!input || !offset || !mask || !grad_output || !grad_input || !grad_offset || !grad_mask)
-        return DCN_ERR_INVALID_ARG;
+    if (!input || !offset_in || !grad_output || !grad_input || !grad_offset_in) return DCN_ERR_INVALID_ARG;
+    const void *offset, *mask, *grad_offset_c, *grad_mask_c;
+    int rc = resolve_records(c, offset_in, mask_in, &offset, &mask);
+    if (rc != DCN_OK) return rc;
+    rc = resolve_records(c, grad_offset_in, grad_mask_in, &grad_offset_c, &grad_mask_c);
+    if (rc != DCN_OK) return rc;
+    void* grad_offset = const_cast<void*>(grad_offset_c);
+    void* grad_mask = const_cast<void*>(grad_mask_c);
     const uintptr_t eb = (uintptr_t)c.ebytes;
-    if (!aligned(input, eb) || !aligned(grad_output, eb) || !aligned(grad_input, eb) || !aligned(offset, 2 * eb) ||
-        !aligned(grad_offset, 2 * eb) || !aligned(mask, eb) || !aligned(grad_mask, eb))
-        return DCN_ERR_INVALID_ARG;
+    if (!aligned(input, eb) || !aligned(grad_output, eb) || !aligned(grad_input, eb)) return DCN_ERR_INVALID_ARG;
+    const int dtype = c.dtype;
     if (dtype != DCN_F32) {
         BwdArgs a{};
         a.input = input; a.offset = offset; a.mask = mask; a.grad_out = grad_output;
@@ -509,7 +558,7 @@ extern "C" int dcn_core_backward(const void* input, const void* offset, const vo
         // owners write every element of grad_input; the gradient kernel
         // then adds the corners that are not near with atomics
         a.geo = make_geometry(c, 8);
-        rc = c.K == 3 ? launch_owner<float, 3>(a, op, st) : launch_owner<float, 0>(a, op, st);
+        rc = c.k3() ? launch_owner<float, 3>(a, op, st) : launch_owner<float, 0>(a, op, st);
         a.near_m = op.og.M;
     } else {
         rc = zero_fill((float*)grad_input, (int64_t)N * H * W * G * Cg, st);
@@ -518,6 +567,54 @@ extern "C" int dcn_core_backward(const void* input, const void* offset, const vo
     TilePlan tp;
     if (DCN_USE_GRAD_TILES && plan_tiles(c, input, grad_output, tp)) return backward_grad_tiled<float>(a, c, tp, st);
     return LB == 16 ? backward_lanes<16>(a, c, st, L) : backward_lanes<4>(a, c, st, L);
+}
+}  // namespace
+
+extern "C" int dcn_core_forward_ex(const void* input, const void* offset, const void* mask, void* output,
+                                   int N, int H, int W, int G, int Cg, int K, int stride, int pad,
+                                   int dilation, float offset_scale, int flags, int dtype, void* stream)
+{
+    Call c;
+    const int rc = validate_ex(c, N, H, W, G, Cg, K, stride, pad, dilation, offset_scale, flags, dtype);
+    if (rc != DCN_OK) return rc;
+    return forward_call(c, input, offset, mask, output, stream);
+}
+
+extern "C" int dcn_core_forward(const void* input, const void* offset, const void* mask, void* output,
+                                int N, int H, int W, int G, int Cg, int K, int stride, int pad,
+                                int dilation, float offset_scale, int softmax_flag, int dtype,
+                                void* stream)
+{
+    Call c;
+    const int rc = validate(c, N, H, W, G, Cg, K, stride, pad, dilation, offset_scale, softmax_flag, dtype);
+    if (rc != DCN_OK) return rc;
+    if (N > 0 && !mask) return DCN_ERR_INVALID_ARG;
+    return forward_call(c, input, offset, mask, output, stream);
+}
+
+extern "C" int dcn_core_backward_ex(const void* input, const void* offset, const void* mask,
+                                    const void* grad_output, void* grad_input, void* grad_offset,
+                                    void* grad_mask, int N, int H, int W, int G, int Cg, int K, int stride,
+                                    int pad, int dilation, float offset_scale, int flags, int dtype,
+                                    void* stream)
+{
+    Call c;
+    const int rc = validate_ex(c, N, H, W, G, Cg, K, stride, pad, dilation, offset_scale, flags, dtype);
+    if (rc != DCN_OK) return rc;
+    return backward_call(c, input, offset, mask, grad_output, grad_input, grad_offset, grad_mask, stream);
+}
+
+extern "C" int dcn_core_backward(const void* input, const void* offset, const void* mask,
+                                 const void* grad_output, void* grad_input, void* grad_offset,
+                                 void* grad_mask, int N, int H, int W, int G, int Cg, int K, int stride,
+                                 int pad, int dilation, float offset_scale, int softmax_flag, int dtype,
+                                 void* stream)
+{
+    Call c;
+    const int rc = validate(c, N, H, W, G, Cg, K, stride, pad, dilation, offset_scale, softmax_flag, dtype);
+    if (rc != DCN_OK) return rc;
+    if (N > 0 && (!mask || !grad_mask)) return DCN_ERR_INVALID_ARG;
+    return backward_call(c, input, offset, mask, grad_output, grad_input, grad_offset, grad_mask, stream);
 }
 
 extern "C" const char* dcn_status_string(int status)

@@ -86,14 +86,29 @@ __device__ __forceinline__ float ld1(const T* p)
     else return Elem<T>::widen(*(const uint16_t*)p);
 }
 
-// Two consecutive elements (an offset pair; 2*sizeof(T)-aligned).
+// Two consecutive elements (an offset pair).  A half-precision pair is read
+// as two 16-bit loads: in the packed offset+mask record (3P elements per
+// record) an odd P puts every other record on a 2-byte boundary.
 template <typename T>
 __device__ __forceinline__ float2 ld2(const T* p)
 {
     if constexpr (sizeof(T) == 4) return *(const float2*)p;
     else {
-        const uint32_t u = *(const uint32_t*)p;
-        return make_float2(Elem<T>::widen(u & 0xffffu), Elem<T>::widen(u >> 16));
+        const uint16_t* h = (const uint16_t*)p;
+        return make_float2(Elem<T>::widen(h[0]), Elem<T>::widen(h[1]));
+    }
+}
+
+// Store an offset pair (the gradient of (dx, dy)); same alignment rule as ld2.
+template <typename T>
+__device__ __forceinline__ void store_pair(T* p, float x, float y)
+{
+    if constexpr (sizeof(T) == 4) {
+        *(float2*)p = make_float2(x, y);
+    } else {
+        uint16_t* h = (uint16_t*)p;
+        h[0] = (uint16_t)Elem<T>::narrow(x);
+        h[1] = (uint16_t)Elem<T>::narrow(y);
     }
 }
 
@@ -154,6 +169,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t image_rsrc(const void* base, u
                                              0x00020000);
 }
 
+// Buffer resource over one image of offset records, based on the dword
+// boundary at or below the image start; lead (0 or 2) is the byte distance
+// from that boundary to the image.  A packed half-precision record of odd P
+// can start an image on a 2-byte boundary, and load_record's realignment
+// needs byte offsets that are true to the address's alignment.  Reading back
+// to the boundary stays inside the word that holds the image's first byte.
+struct RecordRsrc {
+    __amdgpu_buffer_rsrc_t r;
+    uint32_t lead;
+};
+
+__device__ __forceinline__ RecordRsrc record_rsrc(const void* img, uint32_t bytes)
+{
+    const uint32_t lead = (uint32_t)(uintptr_t)img & 3u;
+    return RecordRsrc{image_rsrc((const char*)img - lead, bytes + lead), lead};
+}
+
 // The hardware hands workgroup b to XCD (b mod 8).  Renumber so each XCD gets
 // one contiguous range of logical tiles: neighbouring tiles, which sample
 // overlapping input rows, then share that XCD's L2.
@@ -165,6 +197,8 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb)
 
 struct Geometry {
     int H, W, C, groups, Ho, Wo, K, P, stride, pad, dil, c0;
+    int rc;                       // 1: the centre tap is left out (P = K*K - 1)
+    int off_stride, mask_stride;  // elements per (pixel, group) record of offset / mask
     float alpha;
     int softmax;
     uint32_t in_image_bytes;      // H*W*C*b
@@ -176,6 +210,15 @@ struct Geometry {
     FastDiv lanes_per_group;      // L = Cg/CPL
     FastDiv wo_div;               // Wo
 };
+
+// Index among the P points of tap (i, j) (p = i*K + j, with the centre
+// left out under remove_center), or -1 for the left-out tap.
+__device__ __forceinline__ int point_of(const Geometry& G, int i, int j)
+{
+    const int p = i * G.K + j, centre = (G.K * G.K - 1) >> 1;
+    if (!G.rc) return p;
+    return p == centre ? -1 : p - (p > centre ? 1 : 0);
+}
 
 struct FwdArgs {
     const void* input;
@@ -277,8 +320,8 @@ __global__ __launch_bounds__(kBlock) void dcn_forward_kernel(FwdArgs a)
     const uint32_t chan_bytes = lw.cc * (CPL * Elem<T>::bytes);
     const size_t pix_global = (size_t)lw.n * G.Ho * G.Wo + lw.pix;
     const size_t pg = pix_global * G.groups + lw.g;
-    const T* off = (const T*)a.offset + pg * G.P * 2;
-    const T* mk = (const T*)a.mask + pg * G.P;
+    const T* off = (const T*)a.offset + pg * G.off_stride;
+    const T* mk = (const T*)a.mask + pg * G.mask_stride;
     const float bx = (float)((int)lw.wo * G.stride - G.pad + G.c0);
     const float by = (float)((int)lw.ho * G.stride - G.pad + G.c0);
 
@@ -337,7 +380,8 @@ __global__ __launch_bounds__(kBlock) void dcn_forward_kernel(FwdArgs a)
         }
         for (int i = 0; i < G.K; ++i)
             for (int j = 0; j < G.K; ++j) {
-                const int p = i * G.K + j;
+                const int p = point_of(G, i, j);
+                if (p < 0) continue;
                 float m = ld1(mk + p);
                 if (G.softmax) m = __expf(m - mx) * inv;
                 point(i, j, m, ld2(off + 2 * p));
@@ -413,14 +457,21 @@ __device__ __forceinline__ bool ordered(float x, float y)
 // types) so a prefetch of all points stays small; widen_* converts later.
 template <typename T> struct RawPair { uint32_t v[Elem<T>::bytes == 4 ? 2 : 1]; };
 
+// odd: the records may start on a 2-byte boundary (half precision, packed
+// record of odd P); the pair is then read as two 16-bit halves.  The flag is
+// the same for every lane of the launch.
 template <typename T>
-__device__ __forceinline__ RawPair<T> load_offset_raw(__amdgpu_buffer_rsrc_t r, uint32_t voff, int q)
+__device__ __forceinline__ RawPair<T> load_offset_raw(__amdgpu_buffer_rsrc_t r, uint32_t voff, int q, bool odd)
 {
     RawPair<T> rp;
     if constexpr (Elem<T>::bytes == 4) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, q * 8, 0);
         rp.v[0] = v[0];
         rp.v[1] = v[1];
+    } else if (odd) {
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, voff, q * 4, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, voff, q * 4 + 2, 0);
+        rp.v[0] = lo | (hi << 16);
     } else {
         rp.v[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, q * 4, 0);
     }
@@ -453,17 +504,37 @@ struct PointRecord {
 
 template <typename T, int PK>
 __device__ __forceinline__ void load_record(PointRecord<T, PK>& rec, __amdgpu_buffer_rsrc_t roff, uint32_t voff,
-                                            __amdgpu_buffer_rsrc_t rmk, uint32_t vmk)
+                                            __amdgpu_buffer_rsrc_t rmk, uint32_t vmk, bool odd)
 {
     constexpr int ND = PK * 2 * Elem<T>::bytes / 4;      // offset dwords
-    int i = 0;
+    if (Elem<T>::bytes == 2 && odd) {
+        // half-precision records that may start on a 2-byte boundary (packed
+        // record, odd P): read ND + 1 dwords from the dword boundary at or
+        // below the record and shift each dword pair down by the misalignment.
+        // The extra dword is the record's first mask value when the record is
+        // dword aligned, and lies inside the record otherwise.
+        const uint32_t base = voff & ~3u, sh = (voff & 2u) * 8u;
+        uint32_t d[ND + 1];
+        int i = 0;
 #pragma unroll
-    for (; i + 4 <= ND; i += 4) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(roff, voff, i * 4, 0);
-        rec.off[i] = v[0]; rec.off[i + 1] = v[1]; rec.off[i + 2] = v[2]; rec.off[i + 3] = v[3];
+        for (; i + 4 <= ND + 1; i += 4) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(roff, base, i * 4, 0);
+            d[i] = v[0]; d[i + 1] = v[1]; d[i + 2] = v[2]; d[i + 3] = v[3];
+        }
+#pragma unroll
+        for (; i < ND + 1; ++i) d[i] = __builtin_amdgcn_raw_buffer_load_b32(roff, base, i * 4, 0);
+#pragma unroll
+        for (int k = 0; k < ND; ++k) rec.off[k] = __builtin_amdgcn_alignbit(d[k + 1], d[k], sh);
+    } else {
+        int i = 0;
+#pragma unroll
+        for (; i + 4 <= ND; i += 4) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(roff, voff, i * 4, 0);
+            rec.off[i] = v[0]; rec.off[i + 1] = v[1]; rec.off[i + 2] = v[2]; rec.off[i + 3] = v[3];
+        }
+#pragma unroll
+        for (; i < ND; ++i) rec.off[i] = __builtin_amdgcn_raw_buffer_load_b32(roff, voff, i * 4, 0);
     }
-#pragma unroll
-    for (; i < ND; ++i) rec.off[i] = __builtin_amdgcn_raw_buffer_load_b32(roff, voff, i * 4, 0);
     if constexpr (Elem<T>::bytes == 4) {
         int j = 0;
 #pragma unroll
@@ -493,8 +564,10 @@ __device__ __forceinline__ float2 load_offset_pair(__amdgpu_buffer_rsrc_t r, uin
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, q * 8, 0);
         return make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
     } else {
-        const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(r, voff, q * 4, 0);
-        return make_float2(Elem<T>::widen(u & 0xffffu), Elem<T>::widen(u >> 16));
+        // two 16-bit reads: the record may start on a 2-byte boundary (ld2)
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, voff, q * 4, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, voff, q * 4 + 2, 0);
+        return make_float2(Elem<T>::widen(lo), Elem<T>::widen(hi));
     }
 }
 
@@ -751,12 +824,14 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
     const uint32_t pg_img = active ? ((uint32_t)ho * (uint32_t)G.Wo + (uint32_t)wo) * (uint32_t)G.groups + g : 0u;
     const __amdgpu_buffer_rsrc_t rin =
         image_rsrc((const char*)a.input + (size_t)cur.n * G.in_image_bytes, G.in_image_bytes);
-    const __amdgpu_buffer_rsrc_t roff =
-        image_rsrc((const char*)a.offset + (size_t)cur.n * tg.off_image_bytes, tg.off_image_bytes);
+    const RecordRsrc ro =
+        record_rsrc((const char*)a.offset + (size_t)cur.n * tg.off_image_bytes, tg.off_image_bytes);
+    const __amdgpu_buffer_rsrc_t roff = ro.r;
     const __amdgpu_buffer_rsrc_t rmk =
         image_rsrc((const char*)a.mask + (size_t)cur.n * tg.mask_image_bytes, tg.mask_image_bytes);
-    const uint32_t voff = pg_img * (uint32_t)(P * 2 * EB);
-    const uint32_t vmk = pg_img * (uint32_t)(P * EB);
+    const uint32_t voff = pg_img * (uint32_t)(G.off_stride * EB) + ro.lead;
+    const bool odd = EB == 2 && (G.off_stride & 1);   // records on 2-byte boundaries
+    const uint32_t vmk = pg_img * (uint32_t)(G.mask_stride * EB);
     L.bx = (float)(wo * G.stride - G.pad + G.c0);
     L.by = (float)(ho * G.stride - G.pad + G.c0);
     L.x_lo = cur.x_lo;
@@ -778,7 +853,7 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
         // and the points are unrolled so the record stays in registers.
         constexpr int PK = KT * KT;
         PointRecord<T, PK> rec;
-        load_record<T, PK>(rec, roff, voff, rmk, vmk);
+        load_record<T, PK>(rec, roff, voff, rmk, vmk, odd);
         __builtin_amdgcn_s_waitcnt(0);   // the region (and the record) have landed
         __syncthreads();
         float mx = 0.f, inv = 1.f;
@@ -836,22 +911,22 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
         // out of registers.
         RawPair<T> dA, dB;
         uint32_t mA = 0u, mB = 0u;
-        dA = load_offset_raw<T>(roff, voff, 0);
+        dA = load_offset_raw<T>(roff, voff, 0, odd);
         mA = load_mask_raw<T>(rmk, vmk, 0);
-        if (P > 1) { dB = load_offset_raw<T>(roff, voff, 1); mB = load_mask_raw<T>(rmk, vmk, 1); }
+        if (P > 1) { dB = load_offset_raw<T>(roff, voff, 1, odd); mB = load_mask_raw<T>(rmk, vmk, 1); }
         TiledPoint ptA, ptB;
         if (active) ptA = fetch(0, dA, mA);
-        if (P > 2) { dA = load_offset_raw<T>(roff, voff, 2); mA = load_mask_raw<T>(rmk, vmk, 2); }
+        if (P > 2) { dA = load_offset_raw<T>(roff, voff, 2, odd); mA = load_mask_raw<T>(rmk, vmk, 2); }
         int q = 0;
         DCN_UNROLL(1)
         for (; q + 1 < P; q += 2) {
             // here: ptA = point q (reads issued), dB = point q+1, dA = point q+2
             if (active) ptB = fetch(q + 1, dB, mB);
-            if (q + 3 < P) { dB = load_offset_raw<T>(roff, voff, q + 3); mB = load_mask_raw<T>(rmk, vmk, q + 3); }
+            if (q + 3 < P) { dB = load_offset_raw<T>(roff, voff, q + 3, odd); mB = load_mask_raw<T>(rmk, vmk, q + 3); }
             if (active) tiled_accumulate<T, CPL>(ptA, acc);
             if (q + 2 < P) {
                 if (active) ptA = fetch(q + 2, dA, mA);
-                if (q + 4 < P) { dA = load_offset_raw<T>(roff, voff, q + 4); mA = load_mask_raw<T>(rmk, vmk, q + 4); }
+                if (q + 4 < P) { dA = load_offset_raw<T>(roff, voff, q + 4, odd); mA = load_mask_raw<T>(rmk, vmk, q + 4); }
             }
             if (active) tiled_accumulate<T, CPL>(ptB, acc);
         }
@@ -901,10 +976,10 @@ __global__ __launch_bounds__(kBlock) void dcn_backward_kernel(BwdArgs a)
     const uint32_t chan_bytes = lw.cc * (CPL * 4);
     const size_t pix_global = (size_t)lw.n * G.Ho * G.Wo + lw.pix;
     const size_t pg = pix_global * G.groups + lw.g;
-    const float* off = (const float*)a.offset + pg * G.P * 2;
-    const float* mk = (const float*)a.mask + pg * G.P;
-    float* goff = (float*)a.grad_offset + pg * G.P * 2;
-    float* gmk = (float*)a.grad_mask + pg * G.P;
+    const float* off = (const float*)a.offset + pg * G.off_stride;
+    const float* mk = (const float*)a.mask + pg * G.mask_stride;
+    float* goff = (float*)a.grad_offset + pg * G.off_stride;
+    float* gmk = (float*)a.grad_mask + pg * G.mask_stride;
     char* gin = (char*)a.grad_input + (size_t)lw.n * G.in_image_bytes;
     const int bxi = (int)lw.wo * G.stride - G.pad + G.c0;
     const int byi = (int)lw.ho * G.stride - G.pad + G.c0;
@@ -931,7 +1006,8 @@ __global__ __launch_bounds__(kBlock) void dcn_backward_kernel(BwdArgs a)
     const int K = KT > 0 ? KT : G.K;
     for (int i = 0; i < K; ++i)
         for (int j = 0; j < K; ++j) {
-            const int p = i * K + j;
+            const int p = point_of(G, i, j);
+            if (p < 0) continue;                                // (the same for every lane)
             float m = 0.f;
             float2 d = make_float2(__builtin_nanf(""), 0.f);   // inactive: never on the map
             if (act) {
@@ -1099,12 +1175,14 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
     const uint32_t pg_img = active ? ((uint32_t)ho * (uint32_t)G.Wo + (uint32_t)wo) * (uint32_t)G.groups + g : 0u;
     const __amdgpu_buffer_rsrc_t rin =
         image_rsrc((const char*)a.input + (size_t)cur.n * G.in_image_bytes, G.in_image_bytes);
-    const __amdgpu_buffer_rsrc_t roff =
-        image_rsrc((const char*)a.offset + (size_t)cur.n * tg.off_image_bytes, tg.off_image_bytes);
+    const RecordRsrc ro =
+        record_rsrc((const char*)a.offset + (size_t)cur.n * tg.off_image_bytes, tg.off_image_bytes);
+    const __amdgpu_buffer_rsrc_t roff = ro.r;
     const __amdgpu_buffer_rsrc_t rmk =
         image_rsrc((const char*)a.mask + (size_t)cur.n * tg.mask_image_bytes, tg.mask_image_bytes);
-    const uint32_t voff = pg_img * (uint32_t)(P * 2 * EB);
-    const uint32_t vmk = pg_img * (uint32_t)(P * EB);
+    const uint32_t voff = pg_img * (uint32_t)(G.off_stride * EB) + ro.lead;
+    const bool odd = EB == 2 && (G.off_stride & 1);   // records on 2-byte boundaries
+    const uint32_t vmk = pg_img * (uint32_t)(G.mask_stride * EB);
     const int bxi = wo * G.stride - G.pad + G.c0, byi = ho * G.stride - G.pad + G.c0;
     L.bx = (float)bxi;
     L.by = (float)byi;
@@ -1118,8 +1196,8 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
     float go[CPL];
     const size_t pix = ((size_t)cur.n * G.Ho + (size_t)ho) * G.Wo + wo;
     char* gin = (char*)a.grad_input + (size_t)cur.n * G.in_image_bytes;
-    T* goff = (T*)a.grad_offset + ((size_t)cur.n * G.Ho * G.Wo * G.groups + pg_img) * P * 2;
-    T* gmk = (T*)a.grad_mask + ((size_t)cur.n * G.Ho * G.Wo * G.groups + pg_img) * P;
+    T* goff = (T*)a.grad_offset + ((size_t)cur.n * G.Ho * G.Wo * G.groups + pg_img) * G.off_stride;
+    T* gmk = (T*)a.grad_mask + ((size_t)cur.n * G.Ho * G.Wo * G.groups + pg_img) * G.mask_stride;
     if (active) {
         const char* gp = (const char*)a.grad_out + pix * G.C * EB + cur.slab * 128u + (uint32_t)sub * 32u;
         const uint4 h0 = *(const uint4*)(gp + swp * 16), h1 = *(const uint4*)(gp + (swp ^ 1) * 16);
@@ -1142,7 +1220,7 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
     };
 
     PointRecord<T, (KT > 0 ? KT * KT : 1)> rec;
-    if constexpr (KT > 0) load_record<T, KT * KT>(rec, roff, voff, rmk, vmk);
+    if constexpr (KT > 0) load_record<T, KT * KT>(rec, roff, voff, rmk, vmk, odd);
     __builtin_amdgcn_s_waitcnt(0);     // region, upstream gradient and record have landed
     __syncthreads();
     const char* lds = (const char*)region;
@@ -1183,7 +1261,7 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
         if (!pt.inmap) { gm = 0.f; gdx = 0.f; gdy = 0.f; }
         if (active && leader) {
             const float gd[2] = {G.alpha * m * gdx, G.alpha * m * gdy};
-            store<T, 2 * EB>(goff + 2 * q, gd);
+            store_pair<T>(goff + 2 * q, gd[0], gd[1]);
         }
         // corners beyond the owners' reach
         if (active && pt.inmap) {
@@ -1393,8 +1471,9 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
     const int g = ch0 / og.Cg;
     const int K = KT > 0 ? KT : G.K;
     const uint32_t M2 = 2u * (uint32_t)og.M;
-    const __amdgpu_buffer_rsrc_t roff =
-        image_rsrc((const char*)a.offset + (size_t)n * og.off_image_bytes, og.off_image_bytes);
+    const RecordRsrc ro = record_rsrc((const char*)a.offset + (size_t)n * og.off_image_bytes, og.off_image_bytes);
+    const __amdgpu_buffer_rsrc_t roff = ro.r;
+    const bool odd = EB == 2 && (G.off_stride & 1);   // records on 2-byte boundaries
     const __amdgpu_buffer_rsrc_t rmk =
         image_rsrc((const char*)a.mask + (size_t)n * og.mask_image_bytes, og.mask_image_bytes);
 
@@ -1452,8 +1531,8 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
         }
         if constexpr (KT > 0) {
             const uint32_t pg_img = ((uint32_t)ho * (uint32_t)G.Wo + (uint32_t)wo) * (uint32_t)G.groups + (uint32_t)g;
-            load_record<T, KT * KT>(pd.rec, roff, pg_img * (uint32_t)(KT * KT * 2 * EB), rmk,
-                                    pg_img * (uint32_t)(KT * KT * EB));
+            load_record<T, KT * KT>(pd.rec, roff, pg_img * (uint32_t)(G.off_stride * EB) + ro.lead, rmk,
+                                    pg_img * (uint32_t)(G.mask_stride * EB), odd);
         }
     };
     auto mval = [&](uint32_t raw) {
@@ -1498,8 +1577,8 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
                 }
         } else {
             const size_t pg = (((size_t)n * G.Ho + ho) * G.Wo + wo) * G.groups + g;
-            const T* off = (const T*)a.offset + pg * G.P * 2;
-            const T* mk = (const T*)a.mask + pg * G.P;
+            const T* off = (const T*)a.offset + pg * G.off_stride;
+            const T* mk = (const T*)a.mask + pg * G.mask_stride;
             float mx = 0.f, inv = 1.f;
             if (G.softmax) {
                 mx = ld1(mk);
@@ -1510,7 +1589,8 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
             }
             for (int i = 0; i < K; ++i)
                 for (int j = 0; j < K; ++j) {
-                    const int q = i * K + j;
+                    const int q = point_of(G, i, j);
+                    if (q < 0) continue;
                     float m = ld1(mk + q);
                     if (G.softmax) m = __expf(m - mx) * inv;
                     point(i, j, bxi, byi, ld2(off + 2 * q), m, go);

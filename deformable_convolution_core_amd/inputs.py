@@ -52,6 +52,7 @@ class Workload:
     mask_sigma: float = 0.3
     seed_base: int = 0
     backward: bool = False
+    remove_center: bool = False   # odd K: the centre tap is left out
 
     @property
     def C(self) -> int:
@@ -59,7 +60,7 @@ class Workload:
 
     @property
     def P(self) -> int:
-        return self.K * self.K
+        return self.K * self.K - (1 if self.remove_center else 0)
 
     @property
     def elem_bytes(self) -> int:
@@ -138,6 +139,22 @@ def make(w: Workload, with_grad: bool | None = None) -> dict:
     if with_grad or (with_grad is None and w.backward):
         t["grad_out"] = normal(s["output"], w.seed_base + T_GRAD_OUT, 1.0, w.dtype)
     return t
+
+
+def pack_offset_mask(offset: torch.Tensor, mask: torch.Tensor, G: int, P: int) -> torch.Tensor:
+    """DCNv4's single tensor (N, Ho, Wo, G*3P): per (pixel, group) the 2P
+    offset values followed by the P mask values.  A copy, no arithmetic."""
+    N, Ho, Wo = offset.shape[:3]
+    return torch.cat([offset.reshape(N, Ho, Wo, G, 2 * P), mask.reshape(N, Ho, Wo, G, P)],
+                     dim=-1).reshape(N, Ho, Wo, G * 3 * P).contiguous()
+
+
+def unpack_offset_mask(om: torch.Tensor, G: int, P: int):
+    """Inverse of pack_offset_mask: (offset (N,Ho,Wo,G*2P), mask (N,Ho,Wo,G*P))."""
+    N, Ho, Wo = om.shape[:3]
+    r = om.reshape(N, Ho, Wo, G, 3 * P)
+    return (r[..., :2 * P].reshape(N, Ho, Wo, G * 2 * P).contiguous(),
+            r[..., 2 * P:].reshape(N, Ho, Wo, G * P).contiguous())
 
 
 def scaled(w: Workload, **changes) -> Workload:

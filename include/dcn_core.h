@@ -119,6 +119,46 @@ int dcn_core_backward(const void* input, const void* offset, const void* mask,
                       int pad, int dilation, float offset_scale, int softmax_flag, int dtype,
                       void* stream);
 
+/* Options of the _ex entry points, OR-ed into `flags`. */
+enum dcn_flags {
+    /* softmax over each (pixel, group)'s points (DCNv3); absent: raw mask (DCNv4) */
+    DCN_FLAG_SOFTMAX = 1,
+    /* leave out the centre tap of an odd K: P = K*K - 1 points, the remaining
+     * taps keep their order p = i*K + j with the centre index skipped ([FB]
+     * section 4 step 3 subtracts remove_center from the point count; the
+     * DCNv4 module takes the same switch, [V4] programming-interface section).
+     * K must be odd and >= 3. */
+    DCN_FLAG_REMOVE_CENTER = 2,
+    /* DCNv4's single offset-and-weight tensor ([A100] section 1 passes one
+     * tensor carrying both to the DCNv4 core): `offset` is
+     * (N, Ho, Wo, G, 3P), each (pixel, group) record holding its 2P offsets
+     * as (dx, dy) pairs in point order, then its P mask values; `mask` (and
+     * grad_mask) must be NULL and grad_offset receives the gradient in the
+     * same record layout.  The record order is not printed on the pages; this
+     * is the layout the library defines.  The tensor must start on a 4-byte
+     * boundary. */
+    DCN_FLAG_PACKED = 4
+};
+
+/* dcn_core_forward with options: `flags` is an OR of dcn_flags (any other
+ * bit is DCN_ERR_INVALID_ARG); P = K*K, or K*K - 1 with
+ * DCN_FLAG_REMOVE_CENTER, in every tensor shape above.  Otherwise the same
+ * arguments, definition and errors as dcn_core_forward, which equals this
+ * call with flags = softmax_flag. */
+int dcn_core_forward_ex(const void* input, const void* offset, const void* mask, void* output,
+                        int N, int H, int W, int G, int Cg, int K, int stride, int pad,
+                        int dilation, float offset_scale, int flags, int dtype, void* stream);
+
+/* dcn_core_backward with options (flags as for dcn_core_forward_ex).  With
+ * DCN_FLAG_PACKED, offset and grad_offset are packed records and mask and
+ * grad_mask are NULL; the gradient of each mask value lands in its record's
+ * tail.  Same support limits and errors as dcn_core_backward. */
+int dcn_core_backward_ex(const void* input, const void* offset, const void* mask,
+                         const void* grad_output, void* grad_input, void* grad_offset,
+                         void* grad_mask, int N, int H, int W, int G, int Cg, int K, int stride,
+                         int pad, int dilation, float offset_scale, int flags, int dtype,
+                         void* stream);
+
 /* Static, human-readable name of a dcn_status value. */
 const char* dcn_status_string(int status);
 

@@ -100,6 +100,49 @@ def test_backward_validation():
     assert bwd(lib, Cg=3) == UNSUPPORTED
 
 
+def fwd_ex(lib, ptrs=(0x1000, 0x2000, 0x3000, 0x4000), N=1, H=8, W=8, G=2, Cg=8, K=3, s=1, p=1, d=1,
+           alpha=1.0, flags=0, dtype=0):
+    vp = [ctypes.c_void_p(x) if x else None for x in ptrs]
+    return lib.dcn_core_forward_ex(*vp, N, H, W, G, Cg, K, s, p, d, alpha, flags, dtype, None)
+
+
+def bwd_ex(lib, ptrs=(0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000), N=1, H=8, W=8, G=2, Cg=8,
+           K=3, s=1, p=1, d=1, alpha=1.0, flags=0, dtype=0):
+    vp = [ctypes.c_void_p(x) if x else None for x in ptrs]
+    return lib.dcn_core_backward_ex(*vp, N, H, W, G, Cg, K, s, p, d, alpha, flags, dtype, None)
+
+
+PACKED_PTRS = (0x1000, 0x2000, 0, 0x4000)
+INVALID_EX = [
+    dict(flags=8), dict(flags=-1), dict(flags=1 << 30),
+    dict(flags=2, K=4, p=1),                     # remove_center needs an odd K
+    dict(flags=2, K=2, p=0), dict(flags=2, K=1, p=0),
+    dict(flags=4),                               # packed with a separate mask pointer
+    dict(flags=4, ptrs=(0x1000, 0x2002, 0, 0x4000), dtype=1),   # packed tensor on a 2-byte boundary
+    dict(flags=4, ptrs=(0x1000, 0, 0, 0x4000)),  # packed without the tensor
+    dict(flags=0, ptrs=(0x1000, 0x2000, 0, 0x4000)),            # split layout without a mask
+    dict(flags=2, dtype=5), dict(flags=2, N=-1),
+]
+
+
+@pytest.mark.parametrize("kw", INVALID_EX)
+def test_forward_ex_rejects_invalid_arguments_on_host(kw):
+    assert fwd_ex(dcn.load_library(), **kw) == INVALID
+
+
+def test_forward_ex_empty_batch_and_old_entry_points():
+    lib = dcn.load_library()
+    assert fwd_ex(lib, N=0, flags=2 | 4, ptrs=(0, 0, 0, 0)) == OK
+    assert fwd_ex(lib, N=0, flags=0, ptrs=(0, 0, 0, 0)) == OK
+    # the entry points without flags keep their checks: no mask is invalid
+    assert fwd(lib, ptrs=(0x1000, 0x2000, 0, 0x4000)) == INVALID
+    assert bwd_ex(lib, flags=4) == INVALID                   # packed with separate mask pointers
+    assert bwd_ex(lib, flags=4, ptrs=(0x1000, 0x2000, 0, 0x4000, 0x5000, 0x6000, 0x7000)) == INVALID
+    assert bwd_ex(lib, flags=2, K=4) == INVALID
+    assert bwd_ex(lib, flags=16) == INVALID
+    assert bwd_ex(lib, flags=4, N=0, ptrs=(0,) * 7) == OK
+
+
 def test_status_strings():
     lib = dcn.load_library()
     for code, prefix in ((0, b"DCN_OK"), (1, b"DCN_ERR_INVALID_ARG"), (2, b"DCN_ERR_UNSUPPORTED"),

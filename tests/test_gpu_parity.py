@@ -32,14 +32,15 @@ def announce(request):
 
 def cfg_of(w):
     return dict(kernel_size=w.K, stride=w.stride, pad=w.pad, dilation=w.dilation,
-                offset_scale=w.offset_scale, softmax=w.softmax, group=w.G)
+                offset_scale=w.offset_scale, softmax=w.softmax, group=w.G,
+                remove_center=w.remove_center)
 
 
 def oracle_fwd(t, w):
     return oracle.forward(inputs.to_f64(t["input"]), inputs.to_f64(t["offset"]), inputs.to_f64(t["mask"]),
                           K=w.K, stride=w.stride, pad=w.pad, dilation=w.dilation,
                           offset_scale=w.offset_scale, softmax=w.softmax, group=w.G,
-                          coord_mode=oracle.COORD_BINARY32)
+                          coord_mode=oracle.COORD_BINARY32, remove_center=w.remove_center)
 
 
 def gpu_fwd(t, w):
@@ -304,7 +305,7 @@ def oracle_bwd(t, w):
                            inputs.to_f64(t["mask"]), inputs.to_f64(t["grad_out"]),
                            K=w.K, stride=w.stride, pad=w.pad, dilation=w.dilation,
                            offset_scale=w.offset_scale, softmax=w.softmax, group=w.G,
-                           coord_mode=oracle.COORD_BINARY32)
+                           coord_mode=oracle.COORD_BINARY32, remove_center=w.remove_center)
 
 
 def check_backward(w, far_roundings=1):
