@@ -8,9 +8,9 @@ accumulation, N=64, 56x56, C=64, G=4, K=3).  One step = one forward launch
 over the whole batch.  Beside it, in the same JSON line: the bf16 sweep over
 the four FlashInternImage-T stage shapes, the core op of a whole
 FlashInternImage-T forward (the stage shapes at their depths, 30 launches),
-the DCNv3 large-channel stage at stride 1 and 2, the fp32 forward +
-backward, the half-precision backward, and the CPU oracle timed on the host
-cores.
+the DCNv3 large-channel stage at stride 1 and 2, the DCNv4 stage-1 shapes
+with DCNv4's packed offset+mask tensor, the fp32 forward + backward, the
+half-precision backward, and the CPU oracle timed on the host cores.
 
 Inputs are seeded synthetic tensors (no dataset, no weights).  Timing uses
 R rotating copies of every tensor (R * bytes > 512 MB, twice the 256 MB
@@ -58,63 +58,64 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def cfg(w):
-    return dict(kernel_size=w.K, stride=w.stride, pad=w.pad, dilation=w.dilation,
-                offset_scale=w.offset_scale, softmax=w.softmax, group=w.G)
-
-
-def rotating_sets(w, backward=False):
-    """R device copies of the workload's tensors (+ outputs)."""
+def rotating_sets(w, backward=False, packed=False):
+    """R device copies of the workload's tensors (+ outputs).  packed: the
+    offsets and mask travel as DCNv4's single record tensor instead."""
     per = w.min_bytes_backward() if backward else w.min_bytes_forward()
     R = max(2, math.ceil(ROTATE_BYTES / per))
     host = inputs.make(w, with_grad=backward)
+    if packed:
+        host["offset"] = inputs.pack_offset_mask(host["offset"], host.pop("mask"), w.G, w.P)
     sets = []
     for _ in range(R):
         d = {k: v.to("cuda") for k, v in host.items()}
         if backward:
             d["gi"] = torch.empty_like(d["input"])
             d["goff"] = torch.empty_like(d["offset"])
-            d["gm"] = torch.empty_like(d["mask"])
+            d["gm"] = torch.empty_like(d["mask"]) if "mask" in d else None
         else:
             d["out"] = torch.empty(w.shapes()["output"], dtype=d["input"].dtype, device="cuda")
         sets.append(d)
     return sets
 
 
-def launcher(w, backward=False):
+def launcher(w, backward=False, packed=False):
+    """A function launching one forward (or backward) of w on a tensor set
+    through the C ABI (the _ex entry points, flags from the workload)."""
     lib = dcn.load_library()
-    c = cfg(w)
     dt = {"f32": 0, "f16": 1, "bf16": 2}[w.dtype]
+    flags = ((dcn.FLAG_SOFTMAX if w.softmax else 0) | (dcn.FLAG_REMOVE_CENTER if w.remove_center else 0)
+             | (dcn.FLAG_PACKED if packed else 0))
     import ctypes
     vp = ctypes.c_void_p
 
+    def ptr(t):
+        return None if t is None else vp(t.data_ptr())
+
     def fwd(d, stream):
-        rc = lib.dcn_core_forward(vp(d["input"].data_ptr()), vp(d["offset"].data_ptr()),
-                                  vp(d["mask"].data_ptr()), vp(d["out"].data_ptr()),
-                                  w.N, w.H, w.W, w.G, w.Cg, w.K, w.stride, w.pad, w.dilation,
-                                  float(w.offset_scale), int(w.softmax), dt, vp(stream))
+        rc = lib.dcn_core_forward_ex(ptr(d["input"]), ptr(d["offset"]), ptr(d.get("mask")), ptr(d["out"]),
+                                     w.N, w.H, w.W, w.G, w.Cg, w.K, w.stride, w.pad, w.dilation,
+                                     float(w.offset_scale), flags, dt, vp(stream))
         if rc:
             raise dcn.DCNError(rc, lib.dcn_status_string(rc).decode())
 
     def bwd(d, stream):
-        rc = lib.dcn_core_backward(vp(d["input"].data_ptr()), vp(d["offset"].data_ptr()),
-                                   vp(d["mask"].data_ptr()), vp(d["grad_out"].data_ptr()),
-                                   vp(d["gi"].data_ptr()), vp(d["goff"].data_ptr()),
-                                   vp(d["gm"].data_ptr()),
-                                   w.N, w.H, w.W, w.G, w.Cg, w.K, w.stride, w.pad, w.dilation,
-                                   float(w.offset_scale), int(w.softmax), dt, vp(stream))
+        rc = lib.dcn_core_backward_ex(ptr(d["input"]), ptr(d["offset"]), ptr(d.get("mask")),
+                                      ptr(d["grad_out"]), ptr(d["gi"]), ptr(d["goff"]), ptr(d["gm"]),
+                                      w.N, w.H, w.W, w.G, w.Cg, w.K, w.stride, w.pad, w.dilation,
+                                      float(w.offset_scale), flags, dt, vp(stream))
         if rc:
             raise dcn.DCNError(rc, lib.dcn_status_string(rc).decode())
 
     return bwd if backward else fwd
 
 
-def time_launches(w, steps, warmup, backward=False):
+def time_launches(w, steps, warmup, backward=False, packed=False):
     """Mean per-launch time (ms) of `steps` launches over rotating buffers:
     graph-replayed (primary) and eager."""
-    sets = rotating_sets(w, backward)
+    sets = rotating_sets(w, backward, packed)
     R = len(sets)
-    launch = launcher(w, backward)
+    launch = launcher(w, backward, packed)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         h = stream.cuda_stream
@@ -151,10 +152,11 @@ def time_launches(w, steps, warmup, backward=False):
     return graph_ms, eager_ms, R
 
 
-def forward_record(w, steps, warmup):
-    ms, eager_ms, R = time_launches(w, steps, warmup)
+def forward_record(w, steps, warmup, packed=False):
+    ms, eager_ms, R = time_launches(w, steps, warmup, packed=packed)
     gbps = w.min_bytes_forward() / (ms * 1e-3) / 1e9
     return dict(workload=w.name, dtype=w.dtype, softmax=bool(w.softmax),
+                layout="packed offset+mask" if packed else "separate offset and mask",
                 shape=dict(N=w.N, H=w.H, W=w.W, C=w.C, G=w.G, Cg=w.Cg, K=w.K, stride=w.stride,
                            Ho=w.Ho, Wo=w.Wo),
                 us=round(ms * 1e3, 3), eager_us=round(eager_ms * 1e3, 3),
@@ -327,6 +329,13 @@ def main():
             log(f"{name}: {r['us']} us, {r['GBps']} GB/s")
             others.append(r)
         extra["other_forward"] = others
+        # DCNv4's own tensor layout: offsets and mask in one record per (pixel, group)
+        packed = []
+        for name in (inputs.HEADLINE, "c3a_dcnv4_bf16_56"):
+            r = forward_record(inputs.WORKLOADS[name], args.steps, args.warmup, packed=True)
+            log(f"{name} packed: {r['us']} us, {r['GBps']} GB/s")
+            packed.append(r)
+        extra["packed_forward"] = packed
         w5 = inputs.WORKLOADS["c5_dcnv4_f32_56_fwdbwd"]
         bms, beager, R = time_launches(w5, max(20, args.steps // 4), min(args.warmup, 10), backward=True)
         extra["backward"] = dict(workload=w5.name, us=round(bms * 1e3, 3), eager_us=round(beager * 1e3, 3),
