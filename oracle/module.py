@@ -59,26 +59,30 @@ def sigmoid(z):
 
 
 def gate_forward(y, v, z, G):
-    """y * (1 - s) + v * s with s = sigmoid(z), z (..., G), y and v (..., G*Cg)."""
+    """y * (1 - s) + v * s with s = sigmoid(z), z (..., G), y and v (..., G*Cg).
+    1 - s is evaluated as sigmoid(-z), the same number without the
+    cancellation of 1 - s when s is close to 1."""
     sh = y.shape
     Cg = sh[-1] // G
     s = sigmoid(z)[..., None]
+    t = sigmoid(-z)[..., None]
     yg = y.reshape(*sh[:-1], G, Cg)
     vg = v.reshape(*sh[:-1], G, Cg)
-    return (yg * (1.0 - s) + vg * s).reshape(sh)
+    return (yg * t + vg * s).reshape(sh)
 
 
 def gate_backward(y, v, z, gout, G):
-    """Gradients (gy, gv, gz) of gate_forward."""
+    """Gradients (gy, gv, gz) of gate_forward (ds/dz = s * (1 - s))."""
     sh = y.shape
     Cg = sh[-1] // G
     s = sigmoid(z)[..., None]
+    t = sigmoid(-z)[..., None]
     yg = y.reshape(*sh[:-1], G, Cg)
     vg = v.reshape(*sh[:-1], G, Cg)
     go = gout.reshape(*sh[:-1], G, Cg)
-    gy = (go * (1.0 - s)).reshape(sh)
+    gy = (go * t).reshape(sh)
     gv = (go * s).reshape(sh)
-    gz = (go * (vg - yg)).sum(axis=-1) * (s[..., 0] * (1.0 - s[..., 0]))
+    gz = (go * (vg - yg)).sum(axis=-1) * (s[..., 0] * t[..., 0])
     return gy, gv, gz
 
 

@@ -33,7 +33,8 @@ def test_gate_closed_forms():
     v = rng.standard_normal((2, 3, 4, 12))
     G = 3
     big = np.full((2, 3, 4, G), 40.0)
-    np.testing.assert_array_equal(om_oracle.gate_forward(y, v, big, G), v)        # s rounds to 1
+    # s = 1 - 4.2e-18: the result is v to within one rounding
+    np.testing.assert_allclose(om_oracle.gate_forward(y, v, big, G), v, rtol=0, atol=1e-16)
     np.testing.assert_allclose(om_oracle.gate_forward(y, v, -big, G), y, rtol=0, atol=1e-16)
     np.testing.assert_allclose(om_oracle.gate_forward(y, v, np.zeros_like(big), G), (y + v) / 2,
                                rtol=1e-15, atol=0)

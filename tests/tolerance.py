@@ -31,19 +31,21 @@ ATOL = {"f32": 0.0, "f16": 2.0 ** -24, "bf16": 0.0}
 U_STORE = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
 
 
-def bound(ref, S, n_terms, dtype, slack=32, store_roundings=0):
+def bound(ref, S, n_terms, dtype, slack=32, store_roundings=0, atol=None):
     """store_roundings: how many times a partial sum of magnitude <= S may be
     rounded to the storage format besides the final rounding (half-precision
-    atomics add that many)."""
-    return (RTOL[dtype] * np.abs(ref) + (np.asarray(n_terms, np.float64) + slack) * U * S + ATOL[dtype]
-            + store_roundings * U_STORE[dtype] * S)
+    atomics add that many).  atol overrides the dtype's absolute floor (for
+    results that reach the subnormal range of binary32 or bfloat16, whose
+    spacing there is 2^-149 and 2^-133)."""
+    return (RTOL[dtype] * np.abs(ref) + (np.asarray(n_terms, np.float64) + slack) * U * S
+            + (ATOL[dtype] if atol is None else atol) + store_roundings * U_STORE[dtype] * S)
 
 
-def compare(gpu, ref, S, n_terms, dtype, slack=32, store_roundings=0):
+def compare(gpu, ref, S, n_terms, dtype, slack=32, store_roundings=0, atol=None):
     """Returns a dict of statistics; 'ok' is True when every element is within bound."""
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
-    b = bound(ref, S, n_terms, dtype, slack, store_roundings)
+    b = bound(ref, S, n_terms, dtype, slack, store_roundings, atol)
     err = np.abs(gpu - ref)
     finite = np.isfinite(gpu)
     ratio = np.where(b > 0, err / np.where(b > 0, b, 1.0), np.where(err > 0, np.inf, 0.0))
