@@ -27,7 +27,8 @@ import os
 import torch
 
 __all__ = ["forward", "backward", "forward_packed", "backward_packed", "out_size", "dcn_core",
-           "dcnv4_core", "DCNCoreFunction", "DCNv4CoreFunction", "DCNError", "library_path",
+           "dcnv4_core", "center_gate_forward", "center_gate_backward", "center_gate",
+           "DCNCoreFunction", "DCNv4CoreFunction", "CenterGateFunction", "DCNError", "library_path",
            "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +38,8 @@ _lib = None
 DCN_F32, DCN_F16, DCN_BF16 = 0, 1, 2
 _DTYPE = {torch.float32: DCN_F32, torch.float16: DCN_F16, torch.bfloat16: DCN_BF16}
 EXPORTED = ("dcn_core_out_size", "dcn_core_forward", "dcn_core_backward", "dcn_core_forward_ex",
-            "dcn_core_backward_ex", "dcn_status_string")
+            "dcn_core_backward_ex", "dcn_center_gate_forward", "dcn_center_gate_backward",
+            "dcn_status_string")
 FLAG_SOFTMAX, FLAG_REMOVE_CENTER, FLAG_PACKED = 1, 2, 4
 
 
@@ -71,6 +73,11 @@ def load_library(path: str | None = None):
     lib.dcn_core_forward_ex.restype = i
     lib.dcn_core_backward_ex.argtypes = [vp] * 7 + [i] * 9 + [f, i, i, vp]
     lib.dcn_core_backward_ex.restype = i
+    ll = ctypes.c_longlong
+    lib.dcn_center_gate_forward.argtypes = [vp] * 4 + [ll, i, i, i, vp]
+    lib.dcn_center_gate_forward.restype = i
+    lib.dcn_center_gate_backward.argtypes = [vp] * 7 + [ll, i, i, i, vp]
+    lib.dcn_center_gate_backward.restype = i
     lib.dcn_status_string.argtypes = [i]
     lib.dcn_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -218,6 +225,70 @@ def backward_packed(input, offset_mask, grad_output, *, kernel_size=3, stride=1,
     gi, gom, _ = _backward(input, offset_mask, None, grad_output, kernel_size, stride, pad, dilation,
                            offset_scale, softmax, group, remove_center)
     return gi, gom
+
+
+def _gate_check(y, v, z, group):
+    if y.dim() < 1 or y.shape[-1] % group:
+        raise ValueError("y's last axis must hold group * Cg channels")
+    if tuple(v.shape) != tuple(y.shape) or tuple(z.shape) != tuple(y.shape[:-1]) + (group,):
+        raise ValueError(f"v must be shaped like y and z like y[..., :{group}]")
+    for name, t in (("y", y), ("v", v), ("z", z)):
+        _check_tensor(name, t, y)
+    if y.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {y.dtype}")
+    M = y.numel() // y.shape[-1] if y.numel() else 0
+    return M, y.shape[-1] // group
+
+
+def center_gate_forward(y, v, z, *, group, out=None) -> torch.Tensor:
+    """y * (1 - s) + v * s with s = sigmoid(z) per (pixel, group), in HIP.
+    y, v: (..., G*Cg); z: (..., G).  out may be y or v."""
+    M, Cg = _gate_check(y, v, z, group)
+    if out is None:
+        out = torch.empty_like(y)
+    elif out.shape != y.shape or out.dtype != y.dtype or not out.is_contiguous() or out.device != y.device:
+        raise ValueError("out has the wrong shape, dtype, device or layout")
+    with torch.cuda.device(y.device):
+        rc = load_library().dcn_center_gate_forward(_ptr(y), _ptr(v), _ptr(z), _ptr(out), M, group, Cg,
+                                                    _DTYPE[y.dtype], _stream(y.device))
+    _check(rc, "dcn_center_gate_forward")
+    return out
+
+
+def center_gate_backward(y, v, z, grad_output, *, group):
+    """Gradients (grad_y, grad_v, grad_z) of center_gate_forward."""
+    M, Cg = _gate_check(y, v, z, group)
+    if grad_output.shape != y.shape or grad_output.dtype != y.dtype or not grad_output.is_contiguous() \
+            or grad_output.device != y.device:
+        raise ValueError("grad_output has the wrong shape, dtype, device or layout")
+    gy, gv, gz = torch.empty_like(y), torch.empty_like(v), torch.empty_like(z)
+    with torch.cuda.device(y.device):
+        rc = load_library().dcn_center_gate_backward(_ptr(y), _ptr(v), _ptr(z), _ptr(grad_output), _ptr(gy),
+                                                     _ptr(gv), _ptr(gz), M, group, Cg, _DTYPE[y.dtype],
+                                                     _stream(y.device))
+    _check(rc, "dcn_center_gate_backward")
+    return gy, gv, gz
+
+
+class CenterGateFunction(torch.autograd.Function):
+    """Autograd wrapper of the centre-feature gate."""
+
+    @staticmethod
+    def forward(ctx, y, v, z, group):
+        ctx.save_for_backward(y, v, z)
+        ctx.group = group
+        return center_gate_forward(y, v, z, group=group)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        y, v, z = ctx.saved_tensors
+        gy, gv, gz = center_gate_backward(y, v, z, grad_out.contiguous(), group=ctx.group)
+        return gy, gv, gz, None
+
+
+def center_gate(y, v, z, group):
+    """Differentiable centre-feature gate."""
+    return CenterGateFunction.apply(y, v, z, group)
 
 
 class DCNCoreFunction(torch.autograd.Function):

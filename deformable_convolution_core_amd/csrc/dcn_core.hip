@@ -10,10 +10,13 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include <hip/hip_runtime.h>
 
 #include "dcn_core.h"
 #include "dcn_kernels.hpp"
+#include "dcn_gate.hpp"
 
 using namespace dcn;
 
@@ -625,5 +628,96 @@ extern "C" const char* dcn_status_string(int status)
     case DCN_ERR_UNSUPPORTED: return "DCN_ERR_UNSUPPORTED: valid request outside what this build implements";
     case DCN_ERR_HIP: return "DCN_ERR_HIP: the HIP runtime reported an error";
     default: return "unknown dcn_status";
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Centre-feature gate of the DCNv4 layer (dcn_gate.hpp).
+namespace {
+
+struct GateCall {
+    uint64_t rows;
+    uint32_t row_bytes;
+    int vb;            // 16-byte vectors, or one element per access
+    unsigned blocks;
+};
+
+int gate_validate(GateCall& gc, long long M, int G, int Cg, int dtype, std::initializer_list<const void*> ptrs)
+{
+    const int eb = elem_bytes(dtype);
+    if (eb == 0 || M < 0 || G < 1 || Cg < 1) return DCN_ERR_INVALID_ARG;
+    const unsigned long long rows = (unsigned long long)M * (unsigned long long)G;
+    if ((long long)Cg * eb >= (1ll << 30) || rows >= (1ull << 40)) return DCN_ERR_UNSUPPORTED;
+    gc.rows = rows;
+    gc.row_bytes = (uint32_t)(Cg * eb);
+    if (M == 0) return DCN_OK;
+    for (const void* p : ptrs) {
+        if (!p || !aligned(p, (uintptr_t)eb)) return DCN_ERR_INVALID_ARG;
+    }
+    gc.vb = gc.row_bytes % 16 == 0 ? 16 : eb;
+    if ((gc.rows + kGateBlock - 1) / kGateBlock >= (1ull << 31)) return DCN_ERR_UNSUPPORTED;
+    gc.blocks = (unsigned)((gc.rows + kGateBlock - 1) / kGateBlock);
+    return DCN_OK;
+}
+
+template <typename T>
+int gate_forward_typed(const GateCall& gc, const void* y, const void* v, const void* z, void* out, bool vec,
+                       hipStream_t st)
+{
+    if (vec)
+        hipLaunchKernelGGL((dcn_gate_forward_kernel<T, 16>), dim3(gc.blocks), dim3(kGateBlock), 0, st,
+                           (const char*)y, (const char*)v, (const char*)z, (char*)out, gc.rows, gc.row_bytes);
+    else
+        hipLaunchKernelGGL((dcn_gate_forward_kernel<T, Elem<T>::bytes>), dim3(gc.blocks), dim3(kGateBlock), 0, st,
+                           (const char*)y, (const char*)v, (const char*)z, (char*)out, gc.rows, gc.row_bytes);
+    return launch_status();
+}
+
+template <typename T>
+int gate_backward_typed(const GateCall& gc, const void* y, const void* v, const void* z, const void* go, void* gy,
+                        void* gv, void* gz, bool vec, hipStream_t st)
+{
+    if (vec)
+        hipLaunchKernelGGL((dcn_gate_backward_kernel<T, 16>), dim3(gc.blocks), dim3(kGateBlock), 0, st,
+                           (const char*)y, (const char*)v, (const char*)z, (const char*)go, (char*)gy, (char*)gv,
+                           (char*)gz, gc.rows, gc.row_bytes);
+    else
+        hipLaunchKernelGGL((dcn_gate_backward_kernel<T, Elem<T>::bytes>), dim3(gc.blocks), dim3(kGateBlock), 0, st,
+                           (const char*)y, (const char*)v, (const char*)z, (const char*)go, (char*)gy, (char*)gv,
+                           (char*)gz, gc.rows, gc.row_bytes);
+    return launch_status();
+}
+
+}  // namespace
+
+extern "C" int dcn_center_gate_forward(const void* y, const void* v, const void* z, void* output, long long M,
+                                       int G, int Cg, int dtype, void* stream)
+{
+    GateCall gc{};
+    int rc = gate_validate(gc, M, G, Cg, dtype, {y, v, z, output});
+    if (rc != DCN_OK || M == 0) return rc;
+    const bool vec = gc.vb == 16 && aligned(y, 16) && aligned(v, 16) && aligned(output, 16);
+    hipStream_t st = (hipStream_t)stream;
+    switch (dtype) {
+    case DCN_F32: return gate_forward_typed<float>(gc, y, v, z, output, vec, st);
+    case DCN_F16: return gate_forward_typed<_Float16>(gc, y, v, z, output, vec, st);
+    default: return gate_forward_typed<__bf16>(gc, y, v, z, output, vec, st);
+    }
+}
+
+extern "C" int dcn_center_gate_backward(const void* y, const void* v, const void* z, const void* grad_output,
+                                        void* grad_y, void* grad_v, void* grad_z, long long M, int G, int Cg,
+                                        int dtype, void* stream)
+{
+    GateCall gc{};
+    int rc = gate_validate(gc, M, G, Cg, dtype, {y, v, z, grad_output, grad_y, grad_v, grad_z});
+    if (rc != DCN_OK || M == 0) return rc;
+    const bool vec = gc.vb == 16 && aligned(y, 16) && aligned(v, 16) && aligned(grad_output, 16) &&
+                     aligned(grad_y, 16) && aligned(grad_v, 16);
+    hipStream_t st = (hipStream_t)stream;
+    switch (dtype) {
+    case DCN_F32: return gate_backward_typed<float>(gc, y, v, z, grad_output, grad_y, grad_v, grad_z, vec, st);
+    case DCN_F16: return gate_backward_typed<_Float16>(gc, y, v, z, grad_output, grad_y, grad_v, grad_z, vec, st);
+    default: return gate_backward_typed<__bf16>(gc, y, v, z, grad_output, grad_y, grad_v, grad_z, vec, st);
     }
 }

@@ -159,6 +159,32 @@ int dcn_core_backward_ex(const void* input, const void* offset, const void* mask
                          int pad, int dilation, float offset_scale, int flags, int dtype,
                          void* stream);
 
+/* Centre-feature gate of the DCNv4 layer ([FB] section 3: an optional sigmoid
+ * gate blends the centre pixel's projected features with the sampling
+ * result).  For M pixels of G groups of Cg channels:
+ *
+ *   output[m, g*Cg+c] = y[m, g*Cg+c] * (1 - s) + v[m, g*Cg+c] * s,
+ *   s = 1 / (1 + exp(-z[m, g]))
+ *
+ * y (the core's output), v (the layer's projected input) and output are
+ * (M, G*Cg); z is (M, G); one dtype for all, binary32 arithmetic, one
+ * rounding per stored value.  output may be the same buffer as y or v.
+ * M >= 0 (M == 0 is a no-op; then the pointers may be NULL), G, Cg >= 1.
+ * Returns DCN_OK, DCN_ERR_INVALID_ARG (bad size or dtype, a NULL or
+ * misaligned pointer), DCN_ERR_UNSUPPORTED (a row of 2^30 bytes or more, or
+ * 2^40 or more (pixel, group) rows) or DCN_ERR_HIP. */
+int dcn_center_gate_forward(const void* y, const void* v, const void* z, void* output, long long M,
+                            int G, int Cg, int dtype, void* stream);
+
+/* Backward of the gate for grad_output (M, G*Cg): grad_y = grad_output *
+ * (1 - s), grad_v = grad_output * s (each overwritten, shape of y), and
+ * grad_z[m, g] = s (1 - s) * sum_c grad_output * (v - y) (overwritten, shape
+ * of z).  grad_y or grad_v may be the same buffer as grad_output.  Same sizes
+ * and errors as dcn_center_gate_forward. */
+int dcn_center_gate_backward(const void* y, const void* v, const void* z, const void* grad_output,
+                             void* grad_y, void* grad_v, void* grad_z, long long M, int G, int Cg,
+                             int dtype, void* stream);
+
 /* Static, human-readable name of a dcn_status value. */
 const char* dcn_status_string(int status);
 

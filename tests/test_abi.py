@@ -143,6 +143,48 @@ def test_forward_ex_empty_batch_and_old_entry_points():
     assert bwd_ex(lib, flags=4, N=0, ptrs=(0,) * 7) == OK
 
 
+def gate(lib, fn="forward", M=10, G=2, Cg=8, dtype=0, ptrs=None):
+    n = 4 if fn == "forward" else 7
+    ptrs = ptrs if ptrs is not None else tuple(0x1000 * (i + 1) for i in range(n))
+    vp = [ctypes.c_void_p(x) if x else None for x in ptrs]
+    f = lib.dcn_center_gate_forward if fn == "forward" else lib.dcn_center_gate_backward
+    return f(*vp, M, G, Cg, dtype, None)
+
+
+@pytest.mark.parametrize("fn", ["forward", "backward"])
+def test_gate_validation(fn):
+    lib = dcn.load_library()
+    n = 4 if fn == "forward" else 7
+    assert gate(lib, fn, M=-1) == INVALID
+    assert gate(lib, fn, G=0) == INVALID
+    assert gate(lib, fn, Cg=0) == INVALID
+    assert gate(lib, fn, dtype=3) == INVALID
+    assert gate(lib, fn, M=0, ptrs=(0,) * n) == OK
+    for k in range(n):
+        ptrs = [0x1000 * (i + 1) for i in range(n)]
+        ptrs[k] = 0
+        assert gate(lib, fn, ptrs=tuple(ptrs)) == INVALID          # a NULL pointer
+        ptrs[k] = 0x1001
+        assert gate(lib, fn, dtype=1, ptrs=tuple(ptrs)) == INVALID  # not element aligned
+    assert gate(lib, fn, Cg=1 << 29) == UNSUPPORTED                # a row of 2^31 bytes
+    assert gate(lib, fn, M=1 << 39, G=4) == UNSUPPORTED             # 2^41 rows
+
+
+def test_layer_rejects_grid_changing_geometry():
+    from deformable_convolution_core_amd.layer import DCNv4
+    with pytest.raises(ValueError):
+        DCNv4(64, kernel_size=4, group=4)          # even K cannot keep the grid
+    with pytest.raises(ValueError):
+        DCNv4(64, kernel_size=3, stride=2, group=4)
+    with pytest.raises(ValueError):
+        DCNv4(64, kernel_size=3, pad=0, group=4)
+    with pytest.raises(ValueError):
+        DCNv4(60, kernel_size=3, group=8)          # channels not divisible
+    layer = DCNv4(64, kernel_size=3, group=4, remove_center=True, center_feature_scale=True)
+    assert layer.offset_mask.out_features == 4 * 3 * 8
+    assert layer.center_feature_scale_proj.out_features == 4
+
+
 def test_status_strings():
     lib = dcn.load_library()
     for code, prefix in ((0, b"DCN_OK"), (1, b"DCN_ERR_INVALID_ARG"), (2, b"DCN_ERR_UNSUPPORTED"),
