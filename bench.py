@@ -10,7 +10,9 @@ the four FlashInternImage-T stage shapes, the core op of a whole
 FlashInternImage-T forward (the stage shapes at their depths, 30 launches),
 the DCNv3 large-channel stage at stride 1 and 2, the DCNv4 stage-1 shapes
 with DCNv4's packed offset+mask tensor, the fp32 forward + backward, the
-half-precision backward, and the CPU oracle timed on the host cores.
+half-precision backward, the whole DCNv4 layer around the core (projections,
+core, centre-feature gate) at the headline shape, and the CPU oracle timed on
+the host cores.
 
 Inputs are seeded synthetic tensors (no dataset, no weights).  Timing uses
 R rotating copies of every tensor (R * bytes > 512 MB, twice the 256 MB
@@ -214,6 +216,89 @@ def fii_t_sweep(steps, warmup):
                 GBps=round(nbytes / (ms * 1e-3) / 1e9, 1))
 
 
+def graph_time(fn, steps, warmup):
+    """Mean ms of fn() over `steps` calls captured in one graph (on a side
+    stream) and replayed between two events."""
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(steps):
+            fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / steps
+
+
+def eager_time(fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def layer_record(w, steps, warmup):
+    """The DCNv4 layer around the core at workload w's shape, with the
+    centre-feature gate: value and offset+mask projections (BLAS GEMMs), HIP
+    core on the packed records, HIP gate, output projection.  Random weights
+    (no checkpoint).  Forward in a graph; forward + backward eager (autograd).
+    Also the gate kernel alone, against HBM."""
+    from deformable_convolution_core_amd.layer import DCNv4
+    dt = inputs.DTYPES[w.dtype]
+    torch.manual_seed(0)
+    layer = DCNv4(w.C, kernel_size=w.K, group=w.G, offset_scale=w.offset_scale, center_feature_scale=True,
+                  device="cuda", dtype=torch.float32)
+    with torch.no_grad():
+        layer.offset_mask.weight.mul_(1.5)
+    layer = layer.to(dt)
+    x = inputs.normal((w.N, w.H, w.W, w.C), w.seed_base + 21, 1.0, w.dtype).to("cuda")
+    gout = inputs.normal((w.N, w.H, w.W, w.C), w.seed_base + 22, 1.0, w.dtype).to("cuda")
+    with torch.no_grad():
+        fwd_ms = graph_time(lambda: layer(x), steps, warmup)
+    xi = x.clone().requires_grad_(True)
+
+    def fwd_bwd():
+        layer.zero_grad(set_to_none=True)
+        xi.grad = None
+        layer(xi).backward(gout)
+    fb_ms = eager_time(fwd_bwd, max(5, steps // 4), 3)
+    # the gate alone: read y, v, z; write out
+    M = w.N * w.H * w.W
+    y = torch.randn(M, w.C, device="cuda", dtype=dt)
+    v = torch.randn(M, w.C, device="cuda", dtype=dt)
+    z = torch.randn(M, w.G, device="cuda", dtype=dt)
+    out = torch.empty_like(y)
+    gate_ms = graph_time(lambda: dcn.center_gate_forward(y, v, z, group=w.G, out=out), steps, warmup)
+    gate_bytes = (3 * M * w.C + M * w.G) * w.elem_bytes
+    del layer, x, xi, gout, y, v, z, out
+    torch.cuda.empty_cache()
+    return dict(workload=f"DCNv4 layer (value, offset+mask, gate, output projections + core) at {w.name}",
+                dtype=w.dtype, center_feature_scale=True, forward_us=round(fwd_ms * 1e3, 2),
+                forward_backward_us_eager=round(fb_ms * 1e3, 2),
+                images_per_s_forward=round(w.N / (fwd_ms * 1e-3), 1),
+                gate_kernel=dict(us=round(gate_ms * 1e3, 3), min_bytes=gate_bytes,
+                                 GBps=round(gate_bytes / (gate_ms * 1e-3) / 1e9, 1),
+                                 frac_hbm=round(gate_bytes / (gate_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)))
+
+
 def cpu_baseline(w):
     """The oracle as it stands, on the host cores, over whole batches of the
     headline workload, repeated until at least ~10 s of wall time."""
@@ -354,6 +439,10 @@ def main():
                                frac_hbm=round(wh.min_bytes_backward() / (hms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)))
             log(f"backward c5 {dt}: {halves[-1]['us']} us")
         extra["backward_half"] = halves
+        lay = layer_record(inputs.WORKLOADS[inputs.HEADLINE], max(20, args.steps // 4), 5)
+        extra["dcnv4_layer"] = lay
+        log(f"DCNv4 layer at c2: forward {lay['forward_us']} us, forward+backward {lay['forward_backward_us_eager']} us; "
+            f"gate {lay['gate_kernel']['us']} us ({lay['gate_kernel']['GBps']} GB/s)")
         fii = fii_t_sweep(max(5, args.steps // 20), 2)
         extra["fii_t_core_op"] = fii
         log(f"FlashInternImage-T core op: {fii['us_per_batch']} us per batch of {fii['batch']}, "

@@ -15,8 +15,9 @@ mask; the constructor's arguments follow the DCNv4 module of
     out = y @ Wo.T + bo
 
 The four projections are plain GEMMs and run in the platform BLAS through
-torch.nn.functional.linear; the sampling core and the gate run in this
-package's HIP kernels.  Input and output are channels-last (N, H, W, C).  The
+torch (their weight gradients as one batched GEMM over row chunks, see
+weight_grad); the sampling core and the gate run in this package's HIP
+kernels.  Input and output are channels-last (N, H, W, C).  The
 offsets are predicted per input pixel, so the layer keeps the grid: stride
 1 and pad = dilation * (K - 1) / 2 with an odd K.
 """
@@ -26,6 +27,58 @@ import torch
 import torch.nn.functional as F
 
 from . import center_gate, dcnv4_core, points
+
+
+_WGRAD_ROWS = 2048   # rows per chunk of the weight-gradient reduction
+
+
+def weight_grad(g2: torch.Tensor, x2: torch.Tensor) -> torch.Tensor:
+    """sum over rows m of g2[m, :]^T x2[m, :] -> (out, in), for a row count in
+    the hundreds of thousands and a few dozen columns.  One GEMM with that
+    long reduction runs on a handful of tiles; chunks of _WGRAD_ROWS rows as
+    one batched GEMM spread it over the chip, and the per-chunk partials are
+    summed in binary32.  The narrower operand is the one transposed, and both
+    GEMM operands are contiguous."""
+    M, O = g2.shape
+    I = x2.shape[1]
+    S = M // _WGRAD_ROWS
+    out = torch.zeros(O, I, dtype=torch.float32, device=g2.device)
+    if S > 0:
+        n = S * _WGRAD_ROWS
+        gc = g2[:n].view(S, _WGRAD_ROWS, O)
+        xc = x2[:n].view(S, _WGRAD_ROWS, I)
+        if O <= I:
+            part = torch.bmm(gc.transpose(1, 2).contiguous(), xc)              # (S, O, I)
+            out += part.sum(0, dtype=torch.float32)
+        else:
+            part = torch.bmm(xc.transpose(1, 2).contiguous(), gc)              # (S, I, O)
+            out += part.sum(0, dtype=torch.float32).t()
+    if S * _WGRAD_ROWS < M:
+        r = S * _WGRAD_ROWS
+        out += (g2[r:].t().float() @ x2[r:].float())
+    return out.to(g2.dtype)
+
+
+class _Projection(torch.autograd.Function):
+    """x @ W.T + b with the weight gradient formed by weight_grad."""
+
+    @staticmethod
+    def forward(ctx, x, W, b):
+        ctx.save_for_backward(x, W)
+        return F.linear(x, W, b)
+
+    @staticmethod
+    def backward(ctx, g):
+        x, W = ctx.saved_tensors
+        g2 = g.reshape(-1, g.shape[-1]).contiguous()
+        gx = (g2 @ W).view(x.shape) if ctx.needs_input_grad[0] else None
+        gW = weight_grad(g2, x.reshape(-1, x.shape[-1])) if ctx.needs_input_grad[1] else None
+        gb = g2.sum(0, dtype=torch.float32).to(g.dtype) if ctx.needs_input_grad[2] else None
+        return gx, gW, gb
+
+
+def project(x, lin: torch.nn.Linear):
+    return _Projection.apply(x, lin.weight, lin.bias)
 
 
 class DCNv4(torch.nn.Module):
@@ -59,14 +112,14 @@ class DCNv4(torch.nn.Module):
         if x.dim() != 4 or x.shape[-1] != self.channels:
             raise ValueError(f"input must be (N, H, W, {self.channels})")
         x = x.contiguous()
-        v = F.linear(x, self.value_proj.weight, self.value_proj.bias)
-        om = F.linear(x, self.offset_mask.weight, self.offset_mask.bias)
+        v = project(x, self.value_proj)
+        om = project(x, self.offset_mask)
         y = dcnv4_core(v, om, self.kernel_size, 1, self.pad, self.dilation, self.offset_scale, self.group,
                        self.remove_center)
         if self.center_feature_scale_proj is not None:
-            z = F.linear(x, self.center_feature_scale_proj.weight, self.center_feature_scale_proj.bias)
+            z = project(x, self.center_feature_scale_proj)
             y = center_gate(y, v, z, self.group)
-        return F.linear(y, self.output_proj.weight, self.output_proj.bias)
+        return project(y, self.output_proj)
 
     def numpy_params(self) -> dict:
         """The parameters as float64 numpy arrays, keyed Wv, bv, Wom, bom, Wc, bc, Wo, bo."""

@@ -209,3 +209,16 @@ def test_binding_rejects_bad_tensors_before_calling():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         dcn.load_library(str(tmp_path / "nope.so"))
+
+
+@pytest.mark.parametrize("shape", [(5000, 64, 64), (4096, 108, 64), (4097, 4, 64), (100, 8, 8)])
+def test_layer_weight_grad_chunking(shape):
+    """The layer's chunked weight gradient equals the float64 sum over rows
+    (CPU tensors: the function is plain torch)."""
+    from deformable_convolution_core_amd.layer import weight_grad
+    M, O, I = shape
+    gen = torch.Generator().manual_seed(M + O)
+    g, x = torch.randn(M, O, generator=gen), torch.randn(M, I, generator=gen)
+    want = g.double().t() @ x.double()
+    got = weight_grad(g, x).double()
+    assert (got - want).abs().max().item() <= 1e-5 * want.abs().max().item()
