@@ -77,7 +77,9 @@ def test_forward_rejects_invalid_arguments_on_host(kw):
 
 
 @pytest.mark.parametrize("kw", [dict(K=17, H=40, W=40, p=8), dict(N=1, H=40000, W=40000, G=1, Cg=8),
-                                dict(N=1, H=8, W=8, G=1 << 20, Cg=1 << 12)])
+                                dict(N=1, H=8, W=8, G=1 << 20, Cg=1 << 12),
+                                # one pixel row past the largest image the GPU tests run (1448 x 1448 x 512 bf16)
+                                dict(N=1, H=1449, W=1449, G=16, Cg=32, dtype=2)])
 def test_forward_unsupported_sizes(kw):
     assert fwd(dcn.load_library(), **kw) == UNSUPPORTED
 
