@@ -257,10 +257,11 @@ def eager_time(fn, steps, warmup):
 
 def layer_record(w, steps, warmup):
     """The DCNv4 layer around the core at workload w's shape, with the
-    centre-feature gate: value and offset+mask projections (BLAS GEMMs), HIP
-    core on the packed records, HIP gate, output projection.  Random weights
-    (no checkpoint).  Forward in a graph; forward + backward eager (autograd).
-    Also the gate kernel alone, against HBM."""
+    centre-feature gate: value and offset+mask projections (matrix-core
+    GEMM), HIP core on the packed records, HIP gate, output projection.
+    Random weights (no checkpoint).  Forward in a graph; forward + backward
+    eager (autograd).  Also the gate kernel and the value projection alone,
+    against HBM (the projection also on the platform BLAS)."""
     from deformable_convolution_core_amd.layer import DCNv4
     dt = inputs.DTYPES[w.dtype]
     torch.manual_seed(0)
@@ -288,7 +289,14 @@ def layer_record(w, steps, warmup):
     out = torch.empty_like(y)
     gate_ms = graph_time(lambda: dcn.center_gate_forward(y, v, z, group=w.G, out=out), steps, warmup)
     gate_bytes = (3 * M * w.C + M * w.G) * w.elem_bytes
-    del layer, x, xi, gout, y, v, z, out
+    # the value projection alone: this package's matrix-core GEMM against the platform BLAS
+    wv, bv = layer.value_proj.weight, layer.value_proj.bias
+    xm = x.reshape(M, w.C)
+    ym = torch.empty(M, w.C, device="cuda", dtype=dt)
+    lin_ms = graph_time(lambda: dcn.linear(xm, wv, bv, out=ym), steps, warmup)
+    blas_ms = graph_time(lambda: torch.nn.functional.linear(xm, wv, bv), steps, warmup)
+    lin_bytes = (2 * M * w.C + w.C * w.C + w.C) * w.elem_bytes
+    del layer, x, xi, gout, y, v, z, out, xm, ym
     torch.cuda.empty_cache()
     return dict(workload=f"DCNv4 layer (value, offset+mask, gate, output projections + core) at {w.name}",
                 dtype=w.dtype, center_feature_scale=True, forward_us=round(fwd_ms * 1e3, 2),
@@ -296,7 +304,11 @@ def layer_record(w, steps, warmup):
                 images_per_s_forward=round(w.N / (fwd_ms * 1e-3), 1),
                 gate_kernel=dict(us=round(gate_ms * 1e3, 3), min_bytes=gate_bytes,
                                  GBps=round(gate_bytes / (gate_ms * 1e-3) / 1e9, 1),
-                                 frac_hbm=round(gate_bytes / (gate_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)))
+                                 frac_hbm=round(gate_bytes / (gate_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)),
+                value_projection=dict(shape=f"{M}x{w.C} @ {w.C}x{w.C}", us=round(lin_ms * 1e3, 3),
+                                      GBps=round(lin_bytes / (lin_ms * 1e-3) / 1e9, 1),
+                                      frac_hbm=round(lin_bytes / (lin_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                      platform_blas_us=round(blas_ms * 1e3, 3)))
 
 
 def cpu_baseline(w):
@@ -442,7 +454,9 @@ def main():
         lay = layer_record(inputs.WORKLOADS[inputs.HEADLINE], max(20, args.steps // 4), 5)
         extra["dcnv4_layer"] = lay
         log(f"DCNv4 layer at c2: forward {lay['forward_us']} us, forward+backward {lay['forward_backward_us_eager']} us; "
-            f"gate {lay['gate_kernel']['us']} us ({lay['gate_kernel']['GBps']} GB/s)")
+            f"gate {lay['gate_kernel']['us']} us ({lay['gate_kernel']['GBps']} GB/s); value projection "
+            f"{lay['value_projection']['us']} us ({lay['value_projection']['GBps']} GB/s, platform BLAS "
+            f"{lay['value_projection']['platform_blas_us']} us)")
         fii = fii_t_sweep(max(5, args.steps // 20), 2)
         extra["fii_t_core_op"] = fii
         log(f"FlashInternImage-T core op: {fii['us_per_batch']} us per batch of {fii['batch']}, "

@@ -27,7 +27,7 @@ import os
 import torch
 
 __all__ = ["forward", "backward", "forward_packed", "backward_packed", "out_size", "dcn_core",
-           "dcnv4_core", "center_gate_forward", "center_gate_backward", "center_gate",
+           "dcnv4_core", "center_gate_forward", "center_gate_backward", "center_gate", "linear",
            "DCNCoreFunction", "DCNv4CoreFunction", "CenterGateFunction", "DCNError", "library_path",
            "load_library"]
 
@@ -39,7 +39,7 @@ DCN_F32, DCN_F16, DCN_BF16 = 0, 1, 2
 _DTYPE = {torch.float32: DCN_F32, torch.float16: DCN_F16, torch.bfloat16: DCN_BF16}
 EXPORTED = ("dcn_core_out_size", "dcn_core_forward", "dcn_core_backward", "dcn_core_forward_ex",
             "dcn_core_backward_ex", "dcn_center_gate_forward", "dcn_center_gate_backward",
-            "dcn_status_string")
+            "dcn_linear_forward", "dcn_status_string")
 FLAG_SOFTMAX, FLAG_REMOVE_CENTER, FLAG_PACKED = 1, 2, 4
 
 
@@ -78,6 +78,8 @@ def load_library(path: str | None = None):
     lib.dcn_center_gate_forward.restype = i
     lib.dcn_center_gate_backward.argtypes = [vp] * 7 + [ll, i, i, i, vp]
     lib.dcn_center_gate_backward.restype = i
+    lib.dcn_linear_forward.argtypes = [vp] * 4 + [ll, i, i, i, vp]
+    lib.dcn_linear_forward.restype = i
     lib.dcn_status_string.argtypes = [i]
     lib.dcn_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -268,6 +270,30 @@ def center_gate_backward(y, v, z, grad_output, *, group):
                                                      _stream(y.device))
     _check(rc, "dcn_center_gate_backward")
     return gy, gv, gz
+
+
+def linear(x, weight, bias=None, *, out=None) -> torch.Tensor:
+    """x @ weight.T + bias over the last axis of x, on the matrix cores (HIP).
+    x (..., K), weight (N, K), bias (N) or None.  Raises DCNError with status
+    DCN_ERR_UNSUPPORTED (2) for shapes the kernel does not take (K not a
+    multiple of 4, misaligned or too wide), so a caller can use another GEMM."""
+    if weight.dim() != 2 or x.shape[-1] != weight.shape[1]:
+        raise ValueError("x (..., K) and weight (N, K) must agree on K")
+    N, K = weight.shape
+    for name, t in (("x", x), ("weight", weight)) + ((("bias", bias),) if bias is not None else ()):
+        _check_tensor(name, t, x)
+    if bias is not None and tuple(bias.shape) != (N,):
+        raise ValueError("bias must be (N,)")
+    if x.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    M = x.numel() // K if K else 0
+    if out is None:
+        out = torch.empty(*x.shape[:-1], N, dtype=x.dtype, device=x.device)
+    with torch.cuda.device(x.device):
+        rc = load_library().dcn_linear_forward(_ptr(x), _ptr(weight), None if bias is None else _ptr(bias),
+                                               _ptr(out), M, N, K, _DTYPE[x.dtype], _stream(x.device))
+    _check(rc, "dcn_linear_forward")
+    return out
 
 
 class CenterGateFunction(torch.autograd.Function):

@@ -17,6 +17,7 @@
 #include "dcn_core.h"
 #include "dcn_kernels.hpp"
 #include "dcn_gate.hpp"
+#include "dcn_linear.hpp"
 
 using namespace dcn;
 
@@ -720,4 +721,43 @@ extern "C" int dcn_center_gate_backward(const void* y, const void* v, const void
     case DCN_F16: return gate_backward_typed<_Float16>(gc, y, v, z, grad_output, grad_y, grad_v, grad_z, vec, st);
     default: return gate_backward_typed<__bf16>(gc, y, v, z, grad_output, grad_y, grad_v, grad_z, vec, st);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Projections of the DCNv4 layer: Y = X W^T + b (dcn_linear.hpp).
+extern "C" int dcn_linear_forward(const void* x, const void* w, const void* bias, void* y, long long M, int N,
+                                  int K, int dtype, void* stream)
+{
+    const int eb = elem_bytes(dtype);
+    if (eb == 0 || M < 0 || N < 1 || K < 1) return DCN_ERR_INVALID_ARG;
+    if (M == 0) return DCN_OK;
+    if (!x || !w || !y) return DCN_ERR_INVALID_ARG;
+    if (!aligned(x, (uintptr_t)eb) || !aligned(w, (uintptr_t)eb) || !aligned(y, (uintptr_t)eb) ||
+        (bias && !aligned(bias, (uintptr_t)eb)))
+        return DCN_ERR_INVALID_ARG;
+    // four-element row chunks: K a multiple of 4 and 16-byte aligned tensors
+    if (K % 4 != 0 || !aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return DCN_ERR_UNSUPPORTED;
+    const uint64_t lds = (uint64_t)kLinNB * (uint64_t)(K + 4) * (uint64_t)eb;
+    const uint64_t m_tiles = ((uint64_t)M + 15) / 16;
+    if (lds > 160 * 1024 || m_tiles >= (1ull << 32) || (uint64_t)M * (uint64_t)(K > N ? K : N) >= (1ull << 62))
+        return DCN_ERR_UNSUPPORTED;
+    const uint32_t gy = (uint32_t)((N + kLinNB - 1) / kLinNB);
+    uint64_t gx = (m_tiles + 3) / 4;
+    const uint64_t cap = (1024 + gy - 1) / gy;   // about 4 blocks of 4 waves per CU in all
+    if (gx > cap) gx = cap;
+    LinArgs a{x, w, bias, y, (uint64_t)M, N, K, (uint32_t)m_tiles};
+    hipStream_t st = (hipStream_t)stream;
+    const dim3 grid((uint32_t)gx, gy);
+    switch (dtype) {
+    case DCN_F32:
+        hipLaunchKernelGGL(dcn_linear_kernel<float>, grid, dim3(kLinBlock), (uint32_t)lds, st, a);
+        break;
+    case DCN_F16:
+        hipLaunchKernelGGL(dcn_linear_kernel<_Float16>, grid, dim3(kLinBlock), (uint32_t)lds, st, a);
+        break;
+    default:
+        hipLaunchKernelGGL(dcn_linear_kernel<__bf16>, grid, dim3(kLinBlock), (uint32_t)lds, st, a);
+        break;
+    }
+    return launch_status();
 }

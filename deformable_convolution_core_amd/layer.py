@@ -14,10 +14,11 @@ mask; the constructor's arguments follow the DCNv4 module of
                                              optional centre-feature gate (HIP)
     out = y @ Wo.T + bo
 
-The four projections are plain GEMMs and run in the platform BLAS through
-torch (their weight gradients as one batched GEMM over row chunks, see
-weight_grad); the sampling core and the gate run in this package's HIP
-kernels.  Input and output are channels-last (N, H, W, C).  The
+The four projections and their input gradients run in this package's
+matrix-core GEMM (`linear`: X read once, W in on-chip memory), falling back
+to the platform BLAS for shapes it does not take; their weight gradients
+are one batched BLAS GEMM over row chunks (weight_grad).  The sampling core
+and the gate run in this package's HIP kernels.  Input and output are channels-last (N, H, W, C).  The
 offsets are predicted per input pixel, so the layer keeps the grid: stride
 1 and pad = dilation * (K - 1) / 2 with an odd K.
 """
@@ -26,7 +27,7 @@ from __future__ import annotations
 import torch
 import torch.nn.functional as F
 
-from . import center_gate, dcnv4_core, points
+from . import DCNError, center_gate, dcnv4_core, linear, points
 
 
 _WGRAD_ROWS = 2048   # rows per chunk of the weight-gradient reduction
@@ -59,19 +60,31 @@ def weight_grad(g2: torch.Tensor, x2: torch.Tensor) -> torch.Tensor:
     return out.to(g2.dtype)
 
 
+def _matmul_t(x, W, b=None):
+    """x @ W.T + b: the package's matrix-core kernel where it takes the shape,
+    else the platform BLAS."""
+    try:
+        return linear(x, W, b)
+    except DCNError as e:
+        if e.status != 2:        # only "unsupported shape" falls through
+            raise
+        return F.linear(x, W, b)
+
+
 class _Projection(torch.autograd.Function):
-    """x @ W.T + b with the weight gradient formed by weight_grad."""
+    """x @ W.T + b; the input gradient g @ W as the same kernel on W.T, the
+    weight gradient by weight_grad."""
 
     @staticmethod
     def forward(ctx, x, W, b):
         ctx.save_for_backward(x, W)
-        return F.linear(x, W, b)
+        return _matmul_t(x, W, b)
 
     @staticmethod
     def backward(ctx, g):
         x, W = ctx.saved_tensors
         g2 = g.reshape(-1, g.shape[-1]).contiguous()
-        gx = (g2 @ W).view(x.shape) if ctx.needs_input_grad[0] else None
+        gx = _matmul_t(g2, W.t().contiguous()).view(x.shape) if ctx.needs_input_grad[0] else None
         gW = weight_grad(g2, x.reshape(-1, x.shape[-1])) if ctx.needs_input_grad[1] else None
         gb = g2.sum(0, dtype=torch.float32).to(g.dtype) if ctx.needs_input_grad[2] else None
         return gx, gW, gb

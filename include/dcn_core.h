@@ -185,6 +185,23 @@ int dcn_center_gate_backward(const void* y, const void* v, const void* z, const 
                              void* grad_y, void* grad_v, void* grad_z, long long M, int G, int Cg,
                              int dtype, void* stream);
 
+/* A projection of the DCNv4 layer ([FB] section 3: the module's input and
+ * output projections and the fully connected offset/mask layer; [A100]
+ * section 1 merges the latter into one):
+ *
+ *   y[m, n] = sum_k x[m, k] * w[n, k] + bias[n]
+ *
+ * x (M, K), w (N, K) and y (M, N) are dense row-major in one dtype; bias (N)
+ * may be NULL (no bias).  Products and sums are binary32 (half-precision
+ * products are exact), y is rounded once.  M >= 0 (M == 0 is a no-op),
+ * N, K >= 1.  Returns DCN_OK, DCN_ERR_INVALID_ARG (bad size or dtype, a NULL
+ * or misaligned pointer), DCN_ERR_UNSUPPORTED (K not a multiple of 4, x, w
+ * or y not 16-byte aligned, or K > 636 in binary32 / 1276 in half
+ * precision, whose 64 rows of w would not fit in on-chip memory) or
+ * DCN_ERR_HIP.  A caller falls back to another GEMM on DCN_ERR_UNSUPPORTED. */
+int dcn_linear_forward(const void* x, const void* w, const void* bias, void* y, long long M, int N, int K,
+                       int dtype, void* stream);
+
 /* Static, human-readable name of a dcn_status value. */
 const char* dcn_status_string(int status);
 

@@ -172,6 +172,23 @@ def test_gate_validation(fn):
     assert gate(lib, fn, M=1 << 39, G=4) == UNSUPPORTED             # 2^41 rows
 
 
+def test_linear_validation():
+    lib = dcn.load_library()
+    vp = ctypes.c_void_p
+
+    def lin(x=0x1000, w=0x2000, b=None, y=0x3000, M=10, N=8, K=64, dtype=0):
+        return lib.dcn_linear_forward(vp(x) if x else None, vp(w) if w else None, vp(b) if b else None,
+                                      vp(y) if y else None, M, N, K, dtype, None)
+    assert lin(M=-1) == INVALID and lin(N=0) == INVALID and lin(K=0) == INVALID and lin(dtype=7) == INVALID
+    assert lin(x=0) == INVALID and lin(w=0) == INVALID and lin(y=0) == INVALID
+    assert lin(x=0x1001, dtype=1) == INVALID                   # not element aligned
+    assert lin(b=0x4001) == INVALID
+    assert lin(M=0, x=0, w=0, y=0) == OK
+    assert lin(K=6) == UNSUPPORTED                              # K not a multiple of 4
+    assert lin(x=0x1004) == UNSUPPORTED                         # not 16-byte aligned
+    assert lin(K=640) == UNSUPPORTED and lin(K=1280, dtype=1) == UNSUPPORTED   # w rows exceed on-chip memory
+
+
 def test_layer_rejects_grid_changing_geometry():
     from deformable_convolution_core_amd.layer import DCNv4
     with pytest.raises(ValueError):

@@ -162,19 +162,27 @@ def test_layer_fp32_matches_oracle(case):
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_layer_half_stagewise(dt):
     """Half precision: the layer's output equals its stages composed by hand
-    (bit for bit), and the HIP core and gate match the oracle on the layer's
-    own intermediates."""
+    (bit for bit), and the projections, the HIP core and the gate match the
+    float64 definitions on the layer's own intermediates."""
     N, H, W, G, Cg, K = 2, 14, 14, 4, 16, 3
     layer, x, gout = make_layer(N, H, W, G, Cg, K, False, True, 1.0, dt, 6400)
     out = layer(x)
-    v = F.linear(x, layer.value_proj.weight, layer.value_proj.bias)
-    om = F.linear(x, layer.offset_mask.weight, layer.offset_mask.bias)
+    v = dcn.linear(x, layer.value_proj.weight, layer.value_proj.bias)
+    om = dcn.linear(x, layer.offset_mask.weight, layer.offset_mask.bias)
     y = dcn.forward_packed(v, om, kernel_size=K, pad=1, group=G)
-    z = F.linear(x, layer.center_feature_scale_proj.weight, layer.center_feature_scale_proj.bias)
+    z = dcn.linear(x, layer.center_feature_scale_proj.weight, layer.center_feature_scale_proj.bias)
     yg = dcn.center_gate_forward(y, v, z, group=G)
-    want = F.linear(yg, layer.output_proj.weight, layer.output_proj.bias)
+    want = dcn.linear(yg, layer.output_proj.weight, layer.output_proj.bias)
     torch.cuda.synchronize()
     assert torch.equal(out, want)
+    # the projections against the float64 product of the same (half-precision) operands
+    for got, a, lin in ((v, x, layer.value_proj), (om, x, layer.offset_mask),
+                        (z, x, layer.center_feature_scale_proj), (want, yg, layer.output_proj)):
+        A, Wt, B = f64(a).reshape(-1, a.shape[-1]), f64(lin.weight), f64(lin.bias)
+        ref = A @ Wt.T + B
+        S = np.abs(A) @ np.abs(Wt).T + np.abs(B)
+        st = tolerance.compare(f64(got).reshape(ref.shape), ref, S, A.shape[1] + 1, dt)
+        assert st["ok"], ("projection", st)
     P = K * K
     off, mask = inputs.unpack_offset_mask(om.cpu(), G, P)
     ref, S = oracle.forward(f64(v), f64(off), f64(mask), K=K, stride=1, pad=1, dilation=1, offset_scale=1.0,
