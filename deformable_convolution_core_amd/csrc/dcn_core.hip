@@ -725,6 +725,9 @@ extern "C" int dcn_center_gate_backward(const void* y, const void* v, const void
 
 // ---------------------------------------------------------------------------
 // Projections of the DCNv4 layer: Y = X W^T + b (dcn_linear.hpp).
+#ifndef DCN_LIN_BLOCKS
+#define DCN_LIN_BLOCKS 1024
+#endif
 extern "C" int dcn_linear_forward(const void* x, const void* w, const void* bias, void* y, long long M, int N,
                                   int K, int dtype, void* stream)
 {
@@ -737,13 +740,15 @@ extern "C" int dcn_linear_forward(const void* x, const void* w, const void* bias
         return DCN_ERR_INVALID_ARG;
     // four-element row chunks: K a multiple of 4 and 16-byte aligned tensors
     if (K % 4 != 0 || !aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return DCN_ERR_UNSUPPORTED;
-    const uint64_t lds = (uint64_t)kLinNB * (uint64_t)(K + 4) * (uint64_t)eb;
+    // 64 rows of w, and for half types one 16 x 68 x buffer per wave
+    const uint64_t lds = ((uint64_t)kLinNB * (uint64_t)(K + 4) + (eb == 2 ? 4ull * 16ull * 68ull : 0ull)) * (uint64_t)eb;
     const uint64_t m_tiles = ((uint64_t)M + 15) / 16;
     if (lds > 160 * 1024 || m_tiles >= (1ull << 32) || (uint64_t)M * (uint64_t)(K > N ? K : N) >= (1ull << 62))
         return DCN_ERR_UNSUPPORTED;
+    // about DCN_LIN_BLOCKS blocks of 4 waves in all, over the column blocks
     const uint32_t gy = (uint32_t)((N + kLinNB - 1) / kLinNB);
     uint64_t gx = (m_tiles + 3) / 4;
-    const uint64_t cap = (1024 + gy - 1) / gy;   // about 4 blocks of 4 waves per CU in all
+    const uint64_t cap = (DCN_LIN_BLOCKS + gy - 1) / gy;
     if (gx > cap) gx = cap;
     LinArgs a{x, w, bias, y, (uint64_t)M, N, K, (uint32_t)m_tiles};
     hipStream_t st = (hipStream_t)stream;

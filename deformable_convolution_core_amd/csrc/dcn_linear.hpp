@@ -22,6 +22,7 @@ namespace dcn {
 
 constexpr int kLinBlock = 256;   // 4 waves
 constexpr int kLinNB = 64;       // columns of Y per block (W rows staged in LDS)
+constexpr int kLinSU = 8;        // w chunks a thread has in flight while staging
 
 typedef float lin_f4 __attribute__((ext_vector_type(4)));
 typedef _Float16 lin_h4 __attribute__((ext_vector_type(4)));
@@ -86,7 +87,7 @@ struct LinArgs {
 
 // grid: (blocks over 16-row tiles, ceil(N / 64)); K % 4 == 0.  LDS: 64 W rows
 // at a stride of K + 4 elements (the pad puts the 16 rows one 16-lane group
-// reads on distinct banks).
+// reads on distinct banks), then one 16 x 68-element x buffer per wave.
 template <typename T>
 __global__ __launch_bounds__(kLinBlock) void dcn_linear_kernel(LinArgs a)
 {
@@ -99,62 +100,223 @@ __global__ __launch_bounds__(kLinBlock) void dcn_linear_kernel(LinArgs a)
     const int nb = N - n0 < kLinNB ? N - n0 : kLinNB;
     const T* W = (const T*)a.w;
     const T* X = (const T*)a.x;
-    // stage W[n0 : n0 + 64, :] in chunks of four elements; rows past N are zero
-    const int kq = K >> 2;
-    for (int e = t; e < kLinNB * kq; e += kLinBlock) {
-        const int r = e / kq, c = (e - r * kq) * 4;
-        const LinFrag<T> f = r < nb ? lin_load<T>(W + (size_t)(n0 + r) * K + c) : lin_zero<T>();
-        if constexpr (EB == 4) *(uint4*)(wl + r * S + c) = make_uint4(f.d[0], f.d[1], f.d[2], f.d[3]);
-        else *(uint2*)(wl + r * S + c) = make_uint2(f.d[0], f.d[1]);
+    // stage W[n0 : n0 + 64, :] in chunks of four elements, kLinSU chunks per
+    // thread in flight at a time (one read latency per group, not per
+    // chunk); rows past N are zero
+    const int kq = K >> 2, total = kLinNB * kq;
+    for (int e0 = t; e0 < total; e0 += kLinBlock * kLinSU) {
+        LinFrag<T> f[kLinSU];
+#pragma unroll
+        for (int u = 0; u < kLinSU; ++u) {
+            const int e = e0 + u * kLinBlock;
+            const int r = e / kq, c = (e - r * kq) * 4;
+            f[u] = (e < total && r < nb) ? lin_load<T>(W + (size_t)(n0 + r) * K + c) : lin_zero<T>();
+        }
+#pragma unroll
+        for (int u = 0; u < kLinSU; ++u) {
+            const int e = e0 + u * kLinBlock;
+            if (e >= total) break;
+            const int r = e / kq, c = (e - r * kq) * 4;
+            if constexpr (EB == 4) *(uint4*)(wl + r * S + c) = make_uint4(f[u].d[0], f[u].d[1], f[u].d[2], f[u].d[3]);
+            else *(uint2*)(wl + r * S + c) = make_uint2(f[u].d[0], f[u].d[1]);
+        }
     }
     __syncthreads();
 
-    const int ntiles = (nb + 15) >> 4;           // 16-column blocks with any valid column
+    const int ntiles = (nb + 15) >> 4;           // 16-column blocks with any valid column (stores)
     const int q = l >> 4, r16 = l & 15;
+    // this lane's 16 bias values: unconditional reads at a clamped index (so
+    // all 16 are in flight together), zeroed past N afterwards
     float bias[kLinNB / 16][4];
 #pragma unroll
     for (int b = 0; b < kLinNB / 16; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int n = n0 + 16 * b + 4 * q + i;
-            bias[b][i] = (a.bias && n < N) ? ld1((const T*)a.bias + n) : 0.f;
-        }
+        for (int i = 0; i < 4; ++i) bias[b][i] = 0.f;
+    if (a.bias) {
+        const T* bp = (const T*)a.bias;
+#pragma unroll
+        for (int b = 0; b < kLinNB / 16; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = n0 + 16 * b + 4 * q + i;
+                bias[b][i] = ld1(bp + (n < N ? n : N - 1));
+            }
+#pragma unroll
+        for (int b = 0; b < kLinNB / 16; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (n0 + 16 * b + 4 * q + i >= N) bias[b][i] = 0.f;
+    }
     const bool vec_store = (N & 3) == 0;
-    for (uint32_t mt = blockIdx.x * 4u + (uint32_t)wave; mt < a.m_tiles; mt += gridDim.x * 4u) {
-        const uint64_t m = (uint64_t)mt * 16u + (uint32_t)r16;
-        const uint64_t mr = m < a.M ? m : a.M - 1;   // rows past M read the last row and store nothing
-        const T* xrow = X + mr * (uint64_t)K;
-        lin_f4 acc[kLinNB / 16];
+    const int kfull = K & ~15;
+    const int nc = kfull >> 6;                   // full 64-wide chunks of k per tile
+    const uint32_t stride = gridDim.x * 4u;
+    // x of one 64-wide chunk of a 16-row tile is read with whole 16-byte
+    // accesses, each instruction covering whole rows of the chunk
+    // (contiguous in memory), into this wave's LDS buffer; the matrix
+    // operands are then picked out of LDS (rows padded by four elements so a
+    // 16-lane group's reads fall on distinct banks).
+    constexpr int E16 = 16 / EB;                  // elements per 16-byte access
+    constexpr int LPR = 64 / E16;                 // lanes per 64-element row chunk
+    constexpr int RPI = 64 / LPR;                 // rows per instruction
+    constexpr int NI = 16 / RPI;                  // instructions per chunk
+    constexpr int XS = 64 + 4;                    // LDS row stride of the x buffer (elements)
+    T* xl = wl + kLinNB * S + wave * 16 * XS;     // (half precision only)
+    auto load_chunk = [&](uint32_t mtile, int chunk, uint4* raw) {
 #pragma unroll
-        for (int b = 0; b < kLinNB / 16; ++b) acc[b] = lin_f4{0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < K; k0 += 16) {
-            const int kk = k0 + 4 * q;
-            const LinFrag<T> xb = kk < K ? lin_load<T>(xrow + kk) : lin_zero<T>();
+        for (int h = 0; h < NI; ++h) {
+            const uint64_t row = (uint64_t)mtile * 16u + (uint32_t)(h * RPI + l / LPR);
+            const T* p = X + (row < a.M ? row : a.M - 1) * (uint64_t)K + chunk * 64 + (l % LPR) * E16;
+            raw[h] = *(const uint4*)p;
+        }
+    };
+    auto put_chunk = [&](const uint4* raw) {
 #pragma unroll
-            for (int b = 0; b < kLinNB / 16; ++b) {
-                if (b < ntiles) {
-                    const T* wp = wl + (16 * b + r16) * S + kk;
-                    const LinFrag<T> wa = kk < K ? lin_load<T>(wp) : lin_zero<T>();
-                    acc[b] = lin_mfma<T>(wa, xb, acc[b]);
-                }
+        for (int h = 0; h < NI; ++h) {
+            T* d = xl + (h * RPI + l / LPR) * XS + (l % LPR) * E16;
+            if constexpr (EB == 4) {
+                *(uint4*)d = raw[h];
+            } else {   // rows of 136 bytes: 8-byte aligned
+                *(uint2*)d = make_uint2(raw[h].x, raw[h].y);
+                *(uint2*)(d + 4) = make_uint2(raw[h].z, raw[h].w);
             }
         }
-        if (m < a.M) {
-            T* yrow = (T*)a.y + m * (uint64_t)N;
+    };
+    // store one finished 16-row tile: bias, one rounding, four consecutive
+    // outputs per lane (element stores where N is not a multiple of 4)
+    auto finish = [&](uint32_t mtile, const lin_f4* acc) {
+        const uint64_t m = (uint64_t)mtile * 16u + (uint32_t)r16;
+        if (m >= a.M) return;
+        T* yrow = (T*)a.y + m * (uint64_t)N;
+#pragma unroll
+        for (int b = 0; b < kLinNB / 16; ++b) {
+            if (b >= ntiles) continue;
+            const int n = n0 + 16 * b + 4 * q;
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = acc[b][i] + bias[b][i];
+            if (vec_store && n + 3 < N) {
+                store<T, 4 * EB>(yrow + n, v);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (n + i < N) store<T, EB>(yrow + n + i, &v[i]);
+            }
+        }
+    };
+    // the 16-wide steps past the full chunks, then a guarded partial step
+    // when K is not a multiple of 16
+    auto rest = [&](uint32_t mtile, lin_f4* acc) {
+        const uint64_t row = (uint64_t)mtile * 16u + (uint32_t)r16;
+        const T* xrow = X + (row < a.M ? row : a.M - 1) * (uint64_t)K;
+        for (int k0 = nc * 64; k0 < kfull; k0 += 16) {
+            const LinFrag<T> xb = lin_load<T>(xrow + k0 + 4 * q);
+#pragma unroll
+            for (int b = 0; b < kLinNB / 16; ++b)
+                acc[b] = lin_mfma<T>(lin_load<T>(wl + (16 * b + r16) * S + k0 + 4 * q), xb, acc[b]);
+        }
+        if (kfull < K) {
+            const int kk = kfull + 4 * q;
+            const bool in = kk < K;
+            const LinFrag<T> xb = in ? lin_load<T>(xrow + kk) : lin_zero<T>();
 #pragma unroll
             for (int b = 0; b < kLinNB / 16; ++b) {
-                if (b >= ntiles) continue;
-                const int n = n0 + 16 * b + 4 * q;
-                float v[4];
+                const LinFrag<T> wa = in ? lin_load<T>(wl + (16 * b + r16) * S + kk) : lin_zero<T>();
+                acc[b] = lin_mfma<T>(wa, xb, acc[b]);
+            }
+        }
+    };
+
+    const uint32_t first = blockIdx.x * 4u + (uint32_t)wave;
+    const uint32_t my_tiles = first < a.m_tiles ? (a.m_tiles - first + stride - 1) / stride : 0u;
+    lin_f4 acc[kLinNB / 16];
+    if (nc == 0) {
+        // K < 64: no full chunk to stream
+        for (uint32_t i = 0; i < my_tiles; ++i) {
+            const uint32_t mtile = first + i * stride;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = acc[b][i] + bias[b][i];
-                if (vec_store && n + 3 < N) {
-                    store<T, 4 * EB>(yrow + n, v);
-                } else {
+            for (int b = 0; b < kLinNB / 16; ++b) acc[b] = lin_f4{0.f, 0.f, 0.f, 0.f};
+            rest(mtile, acc);
+            finish(mtile, acc);
+        }
+        return;
+    }
+    const uint32_t nchunks = my_tiles * (uint32_t)nc;
+    if constexpr (EB == 2) {
+        // The full chunks of this wave's tiles form one stream: chunk s+1 is
+        // read from memory into registers while chunk s multiplies out of
+        // the LDS buffer.  Every branch is uniform per wave; the buffer is
+        // the wave's own, and its LDS accesses complete in order, so no
+        // barrier is needed.
+        auto step = [&](uint32_t s_) {
+            const uint32_t i = s_ / (uint32_t)nc;
+            const int c = (int)(s_ - i * (uint32_t)nc);
+            if (c == 0) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (n + i < N) store<T, EB>(yrow + n + i, &v[i]);
-                }
+                for (int b = 0; b < kLinNB / 16; ++b) acc[b] = lin_f4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const LinFrag<T> xb = lin_load<T>(xl + r16 * XS + 16 * u + 4 * q);
+#pragma unroll
+                for (int b = 0; b < kLinNB / 16; ++b)
+                    acc[b] = lin_mfma<T>(lin_load<T>(wl + (16 * b + r16) * S + c * 64 + 16 * u + 4 * q), xb,
+                                         acc[b]);
+            }
+            if (c == nc - 1) {
+                const uint32_t mtile = first + i * stride;
+                rest(mtile, acc);
+                finish(mtile, acc);
+            }
+        };
+        uint4 raw[NI];
+        if (nchunks > 0) load_chunk(first, 0, raw);
+        for (uint32_t s_ = 0; s_ < nchunks; ++s_) {
+            put_chunk(raw);
+            if (s_ + 1 < nchunks) {
+                const uint32_t i = (s_ + 1) / (uint32_t)nc;
+                load_chunk(first + i * stride, (int)(s_ + 1 - i * (uint32_t)nc), raw);
+            }
+            step(s_);
+        }
+    } else {
+        // binary32: a lane's four consecutive x elements are already one
+        // 16-byte read, so the operands come straight from memory, two chunks
+        // in two register sets (one streams in while the other multiplies)
+        auto direct_chunk = [&](uint32_t s_, LinFrag<T>* dst) {
+            const uint32_t i = s_ / (uint32_t)nc;
+            const uint64_t row = (uint64_t)(first + i * stride) * 16u + (uint32_t)r16;
+            const T* p = X + (row < a.M ? row : a.M - 1) * (uint64_t)K + (s_ - i * (uint32_t)nc) * 64 + 4 * q;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) dst[u] = lin_load<T>(p + 16 * u);
+        };
+        auto step = [&](uint32_t s_, const LinFrag<T>* xs) {
+            const uint32_t i = s_ / (uint32_t)nc;
+            const int c = (int)(s_ - i * (uint32_t)nc);
+            if (c == 0) {
+#pragma unroll
+                for (int b = 0; b < kLinNB / 16; ++b) acc[b] = lin_f4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int b = 0; b < kLinNB / 16; ++b)
+                    acc[b] = lin_mfma<T>(lin_load<T>(wl + (16 * b + r16) * S + c * 64 + 16 * u + 4 * q), xs[u],
+                                         acc[b]);
+            if (c == nc - 1) {
+                const uint32_t mtile = first + i * stride;
+                rest(mtile, acc);
+                finish(mtile, acc);
+            }
+        };
+        LinFrag<T> xa[4], xb[4];
+        if (nchunks > 0) direct_chunk(0, xa);
+        for (uint32_t s_ = 0; s_ < nchunks; s_ += 2) {
+            if (s_ + 1 < nchunks) direct_chunk(s_ + 1, xb);
+            step(s_, xa);
+            if (s_ + 1 < nchunks) {
+                if (s_ + 2 < nchunks) direct_chunk(s_ + 2, xa);
+                step(s_ + 1, xb);
             }
         }
     }

@@ -196,7 +196,7 @@ int dcn_center_gate_backward(const void* y, const void* v, const void* z, const 
  * products are exact), y is rounded once.  M >= 0 (M == 0 is a no-op),
  * N, K >= 1.  Returns DCN_OK, DCN_ERR_INVALID_ARG (bad size or dtype, a NULL
  * or misaligned pointer), DCN_ERR_UNSUPPORTED (K not a multiple of 4, x, w
- * or y not 16-byte aligned, or K > 636 in binary32 / 1276 in half
+ * or y not 16-byte aligned, or K > 636 in binary32 / 1208 in half
  * precision, whose 64 rows of w would not fit in on-chip memory) or
  * DCN_ERR_HIP.  A caller falls back to another GEMM on DCN_ERR_UNSUPPORTED. */
 int dcn_linear_forward(const void* x, const void* w, const void* bias, void* y, long long M, int N, int K,

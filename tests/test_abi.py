@@ -186,7 +186,7 @@ def test_linear_validation():
     assert lin(M=0, x=0, w=0, y=0) == OK
     assert lin(K=6) == UNSUPPORTED                              # K not a multiple of 4
     assert lin(x=0x1004) == UNSUPPORTED                         # not 16-byte aligned
-    assert lin(K=640) == UNSUPPORTED and lin(K=1280, dtype=1) == UNSUPPORTED   # w rows exceed on-chip memory
+    assert lin(K=640) == UNSUPPORTED and lin(K=1212, dtype=1) == UNSUPPORTED   # w rows exceed on-chip memory
 
 
 def test_layer_rejects_grid_changing_geometry():
