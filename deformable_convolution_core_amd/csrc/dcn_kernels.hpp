@@ -169,12 +169,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t image_rsrc(const void* base, u
                                              0x00020000);
 }
 
-// Buffer resource over one image of offset records, based on the dword
-// boundary at or below the image start; lead (0 or 2) is the byte distance
-// from that boundary to the image.  A packed half-precision record of odd P
-// can start an image on a 2-byte boundary, and load_record's realignment
-// needs byte offsets that are true to the address's alignment.  Reading back
-// to the boundary stays inside the word that holds the image's first byte.
+// Buffer resource over one image of offset or mask records, based on the
+// dword boundary at or below the image start; lead (0 or 2) is the byte
+// distance from that boundary to the image.  Half-precision records can start
+// on a 2-byte boundary (a mask record of odd P, a packed record of odd P, an
+// image after an odd number of them), and load_record's realignment needs
+// byte offsets that are true to the address's alignment.  Reading back to the
+// boundary stays inside the word that holds the image's first byte.
 struct RecordRsrc {
     __amdgpu_buffer_rsrc_t r;
     uint32_t lead;
@@ -182,8 +183,10 @@ struct RecordRsrc {
 
 __device__ __forceinline__ RecordRsrc record_rsrc(const void* img, uint32_t bytes)
 {
+    // the range ends on a dword boundary too: a dword holding the image's
+    // last bytes is read whole
     const uint32_t lead = (uint32_t)(uintptr_t)img & 3u;
-    return RecordRsrc{image_rsrc((const char*)img - lead, bytes + lead), lead};
+    return RecordRsrc{image_rsrc((const char*)img - lead, (bytes + lead + 3u) & ~3u), lead};
 }
 
 // The hardware hands workgroup b to XCD (b mod 8).  Renumber so each XCD gets
@@ -545,8 +548,30 @@ __device__ __forceinline__ void load_record(PointRecord<T, PK>& rec, __amdgpu_bu
 #pragma unroll
         for (; j < PK; ++j) rec.mask[j] = __builtin_amdgcn_raw_buffer_load_b32(rmk, vmk, j * 4, 0);
     } else {
+        // PK half values from a 2-byte boundary: read the dwords that hold
+        // them (from the dword boundary at or below, so byte offsets must be
+        // true to the address's alignment, see record_rsrc) and shift each
+        // dword pair down by the misalignment.  Every dword read holds a byte
+        // of the record, except the last one of an even PK on a dword
+        // boundary, which is then not read.
+        constexpr int MW = PK / 2 + 1;
+        const uint32_t mb = vmk & ~3u, msh = (vmk & 2u) * 8u;
+        uint32_t md[MW];
+        int k = 0;
 #pragma unroll
-        for (int j = 0; j < PK; ++j) rec.mask[j] = __builtin_amdgcn_raw_buffer_load_b16(rmk, vmk, j * 2, 0);
+        for (; k + 4 <= MW - 1; k += 4) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rmk, mb, k * 4, 0);
+            md[k] = v[0]; md[k + 1] = v[1]; md[k + 2] = v[2]; md[k + 3] = v[3];
+        }
+#pragma unroll
+        for (; k < MW - 1; ++k) md[k] = __builtin_amdgcn_raw_buffer_load_b32(rmk, mb, k * 4, 0);
+        if constexpr (PK % 2 == 1) md[MW - 1] = __builtin_amdgcn_raw_buffer_load_b32(rmk, mb, (MW - 1) * 4, 0);
+        else md[MW - 1] = msh ? __builtin_amdgcn_raw_buffer_load_b32(rmk, mb, (MW - 1) * 4, 0) : 0u;
+#pragma unroll
+        for (int j = 0; j < PK; ++j) {
+            const uint32_t w = __builtin_amdgcn_alignbit(md[j / 2 + 1], md[j / 2], msh);
+            rec.mask[j] = (j & 1) ? (w >> 16) : (w & 0xffffu);
+        }
     }
 }
 
@@ -827,11 +852,12 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
     const RecordRsrc ro =
         record_rsrc((const char*)a.offset + (size_t)cur.n * tg.off_image_bytes, tg.off_image_bytes);
     const __amdgpu_buffer_rsrc_t roff = ro.r;
-    const __amdgpu_buffer_rsrc_t rmk =
-        image_rsrc((const char*)a.mask + (size_t)cur.n * tg.mask_image_bytes, tg.mask_image_bytes);
+    const RecordRsrc rm =
+        record_rsrc((const char*)a.mask + (size_t)cur.n * tg.mask_image_bytes, tg.mask_image_bytes);
+    const __amdgpu_buffer_rsrc_t rmk = rm.r;
     const uint32_t voff = pg_img * (uint32_t)(G.off_stride * EB) + ro.lead;
     const bool odd = EB == 2 && (G.off_stride & 1);   // records on 2-byte boundaries
-    const uint32_t vmk = pg_img * (uint32_t)(G.mask_stride * EB);
+    const uint32_t vmk = pg_img * (uint32_t)(G.mask_stride * EB) + rm.lead;
     L.bx = (float)(wo * G.stride - G.pad + G.c0);
     L.by = (float)(ho * G.stride - G.pad + G.c0);
     L.x_lo = cur.x_lo;
@@ -1178,11 +1204,12 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
     const RecordRsrc ro =
         record_rsrc((const char*)a.offset + (size_t)cur.n * tg.off_image_bytes, tg.off_image_bytes);
     const __amdgpu_buffer_rsrc_t roff = ro.r;
-    const __amdgpu_buffer_rsrc_t rmk =
-        image_rsrc((const char*)a.mask + (size_t)cur.n * tg.mask_image_bytes, tg.mask_image_bytes);
+    const RecordRsrc rm =
+        record_rsrc((const char*)a.mask + (size_t)cur.n * tg.mask_image_bytes, tg.mask_image_bytes);
+    const __amdgpu_buffer_rsrc_t rmk = rm.r;
     const uint32_t voff = pg_img * (uint32_t)(G.off_stride * EB) + ro.lead;
     const bool odd = EB == 2 && (G.off_stride & 1);   // records on 2-byte boundaries
-    const uint32_t vmk = pg_img * (uint32_t)(G.mask_stride * EB);
+    const uint32_t vmk = pg_img * (uint32_t)(G.mask_stride * EB) + rm.lead;
     const int bxi = wo * G.stride - G.pad + G.c0, byi = ho * G.stride - G.pad + G.c0;
     L.bx = (float)bxi;
     L.by = (float)byi;
@@ -1474,8 +1501,8 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
     const RecordRsrc ro = record_rsrc((const char*)a.offset + (size_t)n * og.off_image_bytes, og.off_image_bytes);
     const __amdgpu_buffer_rsrc_t roff = ro.r;
     const bool odd = EB == 2 && (G.off_stride & 1);   // records on 2-byte boundaries
-    const __amdgpu_buffer_rsrc_t rmk =
-        image_rsrc((const char*)a.mask + (size_t)n * og.mask_image_bytes, og.mask_image_bytes);
+    const RecordRsrc rm = record_rsrc((const char*)a.mask + (size_t)n * og.mask_image_bytes, og.mask_image_bytes);
+    const __amdgpu_buffer_rsrc_t rmk = rm.r;
 
     // one sample point of output pixel (ho, wo): m*w*g of each near corner in the tile
     auto point = [&](int i, int j, int bxi, int byi, float2 d, float m, const float* go) {
@@ -1532,7 +1559,7 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
         if constexpr (KT > 0) {
             const uint32_t pg_img = ((uint32_t)ho * (uint32_t)G.Wo + (uint32_t)wo) * (uint32_t)G.groups + (uint32_t)g;
             load_record<T, KT * KT>(pd.rec, roff, pg_img * (uint32_t)(G.off_stride * EB) + ro.lead, rmk,
-                                    pg_img * (uint32_t)(G.mask_stride * EB), odd);
+                                    pg_img * (uint32_t)(G.mask_stride * EB) + rm.lead, odd);
         }
     };
     auto mval = [&](uint32_t raw) {
