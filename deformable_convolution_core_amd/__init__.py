@@ -38,8 +38,8 @@ _lib = None
 DCN_F32, DCN_F16, DCN_BF16 = 0, 1, 2
 _DTYPE = {torch.float32: DCN_F32, torch.float16: DCN_F16, torch.bfloat16: DCN_BF16}
 EXPORTED = ("dcn_core_out_size", "dcn_core_forward", "dcn_core_backward", "dcn_core_forward_ex",
-            "dcn_core_backward_ex", "dcn_center_gate_forward", "dcn_center_gate_backward",
-            "dcn_linear_forward", "dcn_status_string")
+            "dcn_core_backward_ex", "dcn_core_backward_workspace_size", "dcn_core_backward_ws",
+            "dcn_center_gate_forward", "dcn_center_gate_backward", "dcn_linear_forward", "dcn_status_string")
 FLAG_SOFTMAX, FLAG_REMOVE_CENTER, FLAG_PACKED = 1, 2, 4
 
 
@@ -74,6 +74,10 @@ def load_library(path: str | None = None):
     lib.dcn_core_backward_ex.argtypes = [vp] * 7 + [i] * 9 + [f, i, i, vp]
     lib.dcn_core_backward_ex.restype = i
     ll = ctypes.c_longlong
+    lib.dcn_core_backward_workspace_size.argtypes = [vp] * 3 + [i] * 9 + [f, i, i]
+    lib.dcn_core_backward_workspace_size.restype = ll
+    lib.dcn_core_backward_ws.argtypes = [vp] * 7 + [i] * 9 + [f, i, i, vp, ll, vp]
+    lib.dcn_core_backward_ws.restype = i
     lib.dcn_center_gate_forward.argtypes = [vp] * 4 + [ll, i, i, i, vp]
     lib.dcn_center_gate_forward.restype = i
     lib.dcn_center_gate_backward.argtypes = [vp] * 7 + [ll, i, i, i, vp]
@@ -186,12 +190,20 @@ def _backward(input, offset, mask, grad_output, kernel_size, stride, pad, dilati
     goff = torch.empty_like(offset)
     gm = None if mask is None else torch.empty_like(mask)
     flags = _flags(softmax, remove_center, mask is None)
+    lib = load_library()
+    geo = (N, H, W, group, Cg, kernel_size, stride, pad, dilation, float(offset_scale), flags, _DTYPE[input.dtype])
+    # half precision outside the tiled shapes accumulates grad_input in a
+    # binary32 workspace, allocated here only when the library asks for one
+    need = lib.dcn_core_backward_workspace_size(_ptr(input), _ptr(grad_output), _ptr(gi), *geo)
+    if need < 0:
+        _check(int(-need), "dcn_core_backward_workspace_size")
+    ws = torch.empty((need + 3) // 4, dtype=torch.float32, device=input.device) if need > 0 else None
     with torch.cuda.device(input.device):
-        rc = load_library().dcn_core_backward_ex(
+        rc = lib.dcn_core_backward_ws(
             _ptr(input), _ptr(offset), None if mask is None else _ptr(mask), _ptr(grad_output), _ptr(gi),
-            _ptr(goff), None if gm is None else _ptr(gm), N, H, W, group, Cg, kernel_size, stride, pad,
-            dilation, float(offset_scale), flags, _DTYPE[input.dtype], _stream(input.device))
-    _check(rc, "dcn_core_backward_ex")
+            _ptr(goff), None if gm is None else _ptr(gm), *geo, None if ws is None else _ptr(ws),
+            0 if ws is None else ws.numel() * 4, _stream(input.device))
+    _check(rc, "dcn_core_backward_ws")
     return gi, goff, gm
 
 

@@ -410,6 +410,71 @@ int backward_half(BwdArgs a, const Call& c, hipStream_t st)
     return backward_grad_tiled<T>(a, c, tp, st);
 }
 
+// Whether the tiled half-precision kernels take this call (both planners
+// accept it); otherwise a half-precision backward needs the workspace path.
+bool half_tiled_ok(const Call& c, const void* input, const void* gout, const void* gin)
+{
+    OwnerPlan op;
+    TilePlan tp;
+    return plan_owner(c, gout, gin, op) && plan_tiles(c, input, gout, tp, 1, 160 * 1024);
+}
+
+int zero_fill(float* p, int64_t n, hipStream_t st);
+
+// Half-precision backward on any shape whose group splits into a power of
+// two of lanes: binary32 atomics into the zeroed workspace, then one
+// rounding into grad_input.
+template <typename T>
+int backward_generic(const BwdArgs& base, const Call& c, float* ws, hipStream_t st)
+{
+    const int eb = (int)sizeof(T);
+    int lb = 0, L = 0;
+    for (int cand = 16; cand >= eb; cand >>= 1) {
+        const int cpl = cand / eb;
+        if (c.Cg % cpl) continue;
+        const int l = c.Cg / cpl;
+        if (!(l > 0 && (l & (l - 1)) == 0 && l <= 64)) continue;
+        if (!aligned(base.input, (uintptr_t)cand) || !aligned(base.grad_out, (uintptr_t)eb)) continue;
+        lb = cand;
+        L = l;
+        break;
+    }
+    if (lb == 0) return DCN_ERR_UNSUPPORTED;
+    const int64_t n = (int64_t)c.N * c.H * c.W * c.G * c.Cg;
+    int rc = zero_fill(ws, n, st);
+    if (rc != DCN_OK) return rc;
+    BwdArgs a = base;
+    a.geo = make_geometry(c, lb / eb);
+    const uint64_t blocks = (uint64_t)c.N * a.geo.blocks_per_image;
+    if (blocks >= (1ll << 31)) return DCN_ERR_UNSUPPORTED;
+    const dim3 grid((uint32_t)blocks), blk(kBlock);
+    const bool k3 = c.k3();
+    switch (lb) {
+    case 16:
+        if (k3) hipLaunchKernelGGL((dcn_backward_generic<T, 16, 3>), grid, blk, 0, st, a, ws, L);
+        else hipLaunchKernelGGL((dcn_backward_generic<T, 16, 0>), grid, blk, 0, st, a, ws, L);
+        break;
+    case 8:
+        if (k3) hipLaunchKernelGGL((dcn_backward_generic<T, 8, 3>), grid, blk, 0, st, a, ws, L);
+        else hipLaunchKernelGGL((dcn_backward_generic<T, 8, 0>), grid, blk, 0, st, a, ws, L);
+        break;
+    case 4:
+        if (k3) hipLaunchKernelGGL((dcn_backward_generic<T, 4, 3>), grid, blk, 0, st, a, ws, L);
+        else hipLaunchKernelGGL((dcn_backward_generic<T, 4, 0>), grid, blk, 0, st, a, ws, L);
+        break;
+    default:
+        if (k3) hipLaunchKernelGGL((dcn_backward_generic<T, 2, 3>), grid, blk, 0, st, a, ws, L);
+        else hipLaunchKernelGGL((dcn_backward_generic<T, 2, 0>), grid, blk, 0, st, a, ws, L);
+        break;
+    }
+    rc = launch_status();
+    if (rc != DCN_OK) return rc;
+    const int64_t sb = (n + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL(dcn_store_workspace<T>, dim3((uint32_t)(sb < 4096 ? sb : 4096)), blk, 0, st, (const float*)ws,
+                       (T*)a.grad_input, (size_t)n);
+    return launch_status();
+}
+
 template <int LB, int L>
 int backward_variant(const BwdArgs& base, const Call& c, hipStream_t st)
 {
@@ -521,7 +586,7 @@ int forward_call(const Call& c, const void* input, const void* offset, const voi
 
 int backward_call(const Call& c, const void* input, const void* offset_in, const void* mask_in,
                   const void* grad_output, void* grad_input, void* grad_offset_in, void* grad_mask_in,
-                  void* stream)
+                  void* stream, void* workspace = nullptr, long long workspace_bytes = 0)
 {
     const int N = c.N, H = c.H, W = c.W, G = c.G, Cg = c.Cg;
     if (N == 0) return DCN_OK;
@@ -541,8 +606,13 @@ int backward_call(const Call& c, const void* input, const void* offset_in, const
         a.input = input; a.offset = offset; a.mask = mask; a.grad_out = grad_output;
         a.grad_input = grad_input; a.grad_offset = grad_offset; a.grad_mask = grad_mask;
         a.near_m = -1;
-        return dtype == DCN_F16 ? backward_half<_Float16>(a, c, (hipStream_t)stream)
-                                : backward_half<__bf16>(a, c, (hipStream_t)stream);
+        hipStream_t st = (hipStream_t)stream;
+        if (half_tiled_ok(c, input, grad_output, grad_input))
+            return dtype == DCN_F16 ? backward_half<_Float16>(a, c, st) : backward_half<__bf16>(a, c, st);
+        if (!workspace) return DCN_ERR_UNSUPPORTED;
+        if (workspace_bytes < (long long)N * H * W * G * Cg * 4 || !aligned(workspace, 4)) return DCN_ERR_INVALID_ARG;
+        return dtype == DCN_F16 ? backward_generic<_Float16>(a, c, (float*)workspace, st)
+                                : backward_generic<__bf16>(a, c, (float*)workspace, st);
     }
     int LB, L;
     if (Cg % 4 == 0 && pow2(Cg / 4) && Cg / 4 <= 64 && aligned(input, 16) && aligned(grad_input, 16)) {
@@ -606,6 +676,32 @@ extern "C" int dcn_core_backward_ex(const void* input, const void* offset, const
     const int rc = validate_ex(c, N, H, W, G, Cg, K, stride, pad, dilation, offset_scale, flags, dtype);
     if (rc != DCN_OK) return rc;
     return backward_call(c, input, offset, mask, grad_output, grad_input, grad_offset, grad_mask, stream);
+}
+
+extern "C" long long dcn_core_backward_workspace_size(const void* input, const void* grad_output,
+                                                      const void* grad_input, int N, int H, int W, int G, int Cg,
+                                                      int K, int stride, int pad, int dilation, float offset_scale,
+                                                      int flags, int dtype)
+{
+    Call c;
+    const int rc = validate_ex(c, N, H, W, G, Cg, K, stride, pad, dilation, offset_scale, flags, dtype);
+    if (rc != DCN_OK) return -(long long)rc;
+    if (dtype == DCN_F32 || N == 0 || half_tiled_ok(c, input, grad_output, grad_input)) return 0;
+    return (long long)N * H * W * G * Cg * 4;
+}
+
+extern "C" int dcn_core_backward_ws(const void* input, const void* offset, const void* mask,
+                                    const void* grad_output, void* grad_input, void* grad_offset,
+                                    void* grad_mask, int N, int H, int W, int G, int Cg, int K, int stride,
+                                    int pad, int dilation, float offset_scale, int flags, int dtype,
+                                    void* workspace, long long workspace_bytes, void* stream)
+{
+    Call c;
+    const int rc = validate_ex(c, N, H, W, G, Cg, K, stride, pad, dilation, offset_scale, flags, dtype);
+    if (rc != DCN_OK) return rc;
+    if (workspace_bytes < 0) return DCN_ERR_INVALID_ARG;
+    return backward_call(c, input, offset, mask, grad_output, grad_input, grad_offset, grad_mask, stream,
+                         workspace, workspace_bytes);
 }
 
 extern "C" int dcn_core_backward(const void* input, const void* offset, const void* mask,

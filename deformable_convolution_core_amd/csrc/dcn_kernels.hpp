@@ -1638,6 +1638,124 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Half-precision backward for the shapes the tiled kernels do not take: the
+// lane mapping and arithmetic of dcn_backward_kernel (the binary32 fallback)
+// on half-precision tensors, with every grad_input contribution added by a
+// binary32 atomic into a caller's workspace (N*H*W*C floats, zeroed first)
+// that dcn_store_workspace then rounds once into grad_input.  L, the lanes of
+// one group (a power of two up to 64), is a runtime value here.
+__device__ __forceinline__ float group_sum_rt(float v, int L)
+{
+    for (int o = 1; o < L; o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+template <typename T, int LB, int KT>
+__global__ __launch_bounds__(kBlock) void dcn_backward_generic(BwdArgs a, float* ws, int L)
+{
+    constexpr int EB = Elem<T>::bytes;
+    constexpr int CPL = LB / EB;
+    const Geometry& G = a.geo;
+    const LaneWork lw = lane_work(G);
+    // inactive lanes (past the image) stay for the cross-lane sums but touch
+    // no memory; a group is always wholly active or wholly inactive
+    const bool act = lw.active;
+
+    const char* in_img = (const char*)a.input + (size_t)lw.n * G.in_image_bytes;
+    const __amdgpu_buffer_rsrc_t rin = image_rsrc(in_img, G.in_image_bytes);
+    const uint32_t chan_bytes = lw.cc * (CPL * EB);
+    const size_t pix_global = (size_t)lw.n * G.Ho * G.Wo + lw.pix;
+    const size_t pg = pix_global * G.groups + lw.g;
+    const T* off = (const T*)a.offset + pg * G.off_stride;
+    const T* mk = (const T*)a.mask + pg * G.mask_stride;
+    T* goff = (T*)a.grad_offset + pg * G.off_stride;
+    T* gmk = (T*)a.grad_mask + pg * G.mask_stride;
+    float* wimg = ws + (size_t)lw.n * (G.in_image_bytes / EB);
+    const int bxi = (int)lw.wo * G.stride - G.pad + G.c0;
+    const int byi = (int)lw.ho * G.stride - G.pad + G.c0;
+    const float bx = (float)bxi, by = (float)byi;
+    const bool leader = (lw.cc & (uint32_t)(L - 1)) == 0;
+
+    float go[CPL];
+    {
+        const T* gp = (const T*)a.grad_out + pix_global * G.C + lw.cc * CPL;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) go[c] = act ? ld1(gp + c) : 0.f;
+    }
+    float mx = 0.f, inv = 1.f;
+    if (G.softmax && act) {
+        mx = ld1(mk);
+        for (int p = 1; p < G.P; ++p) mx = fmaxf(mx, ld1(mk + p));
+        float sum = 0.f;
+        for (int p = 0; p < G.P; ++p) sum += __expf(ld1(mk + p) - mx);
+        inv = 1.0f / sum;
+    }
+    float dot = 0.f;   // sum_q m_q gm_q (softmax)
+
+    const int K = KT > 0 ? KT : G.K;
+    for (int i = 0; i < K; ++i)
+        for (int j = 0; j < K; ++j) {
+            const int p = point_of(G, i, j);
+            if (p < 0) continue;                                // (the same for every lane)
+            float m = 0.f;
+            float2 d = make_float2(__builtin_nanf(""), 0.f);   // inactive: never on the map
+            if (act) {
+                m = ld1(mk + p);
+                if (G.softmax) m = __expf(m - mx) * inv;
+                d = ld2(off + 2 * p);
+            }
+            const Sample s = make_sample(G, bx, by, i, j, d.x, d.y, chan_bytes);
+            const float hy = 1.0f - s.ly, hx = 1.0f - s.lx;
+            const float wb[4] = {hy * hx, hy * s.lx, s.ly * hx, s.ly * s.lx};
+            const float dwx[4] = {-hy, hy, -s.ly, s.ly};
+            const float dwy[4] = {-hx, -s.lx, hx, s.lx};
+            float gm = 0.f, gdx = 0.f, gdy = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float f[CPL];
+                gather<T, LB>(rin, s.off[k], f);
+                float sk = 0.f;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) sk = fmaf(go[c], f[c], sk);
+                gm = fmaf(wb[k], sk, gm);
+                gdx = fmaf(dwx[k], sk, gdx);
+                gdy = fmaf(dwy[k], sk, gdy);
+                if (s.v[k]) {
+                    const float mw = m * wb[k];
+                    float* dst = wimg + s.off[k] / EB;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) atomicAdd(dst + c, mw * go[c]);
+                }
+            }
+            gm = group_sum_rt(gm, L);
+            gdx = group_sum_rt(gdx, L);
+            gdy = group_sum_rt(gdy, L);
+            if (!s.inmap) { gm = 0.f; gdx = 0.f; gdy = 0.f; }
+            if (act && leader) {
+                store_pair<T>(goff + 2 * p, G.alpha * m * gdx, G.alpha * m * gdy);
+                store<T, EB>(gmk + p, &gm);
+            }
+            dot = fmaf(m, gm, dot);
+        }
+    if (G.softmax && act && leader) {
+        // second pass over the stored raw gm (rounded once to the dtype)
+        for (int p = 0; p < G.P; ++p) {
+            const float m = __expf(ld1(mk + p) - mx) * inv;
+            const float v = m * (ld1(gmk + p) - dot);
+            store<T, EB>(gmk + p, &v);
+        }
+    }
+}
+
+// grad_input = the binary32 workspace, rounded once to the dtype
+template <typename T>
+__global__ __launch_bounds__(kBlock) void dcn_store_workspace(const float* ws, T* gi, size_t n)
+{
+    const size_t stride = (size_t)gridDim.x * kBlock;
+    for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) store<T, Elem<T>::bytes>(gi + i, ws + i);
+}
+
 // Zero fill on the caller's stream (a kernel rather than a memset node, so
 // a caller may capture the call in a graph).
 __global__ __launch_bounds__(kBlock) void dcn_zero_kernel(float4* p, size_t n4, float* tail, int ntail)

@@ -112,7 +112,8 @@ int dcn_core_forward(const void* input, const void* offset, const void* mask, vo
  * them through half-precision atomic adds, one rounding each.  Half precision
  * needs group rows of 32, 64 or 128 bytes, channel rows a multiple of 128
  * bytes, 16-byte aligned input, grad_output and grad_input, stride <= 4 and
- * K <= 7; other half-precision calls return DCN_ERR_UNSUPPORTED. */
+ * K <= 7; other half-precision calls return DCN_ERR_UNSUPPORTED here and run in
+ * dcn_core_backward_ws with a workspace. */
 int dcn_core_backward(const void* input, const void* offset, const void* mask,
                       const void* grad_output, void* grad_input, void* grad_offset,
                       void* grad_mask, int N, int H, int W, int G, int Cg, int K, int stride,
@@ -158,6 +159,33 @@ int dcn_core_backward_ex(const void* input, const void* offset, const void* mask
                          void* grad_mask, int N, int H, int W, int G, int Cg, int K, int stride,
                          int pad, int dilation, float offset_scale, int flags, int dtype,
                          void* stream);
+
+/* Bytes of device workspace dcn_core_backward_ws needs for this call: 0 when
+ * the call runs without one (binary32, an empty batch, or half precision on
+ * the shapes dcn_core_backward takes), else N*H*W*G*Cg*4 (one binary32
+ * accumulator per grad_input element).  The pointers are the ones the call
+ * will use (only their alignment is read).  Returns minus a dcn_status for
+ * invalid arguments. */
+long long dcn_core_backward_workspace_size(const void* input, const void* grad_output, const void* grad_input,
+                                           int N, int H, int W, int G, int Cg, int K, int stride, int pad,
+                                           int dilation, float offset_scale, int flags, int dtype);
+
+/* dcn_core_backward_ex with a caller-owned device workspace (workspace_bytes
+ * of it, at least what dcn_core_backward_workspace_size returns, 4-byte
+ * aligned; NULL and 0 when none is needed).  It extends half-precision
+ * backward to every shape whose channels per group split into a power-of-two
+ * number of lanes: each grad_input contribution is added by a binary32 atomic
+ * into the zeroed workspace, which is then rounded once into grad_input (the
+ * workspace is overwritten; its contents after the call are unspecified).
+ * Other shapes behave as in dcn_core_backward_ex.  Returns
+ * DCN_ERR_INVALID_ARG for a workspace that is too small or misaligned,
+ * DCN_ERR_UNSUPPORTED if one is needed and none is given or if the group
+ * width does not split. */
+int dcn_core_backward_ws(const void* input, const void* offset, const void* mask,
+                         const void* grad_output, void* grad_input, void* grad_offset,
+                         void* grad_mask, int N, int H, int W, int G, int Cg, int K, int stride,
+                         int pad, int dilation, float offset_scale, int flags, int dtype,
+                         void* workspace, long long workspace_bytes, void* stream);
 
 /* Centre-feature gate of the DCNv4 layer ([FB] section 3: an optional sigmoid
  * gate blends the centre pixel's projected features with the sampling

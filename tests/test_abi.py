@@ -90,6 +90,23 @@ def test_forward_empty_batch_is_noop():
     assert fwd(lib, N=0, ptrs=(0, 0, 0, 0)) == OK
 
 
+def test_backward_workspace_entry_points():
+    lib = dcn.load_library()
+    vp = ctypes.c_void_p
+    p3 = [vp(0x1000), vp(0x2000), vp(0x3000)]
+    geo = (1, 8, 8, 2, 8, 3, 1, 1, 1, ctypes.c_float(1.0), 0)
+    assert lib.dcn_core_backward_workspace_size(*p3, *geo, 0) == 0            # binary32 needs none
+    assert lib.dcn_core_backward_workspace_size(*p3, *geo, 1) == 8 * 8 * 16 * 4   # C = 16 half: not tiled
+    assert lib.dcn_core_backward_workspace_size(*p3, 1, 8, 8, 2, 8, 0, 1, 1, 1, ctypes.c_float(1.0), 0, 1) == -1
+    ptrs = [vp(0x1000 * (i + 1)) for i in range(7)]
+    ws = vp(0x100000)
+    args = (1, 8, 8, 2, 8, 3, 1, 1, 1, ctypes.c_float(1.0), 0, 1)
+    assert lib.dcn_core_backward_ws(*ptrs, *args, ws, 8 * 8 * 16 * 4 - 4, None) == INVALID   # too small
+    assert lib.dcn_core_backward_ws(*ptrs, *args, vp(0x100002), 8 * 8 * 16 * 4, None) == INVALID   # misaligned
+    assert lib.dcn_core_backward_ws(*ptrs, *args, None, 0, None) == UNSUPPORTED   # needs one, none given
+    assert lib.dcn_core_backward_ws(*ptrs, *args, ws, -1, None) == INVALID
+
+
 def test_backward_validation():
     lib = dcn.load_library()
     # half precision needs the tiled shapes: C = 16 is not a multiple of 32

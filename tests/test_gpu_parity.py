@@ -410,14 +410,61 @@ def test_backward_half_precision(case):
     check_backward(w, far_roundings=far)
 
 
-def test_backward_half_unsupported_shape_raises():
-    """Half precision covers the tiled shapes only (C a multiple of 64 here)."""
+def test_backward_half_outside_the_tiled_shapes_needs_the_workspace():
+    """dcn_core_backward itself still declines a half-precision call outside
+    the tiled shapes (C = 16 here); the binding then runs it with a binary32
+    workspace (parity of that path: test_backward_half_generic)."""
+    import ctypes
     x = torch.randn(1, 8, 8, 16, device=DEV, dtype=torch.float16)
     off = torch.zeros(1, 8, 8, 2 * 9 * 2, device=DEV, dtype=torch.float16)
     m = torch.ones(1, 8, 8, 2 * 9, device=DEV, dtype=torch.float16)
     g = torch.ones(1, 8, 8, 16, device=DEV, dtype=torch.float16)
-    with pytest.raises(dcn.DCNError):
-        dcn.backward(x, off, m, g, group=2)
+    gi, goff, gm = torch.empty_like(x), torch.empty_like(off), torch.empty_like(m)
+    lib = dcn.load_library()
+    vp = ctypes.c_void_p
+    rc = lib.dcn_core_backward(*(vp(t.data_ptr()) for t in (x, off, m, g, gi, goff, gm)), 1, 8, 8, 2, 8, 3, 1, 1, 1,
+                               ctypes.c_float(1.0), 0, 1, None)
+    assert rc == 2
+    need = lib.dcn_core_backward_workspace_size(vp(x.data_ptr()), vp(g.data_ptr()), vp(gi.data_ptr()), 1, 8, 8, 2, 8,
+                                                3, 1, 1, 1, ctypes.c_float(1.0), 0, 1)
+    assert need == 1 * 8 * 8 * 16 * 4
+    gi2, _, _ = dcn.backward(x, off, m, g, group=2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(gi2.float()).all()
+
+
+# Half precision outside the tiled shapes: binary32 atomics into a workspace,
+# one rounding into grad_input (grad_mask of a softmax carries one more: the
+# raw gm is stored, then reread for the Jacobian).
+HALF_GENERIC = [  # name, N, H, W, G, Cg, K, stride, pad, dil, alpha, softmax, dtype
+    ("g_cg8_f16", 2, 13, 11, 2, 8, 3, 1, 1, 1, 1.0, False, "f16"),
+    ("g_cg4_bf16_softmax", 1, 12, 9, 3, 4, 3, 1, 1, 1, 0.9, True, "bf16"),
+    ("g_cg2_f16_k5", 1, 11, 10, 4, 2, 5, 1, 2, 1, 1.0, False, "f16"),
+    ("g_stride5_bf16", 1, 23, 21, 4, 16, 3, 5, 1, 1, 1.0, False, "bf16"),
+    ("g_k9_f16_softmax", 1, 14, 15, 2, 16, 9, 1, 4, 1, 1.0, True, "f16"),
+    ("g_cg1_bf16", 1, 7, 8, 8, 1, 3, 1, 1, 2, 1.3, False, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", HALF_GENERIC, ids=lambda c: c[0])
+def test_backward_half_generic(case):
+    name, N, H, W, G, Cg, K, s, p, d, a, sm, dt = case
+    Ho, Wo = oracle.out_size(H, K, s, p, d), oracle.out_size(W, K, s, p, d)
+    w = inputs.Workload(name=name, N=N, H=H, W=W, G=G, Cg=Cg, Ho=Ho, Wo=Wo, K=K, stride=s, pad=p, dilation=d,
+                        offset_scale=a, softmax=sm, dtype=dt, offset_sigma=2.0, mask_sigma=1.0 if sm else 0.5,
+                        seed_base=98000 + 13 * len(name), backward=True)
+    t = inputs.make(w, with_grad=True)
+    dd = {k: v.to(DEV) for k, v in t.items()}
+    gi, goff, gm = dcn.backward(dd["input"], dd["offset"], dd["mask"], dd["grad_out"], **cfg_of(w))
+    torch.cuda.synchronize()
+    r = oracle_bwd(t, w)
+    for key, got, S, n, extra in (("grad_input", gi, r["gi_abs"], r["gi_cnt"], 0),
+                                  ("grad_offset", goff, r["goff_abs"], 4 * Cg, 0),
+                                  ("grad_mask", gm, r["gmask_abs"], 4 * Cg * (w.P + 1) if sm else 4 * Cg,
+                                   1 if sm else 0)):
+        st = tolerance.compare(got.float().cpu().numpy().reshape(r[key].shape), r[key], S, n, dt,
+                               store_roundings=extra)
+        assert st["ok"], (name, key, st)
 
 
 def test_backward_repeat_within_tolerance_and_autograd():
