@@ -296,7 +296,15 @@ def layer_record(w, steps, warmup):
     lin_ms = graph_time(lambda: dcn.linear(xm, wv, bv, out=ym), steps, warmup)
     blas_ms = graph_time(lambda: torch.nn.functional.linear(xm, wv, bv), steps, warmup)
     lin_bytes = (2 * M * w.C + w.C * w.C + w.C) * w.elem_bytes
-    del layer, x, xi, gout, y, v, z, out, xm, ym
+    # the offset+mask projection's weight and bias gradients alone: this
+    # package's matrix-core reduction against the batched BLAS path
+    from deformable_convolution_core_amd.layer import weight_grad
+    O = layer.offset_mask.weight.shape[0]
+    gom = torch.randn(M, O, device="cuda", dtype=dt)
+    wg_ms = eager_time(lambda: dcn.linear_weight_grad(gom, xm), steps, warmup)
+    wg_blas_ms = eager_time(lambda: (weight_grad(gom, xm), gom.sum(0, dtype=torch.float32)), steps, warmup)
+    wg_bytes = M * (O + w.C) * w.elem_bytes
+    del layer, x, xi, gout, y, v, z, out, xm, ym, gom
     torch.cuda.empty_cache()
     return dict(workload=f"DCNv4 layer (value, offset+mask, gate, output projections + core) at {w.name}",
                 dtype=w.dtype, center_feature_scale=True, forward_us=round(fwd_ms * 1e3, 2),
@@ -308,7 +316,11 @@ def layer_record(w, steps, warmup):
                 value_projection=dict(shape=f"{M}x{w.C} @ {w.C}x{w.C}", us=round(lin_ms * 1e3, 3),
                                       GBps=round(lin_bytes / (lin_ms * 1e-3) / 1e9, 1),
                                       frac_hbm=round(lin_bytes / (lin_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                                      platform_blas_us=round(blas_ms * 1e3, 3)))
+                                      platform_blas_us=round(blas_ms * 1e3, 3)),
+                offset_mask_weight_grad=dict(shape=f"({M}x{O})^T @ {M}x{w.C}", us=round(wg_ms * 1e3, 3),
+                                             GBps=round(wg_bytes / (wg_ms * 1e-3) / 1e9, 1),
+                                             frac_hbm=round(wg_bytes / (wg_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                             batched_blas_us=round(wg_blas_ms * 1e3, 3)))
 
 
 def cpu_baseline(w):
@@ -456,7 +468,8 @@ def main():
         log(f"DCNv4 layer at c2: forward {lay['forward_us']} us, forward+backward {lay['forward_backward_us_eager']} us; "
             f"gate {lay['gate_kernel']['us']} us ({lay['gate_kernel']['GBps']} GB/s); value projection "
             f"{lay['value_projection']['us']} us ({lay['value_projection']['GBps']} GB/s, platform BLAS "
-            f"{lay['value_projection']['platform_blas_us']} us)")
+            f"{lay['value_projection']['platform_blas_us']} us); offset+mask weight gradient "
+            f"{lay['offset_mask_weight_grad']['us']} us (batched BLAS {lay['offset_mask_weight_grad']['batched_blas_us']} us)")
         fii = fii_t_sweep(max(5, args.steps // 20), 2)
         extra["fii_t_core_op"] = fii
         log(f"FlashInternImage-T core op: {fii['us_per_batch']} us per batch of {fii['batch']}, "

@@ -28,6 +28,7 @@ import torch
 
 __all__ = ["forward", "backward", "forward_packed", "backward_packed", "out_size", "dcn_core",
            "dcnv4_core", "center_gate_forward", "center_gate_backward", "center_gate", "linear",
+           "linear_weight_grad",
            "DCNCoreFunction", "DCNv4CoreFunction", "CenterGateFunction", "DCNError", "library_path",
            "load_library"]
 
@@ -39,7 +40,8 @@ DCN_F32, DCN_F16, DCN_BF16 = 0, 1, 2
 _DTYPE = {torch.float32: DCN_F32, torch.float16: DCN_F16, torch.bfloat16: DCN_BF16}
 EXPORTED = ("dcn_core_out_size", "dcn_core_forward", "dcn_core_backward", "dcn_core_forward_ex",
             "dcn_core_backward_ex", "dcn_core_backward_workspace_size", "dcn_core_backward_ws",
-            "dcn_center_gate_forward", "dcn_center_gate_backward", "dcn_linear_forward", "dcn_status_string")
+            "dcn_center_gate_forward", "dcn_center_gate_backward", "dcn_linear_forward", "dcn_linear_weight_grad", "dcn_linear_weight_grad_workspace_size",
+            "dcn_status_string")
 FLAG_SOFTMAX, FLAG_REMOVE_CENTER, FLAG_PACKED = 1, 2, 4
 
 
@@ -84,6 +86,10 @@ def load_library(path: str | None = None):
     lib.dcn_center_gate_backward.restype = i
     lib.dcn_linear_forward.argtypes = [vp] * 4 + [ll, i, i, i, vp]
     lib.dcn_linear_forward.restype = i
+    lib.dcn_linear_weight_grad.argtypes = [vp] * 4 + [ll, i, i, i, vp, ll, vp]
+    lib.dcn_linear_weight_grad.restype = i
+    lib.dcn_linear_weight_grad_workspace_size.argtypes = [ll, i, i]
+    lib.dcn_linear_weight_grad_workspace_size.restype = ll
     lib.dcn_status_string.argtypes = [i]
     lib.dcn_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -306,6 +312,35 @@ def linear(x, weight, bias=None, *, out=None) -> torch.Tensor:
                                                _ptr(out), M, N, K, _DTYPE[x.dtype], _stream(x.device))
     _check(rc, "dcn_linear_forward")
     return out
+
+
+def linear_weight_grad(g, x, *, bias: bool = True):
+    """Weight and bias gradients of y = x @ weight.T + bias on the matrix cores
+    (HIP): g (..., O) the gradient of y, x (..., I) the input.  Returns
+    (dw (O, I), db (O,) or None) in binary32; the sums over rows are
+    deterministic (fixed-order chunk partials, kept in a workspace allocated
+    here)."""
+    if g.shape[:-1] != x.shape[:-1]:
+        raise ValueError("g (..., O) and x (..., I) must share their leading dimensions")
+    _check_tensor("g", g, g)
+    _check_tensor("x", x, g)
+    if g.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {g.dtype}")
+    O, I = g.shape[-1], x.shape[-1]
+    M = g.numel() // O if O else 0
+    lib = load_library()
+    need = lib.dcn_linear_weight_grad_workspace_size(M, O, I)
+    if need < 0:
+        _check(int(-need), "dcn_linear_weight_grad_workspace_size")
+    dw = torch.empty(O, I, dtype=torch.float32, device=g.device)
+    db = torch.empty(O, dtype=torch.float32, device=g.device) if bias else None
+    ws = torch.empty((need + 3) // 4, dtype=torch.float32, device=g.device) if need > 0 else None
+    with torch.cuda.device(g.device):
+        rc = lib.dcn_linear_weight_grad(_ptr(g), _ptr(x), _ptr(dw), None if db is None else _ptr(db), M, O, I,
+                                        _DTYPE[g.dtype], None if ws is None else _ptr(ws),
+                                        0 if ws is None else ws.numel() * 4, _stream(g.device))
+    _check(rc, "dcn_linear_weight_grad")
+    return dw, db
 
 
 class CenterGateFunction(torch.autograd.Function):

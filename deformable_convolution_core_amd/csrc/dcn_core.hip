@@ -18,6 +18,7 @@
 #include "dcn_kernels.hpp"
 #include "dcn_gate.hpp"
 #include "dcn_linear.hpp"
+#include "dcn_wgrad.hpp"
 
 using namespace dcn;
 
@@ -860,5 +861,112 @@ extern "C" int dcn_linear_forward(const void* x, const void* w, const void* bias
         hipLaunchKernelGGL(dcn_linear_kernel<__bf16>, grid, dim3(kLinBlock), (uint32_t)lds, st, a);
         break;
     }
+    return launch_status();
+}
+
+#ifndef DCN_WG_BLOCKS
+#define DCN_WG_BLOCKS 512     // blocks of the weight-gradient kernel over all chunks
+#endif
+
+namespace {
+
+struct WgPlan {
+    uint64_t rows_per_chunk, nchunks;
+    int oblocks, iblocks, part_rows, part_ld;
+    uint64_t workspace_bytes;
+};
+
+// Chunks of a multiple of 64 rows, about DCN_WG_BLOCKS blocks in all.
+bool plan_wgrad(long long M, int O, int I, WgPlan& p)
+{
+    p.oblocks = (O + kWgOB - 1) / kWgOB;
+    p.iblocks = (I + kWgIB - 1) / kWgIB;
+    p.part_rows = p.oblocks * kWgOB;
+    p.part_ld = p.iblocks * kWgIB + 16;
+    const uint64_t per = (uint64_t)p.oblocks * (uint64_t)p.iblocks;
+    const uint64_t want = per >= DCN_WG_BLOCKS ? 1 : DCN_WG_BLOCKS / per;
+    const uint64_t m = M > 0 ? (uint64_t)M : 1;
+    const uint64_t rows = ((m + want - 1) / want + kWgRows - 1) / kWgRows * kWgRows;
+    p.rows_per_chunk = rows;
+    p.nchunks = (m + rows - 1) / rows;
+    p.workspace_bytes = p.nchunks * (uint64_t)p.part_rows * (uint64_t)p.part_ld * 4u;
+    return rows < (1ull << 31) && p.nchunks < (1ull << 31) && p.oblocks < 65536 && p.iblocks < 65536;
+}
+
+template <typename T, int VG>
+void launch_wgrad_x(int vx, dim3 grid, const WgArgs& a, hipStream_t st)
+{
+    if (vx == 16) hipLaunchKernelGGL((dcn_wgrad_kernel<T, VG, 16>), grid, dim3(kWgBlock), 0, st, a);
+    else if (vx == 8) hipLaunchKernelGGL((dcn_wgrad_kernel<T, VG, 8>), grid, dim3(kWgBlock), 0, st, a);
+    else hipLaunchKernelGGL((dcn_wgrad_kernel<T, VG, 4>), grid, dim3(kWgBlock), 0, st, a);
+}
+
+// vg, vx: staging read widths of g and x (16, 8 or 4), both 0 for element reads
+template <typename T>
+void launch_wgrad(int vg, int vx, dim3 grid, const WgArgs& a, hipStream_t st)
+{
+    if (vg == 16) launch_wgrad_x<T, 16>(vx, grid, a, st);
+    else if (vg == 8) launch_wgrad_x<T, 8>(vx, grid, a, st);
+    else if (vg == 4) launch_wgrad_x<T, 4>(vx, grid, a, st);
+    else hipLaunchKernelGGL((dcn_wgrad_kernel<T, 0, 0>), grid, dim3(kWgBlock), 0, st, a);
+}
+
+}  // namespace
+
+extern "C" long long dcn_linear_weight_grad_workspace_size(long long M, int O, int I)
+{
+    if (M < 0 || O < 1 || I < 1) return -(long long)DCN_ERR_INVALID_ARG;
+    if (M == 0) return 0;
+    WgPlan p;
+    if (!plan_wgrad(M, O, I, p)) return -(long long)DCN_ERR_UNSUPPORTED;
+    return (long long)p.workspace_bytes;
+}
+
+extern "C" int dcn_linear_weight_grad(const void* g, const void* x, float* dw, float* db, long long M, int O, int I,
+                                      int dtype, void* workspace, long long workspace_bytes, void* stream)
+{
+    const int eb = elem_bytes(dtype);
+    if (eb == 0 || M < 0 || O < 1 || I < 1 || workspace_bytes < 0 || !dw) return DCN_ERR_INVALID_ARG;
+    if (!aligned(dw, 4) || (db && !aligned(db, 4))) return DCN_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    // staging offsets within 64 rows are 32-bit
+    if ((int64_t)O * I >= (1ll << 40) || (int64_t)(O > I ? O : I) * eb * kWgRows >= (1ll << 31))
+        return DCN_ERR_UNSUPPORTED;
+    if (M == 0) {
+        // sums over no rows
+        int rc = zero_fill(dw, (int64_t)O * I, st);
+        if (rc == DCN_OK && db) rc = zero_fill(db, O, st);
+        return rc;
+    }
+    if (!g || !x || !aligned(g, (uintptr_t)eb) || !aligned(x, (uintptr_t)eb)) return DCN_ERR_INVALID_ARG;
+    WgPlan p;
+    if (!plan_wgrad(M, O, I, p)) return DCN_ERR_UNSUPPORTED;
+    if (!workspace || !aligned(workspace, 16) || (uint64_t)workspace_bytes < p.workspace_bytes)
+        return DCN_ERR_INVALID_ARG;
+    // widest staging read that divides a row of g and of x and keeps every
+    // row start aligned (0: element reads)
+    auto vec = [&](const void* ptr, int n) {
+        if ((n * eb) % 16 == 0 && aligned(ptr, 16)) return 16;
+        if ((n * eb) % 8 == 0 && aligned(ptr, 8)) return 8;
+        if ((n * eb) % 4 == 0 && aligned(ptr, 4)) return 4;
+        return 0;
+    };
+    int vg = vec(g, O), vx = vec(x, I);
+    if (vg == 0 || vx == 0) vg = vx = 0;
+    WgArgs a{g, x, (float*)workspace, (uint64_t)M, O, I, (uint32_t)p.rows_per_chunk, p.part_rows, p.part_ld,
+             db ? 1 : 0};
+    const dim3 grid((uint32_t)p.nchunks, (uint32_t)p.oblocks, (uint32_t)p.iblocks);
+    switch (dtype) {
+    case DCN_F32: launch_wgrad<float>(vg, vx, grid, a, st); break;
+    case DCN_F16: launch_wgrad<_Float16>(vg, vx, grid, a, st); break;
+    default: launch_wgrad<__bf16>(vg, vx, grid, a, st); break;
+    }
+    int rc = launch_status();
+    if (rc != DCN_OK) return rc;
+    const int64_t groups = (int64_t)O * (p.part_ld / 4);
+    const uint64_t rb = (uint64_t)((groups + kWgRedCols - 1) / kWgRedCols);
+    if (rb >= (1ull << 31)) return DCN_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(dcn_wgrad_reduce, dim3((uint32_t)rb), dim3(kWgRedCols * kWgRedGroups), 0, st,
+                       (const float*)workspace, dw, db, O, I, p.part_rows, p.part_ld, (uint32_t)p.nchunks);
     return launch_status();
 }

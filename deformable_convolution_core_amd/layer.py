@@ -16,9 +16,11 @@ mask; the constructor's arguments follow the DCNv4 module of
 
 The four projections and their input gradients run in this package's
 matrix-core GEMM (`linear`: X read once, W in on-chip memory), falling back
-to the platform BLAS for shapes it does not take; their weight gradients
-are one batched BLAS GEMM over row chunks (weight_grad).  The sampling core
-and the gate run in this package's HIP kernels.  Input and output are channels-last (N, H, W, C).  The
+to the platform BLAS for shapes it does not take; their weight and bias
+gradients run in the package's split-row matrix-core reduction
+(`linear_weight_grad`), with a batched BLAS GEMM over row chunks
+(weight_grad) as the fallback.  The sampling core and the gate run in this
+package's HIP kernels.  Input and output are channels-last (N, H, W, C).  The
 offsets are predicted per input pixel, so the layer keeps the grid: stride
 1 and pad = dilation * (K - 1) / 2 with an odd K.
 """
@@ -27,7 +29,7 @@ from __future__ import annotations
 import torch
 import torch.nn.functional as F
 
-from . import DCNError, center_gate, dcnv4_core, linear, points
+from . import DCNError, center_gate, dcnv4_core, linear, linear_weight_grad, points
 
 
 _WGRAD_ROWS = 2048   # rows per chunk of the weight-gradient reduction
@@ -73,7 +75,7 @@ def _matmul_t(x, W, b=None):
 
 class _Projection(torch.autograd.Function):
     """x @ W.T + b; the input gradient g @ W as the same kernel on W.T, the
-    weight gradient by weight_grad."""
+    weight and bias gradients by _param_grads."""
 
     @staticmethod
     def forward(ctx, x, W, b):
@@ -85,9 +87,24 @@ class _Projection(torch.autograd.Function):
         x, W = ctx.saved_tensors
         g2 = g.reshape(-1, g.shape[-1]).contiguous()
         gx = _matmul_t(g2, W.t().contiguous()).view(x.shape) if ctx.needs_input_grad[0] else None
-        gW = weight_grad(g2, x.reshape(-1, x.shape[-1])) if ctx.needs_input_grad[1] else None
-        gb = g2.sum(0, dtype=torch.float32).to(g.dtype) if ctx.needs_input_grad[2] else None
+        gW, gb = _param_grads(g2, x.reshape(-1, x.shape[-1]), ctx.needs_input_grad[1], ctx.needs_input_grad[2])
         return gx, gW, gb
+
+
+def _param_grads(g2, x2, want_w, want_b):
+    """Weight and bias gradients of a projection in the weight's dtype: the
+    package's matrix-core reduction, or for shapes it does not take the
+    batched BLAS path (weight_grad) and a column sum."""
+    if not (want_w or want_b):
+        return None, None
+    try:
+        dw, db = linear_weight_grad(g2, x2, bias=want_b)
+    except DCNError as e:
+        if e.status != 2:        # only "unsupported shape" falls through
+            raise
+        dw = weight_grad(g2, x2) if want_w else None
+        db = g2.sum(0, dtype=torch.float32) if want_b else None
+    return (dw.to(g2.dtype) if want_w else None), (db.to(g2.dtype) if want_b else None)
 
 
 def project(x, lin: torch.nn.Linear):

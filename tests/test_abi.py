@@ -90,6 +90,29 @@ def test_forward_empty_batch_is_noop():
     assert fwd(lib, N=0, ptrs=(0, 0, 0, 0)) == OK
 
 
+def test_weight_grad_entry_points():
+    lib = dcn.load_library()
+    vp = ctypes.c_void_p
+    assert lib.dcn_linear_weight_grad_workspace_size(0, 8, 8) == 0
+    assert lib.dcn_linear_weight_grad_workspace_size(-1, 8, 8) == -INVALID
+    assert lib.dcn_linear_weight_grad_workspace_size(10, 0, 8) == -INVALID
+    # partials of every chunk: at least one 128 x (64 + 16) binary32 block, and
+    # more rows never need fewer chunks
+    small = lib.dcn_linear_weight_grad_workspace_size(64, 108, 64)
+    big = lib.dcn_linear_weight_grad_workspace_size(200704, 108, 64)
+    assert small >= 128 * 80 * 4 and big >= small and big % 16 == 0
+    p = [vp(0x10000), vp(0x20000), vp(0x30000), vp(0x40000)]
+    ws = vp(0x100000)
+    assert lib.dcn_linear_weight_grad(*p, 64, 8, 8, 7, ws, 1 << 20, None) == INVALID            # dtype
+    assert lib.dcn_linear_weight_grad(*p, -1, 8, 8, 0, ws, 1 << 20, None) == INVALID            # M
+    assert lib.dcn_linear_weight_grad(p[0], p[1], None, None, 64, 8, 8, 0, ws, 1 << 20, None) == INVALID
+    assert lib.dcn_linear_weight_grad(*p, 64, 8, 8, 0, None, 0, None) == INVALID               # no workspace
+    need = lib.dcn_linear_weight_grad_workspace_size(64, 8, 8)
+    assert lib.dcn_linear_weight_grad(*p, 64, 8, 8, 0, ws, need - 1, None) == INVALID          # too small
+    assert lib.dcn_linear_weight_grad(*p, 64, 8, 8, 0, vp(0x100008), need, None) == INVALID    # misaligned
+    assert lib.dcn_linear_weight_grad(vp(0x10001), p[1], p[2], p[3], 64, 8, 8, 1, ws, need, None) == INVALID
+
+
 def test_backward_workspace_entry_points():
     lib = dcn.load_library()
     vp = ctypes.c_void_p
