@@ -342,14 +342,14 @@ def cpu_baseline(w):
     per = el / reps
     cores = oracle.max_threads()
     return dict(value=round(w.min_bytes_forward() / per / 1e9, 3), unit="GB/s", cores=cores,
-                kind="oracle",
+                kind="oracle", cpu_model=cpu_model(),
                 sample=f"{reps} full batches of {w.name} (N={w.N}), binary64 C loops with OpenMP, "
                        f"{per * 1e3:.1f} ms per batch")
 
 
-def traffic_record(name, min_bytes):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    counters, if they were taken on the current kernel sources."""
+def _counters(name):
+    """The committed rocprofv3 counter record of a workload, if it was taken
+    on the current kernel sources."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     try:
@@ -358,8 +358,47 @@ def traffic_record(name, min_bytes):
         return None
     if d.get("kernel_hash") != kernel_hash():
         return None
-    e = d.get("workloads", {}).get(name)
+    return d.get("workloads", {}).get(name)
+
+
+def traffic_record(name, min_bytes):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counters, if they were taken on the current kernel sources."""
+    e = _counters(name)
     return None if e is None else e.get("hbm_bytes_per_launch")
+
+
+def counter_record(name):
+    """VALU busy, occupancy, LDS utilisation and L2 hit rate of the workload's
+    kernel from the same committed counters (None if stale or missing)."""
+    e = _counters(name)
+    if e is None:
+        return None
+    return {k: e.get(k) for k in ("valu_busy_pct", "occupancy_pct", "lds_util_pct", "l2_hit")}
+
+
+def copy_bandwidth(mb=1024, steps=20):
+    """A device-to-device copy of `mb` MB (read + write bytes over time): the
+    bandwidth a plain stream reaches on this GPU, beside the nameplate."""
+    n = mb * (1 << 20) // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    ms = graph_time(lambda: dst.copy_(src), steps, 3)
+    gbps = 2 * n * 4 / (ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(bytes_per_copy=2 * n * 4, us=round(ms * 1e3, 2), GBps=round(gbps, 1),
+                frac_hbm=round(gbps / HBM_PEAK_GBPS, 4))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def profile_mode(w, args):
@@ -418,8 +457,10 @@ def main():
     log(f"headline {w.name}: steps={args.steps} warmup={args.warmup}")
     head = forward_record(w, args.steps, args.warmup)
     log(f"headline {head['us']} us, {head['GBps']} GB/s")
+    cp = copy_bandwidth()
+    log(f"device-to-device copy {cp['GBps']} GB/s; headline at {head['GBps'] / cp['GBps']:.3f} of it")
 
-    extra = {}
+    extra = {"copy_bandwidth": cp, "frac_measured_copy": round(head["GBps"] / cp["GBps"], 4)}
     if not args.quick:
         sweep = []
         for name in inputs.BF16_SWEEP:
@@ -503,6 +544,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": head["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": head["frac_hbm"],
                      "traffic": traffic_record(w.name, head["min_bytes"])},
+        "counters": counter_record(w.name),
         "cpu_baseline": cpu,
         "kernel_hash": kernel_hash(),
     }

@@ -67,6 +67,18 @@ def test_traffic_counters_are_used_only_for_the_kernel_they_were_taken_on(tmp_pa
     assert bench.traffic_record("c2_dcnv4_f16_56", 1) is None
 
 
+def test_counter_record_follows_the_same_gate(tmp_path, monkeypatch):
+    f = tmp_path / "traffic.json"
+    rec = {"hbm_bytes_per_launch": 1, "valu_busy_pct": 50.0, "occupancy_pct": 30.0, "lds_util_pct": 20.0,
+           "l2_hit": 0.6}
+    json.dump({"kernel_hash": bench.kernel_hash(), "workloads": {"c2_dcnv4_f16_56": rec}}, open(f, "w"))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.counter_record("c2_dcnv4_f16_56") == {k: rec[k] for k in
+                                                       ("valu_busy_pct", "occupancy_pct", "lds_util_pct", "l2_hit")}
+    json.dump({"kernel_hash": "0" * 16, "workloads": {"c2_dcnv4_f16_56": rec}}, open(f, "w"))
+    assert bench.counter_record("c2_dcnv4_f16_56") is None
+
+
 def test_committed_counters_name_the_current_kernel_or_are_ignored():
     """Either the committed counters were taken on these kernel sources, or
     bench.py reports traffic as null (never a stale figure)."""

@@ -467,6 +467,27 @@ def test_backward_half_generic(case):
         assert st["ok"], (name, key, st)
 
 
+@pytest.mark.parametrize("shape", [(4, 16, "f32"), (4, 16, "f16"), (2, 8, "bf16"), (3, 8, "f32")],
+                         ids=["tiled_f32", "tiled_f16", "workspace_bf16", "untiled_f32"])
+def test_backward_of_far_inf_and_nan_offsets_is_zero(shape):
+    """Samples whose coordinates are far off the map, infinite or NaN are
+    skipped by the definition: every gradient is zero (no NaN leaks), on the
+    tiled, the half-precision workspace and the untiled paths."""
+    G, Cg, dt = shape
+    N, H, W = 1, 9, 10
+    T = inputs.DTYPES[dt]
+    x = inputs.normal((N, H, W, G * Cg), 31, 1.0, dt).to(DEV)
+    g = inputs.normal((N, H, W, G * Cg), 32, 1.0, dt).to(DEV)
+    m = inputs.normal((N, H, W, G * 9), 33, 1.0, dt).to(DEV)
+    for big in (1e4, -1e4, float("inf"), float("-inf"), float("nan")):
+        off = torch.full((N, H, W, G * 18), big, dtype=T, device=DEV)
+        for sm in (False, True):
+            gi, goff, gm = dcn.backward(x, off, m, g, group=G, softmax=sm)
+            torch.cuda.synchronize()
+            for name, t in (("grad_input", gi), ("grad_offset", goff), ("grad_mask", gm)):
+                assert torch.equal(t, torch.zeros_like(t)), (big, sm, name)
+
+
 def test_backward_repeat_within_tolerance_and_autograd():
     w = inputs.scaled(inputs.WORKLOADS["c5_dcnv4_f32_56_fwdbwd"], N=2)
     t = {k: v.to(DEV) for k, v in inputs.make(w, with_grad=True).items()}
