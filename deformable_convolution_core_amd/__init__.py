@@ -29,7 +29,8 @@ import torch
 __all__ = ["forward", "backward", "forward_packed", "backward_packed", "out_size", "dcn_core",
            "dcnv4_core", "center_gate_forward", "center_gate_backward", "center_gate", "linear",
            "linear_weight_grad",
-           "DCNCoreFunction", "DCNv4CoreFunction", "CenterGateFunction", "DCNError", "library_path",
+           "DCNCoreFunction", "DCNv4CoreFunction", "CenterGateFunction", "DCNv4GatedFunction",
+           "forward_packed_gated", "DCNError", "library_path",
            "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -41,6 +42,7 @@ _DTYPE = {torch.float32: DCN_F32, torch.float16: DCN_F16, torch.bfloat16: DCN_BF
 EXPORTED = ("dcn_core_out_size", "dcn_core_forward", "dcn_core_backward", "dcn_core_forward_ex",
             "dcn_core_backward_ex", "dcn_core_backward_workspace_size", "dcn_core_backward_ws",
             "dcn_center_gate_forward", "dcn_center_gate_backward", "dcn_linear_forward", "dcn_linear_weight_grad", "dcn_linear_weight_grad_workspace_size",
+            "dcn_core_forward_gated",
             "dcn_status_string")
 FLAG_SOFTMAX, FLAG_REMOVE_CENTER, FLAG_PACKED = 1, 2, 4
 
@@ -86,6 +88,8 @@ def load_library(path: str | None = None):
     lib.dcn_center_gate_backward.restype = i
     lib.dcn_linear_forward.argtypes = [vp] * 4 + [ll, i, i, i, vp]
     lib.dcn_linear_forward.restype = i
+    lib.dcn_core_forward_gated.argtypes = [vp] * 6 + [i] * 9 + [f, i, i, vp]
+    lib.dcn_core_forward_gated.restype = i
     lib.dcn_linear_weight_grad.argtypes = [vp] * 4 + [ll, i, i, i, vp, ll, vp]
     lib.dcn_linear_weight_grad.restype = i
     lib.dcn_linear_weight_grad_workspace_size.argtypes = [ll, i, i]
@@ -236,6 +240,31 @@ def forward_packed(input, offset_mask, *, kernel_size=3, stride=1, pad=1, dilati
     """Forward with DCNv4's single offset-and-mask tensor (N, Ho, Wo, G*3P)."""
     return _forward(input, offset_mask, None, kernel_size, stride, pad, dilation, offset_scale, softmax,
                     group, remove_center, out)
+
+
+def forward_packed_gated(input, offset_mask, gate_logits, *, kernel_size=3, dilation=1, offset_scale=1.0,
+                         group=1, remove_center=False, keep_core_output=False):
+    """DCNv4 forward (packed records, raw mask) with the layer's centre-feature
+    gate fused in: returns (output, core_output or None), output = y (1 - s) +
+    input s with s = sigmoid(gate_logits) per (pixel, group) and y the sampled
+    result (returned rounded to the dtype if keep_core_output).  Stride 1 and
+    pad = dilation (K - 1) / 2 with an odd K.  Raises DCNError with status
+    DCN_ERR_UNSUPPORTED (2) for shapes the fused kernel does not take."""
+    pad = dilation * (kernel_size - 1) // 2
+    N, H, W, C, Cg, Ho, Wo = _geometry(input, offset_mask, None, kernel_size, 1, pad, dilation, group,
+                                       remove_center)
+    if tuple(gate_logits.shape) != (N, Ho, Wo, group):
+        raise ValueError("gate_logits must be (N, H, W, group)")
+    _check_tensor("gate_logits", gate_logits, input)
+    out = torch.empty((N, Ho, Wo, C), dtype=input.dtype, device=input.device)
+    core = torch.empty_like(out) if keep_core_output else None
+    with torch.cuda.device(input.device):
+        rc = load_library().dcn_core_forward_gated(
+            _ptr(input), _ptr(offset_mask), None, _ptr(gate_logits), _ptr(out), None if core is None else _ptr(core),
+            N, H, W, group, Cg, kernel_size, 1, pad, dilation, float(offset_scale),
+            _flags(False, remove_center, True), _DTYPE[input.dtype], _stream(input.device))
+    _check(rc, "dcn_core_forward_gated")
+    return out, core
 
 
 def backward_packed(input, offset_mask, grad_output, *, kernel_size=3, stride=1, pad=1, dilation=1,
@@ -401,6 +430,30 @@ class DCNv4CoreFunction(torch.autograd.Function):
         input, offset_mask = ctx.saved_tensors
         gi, gom = backward_packed(input, offset_mask, grad_out.contiguous(), **ctx.cfg)
         return gi, gom, None, None, None, None, None, None, None
+
+
+class DCNv4GatedFunction(torch.autograd.Function):
+    """Autograd wrapper of the fused DCNv4 core + centre-feature gate.  The
+    backward is the gate's backward (on the saved pre-gate result) followed
+    by the core's, the two gradients of the input added."""
+
+    @staticmethod
+    def forward(ctx, input, offset_mask, gate_logits, kernel_size, dilation, offset_scale, group, remove_center):
+        ctx.cfg = dict(kernel_size=kernel_size, stride=1, pad=dilation * (kernel_size - 1) // 2,
+                       dilation=dilation, offset_scale=offset_scale, softmax=False, group=group,
+                       remove_center=remove_center)
+        out, core = forward_packed_gated(input, offset_mask, gate_logits, kernel_size=kernel_size,
+                                         dilation=dilation, offset_scale=offset_scale, group=group,
+                                         remove_center=remove_center, keep_core_output=True)
+        ctx.save_for_backward(input, offset_mask, gate_logits, core)
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        input, offset_mask, z, core = ctx.saved_tensors
+        gy, gv, gz = center_gate_backward(core, input, z, grad_out.contiguous(), group=ctx.cfg["group"])
+        gi, gom = backward_packed(input, offset_mask, gy, **ctx.cfg)
+        return gi + gv, gom, gz, None, None, None, None, None
 
 
 def dcn_core(input, offset, mask, kernel_size=3, stride=1, pad=1, dilation=1, offset_scale=1.0,

@@ -225,14 +225,14 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan, 
     return true;
 }
 
-template <typename T, int KT, int NT, bool SM>
+template <typename T, int KT, int NT, bool SM, bool GATE = false>
 int launch_tiled(const FwdArgs& a, const TilePlan& pl, hipStream_t st)
 {
     if (pl.tg.whole)
-        hipLaunchKernelGGL((dcn_forward_tiled<T, KT, NT, SM, true>), dim3((uint32_t)pl.blocks), dim3(NT), pl.lds_bytes,
-                           st, a, pl.tg);
+        hipLaunchKernelGGL((dcn_forward_tiled<T, KT, NT, SM, true, GATE>), dim3((uint32_t)pl.blocks), dim3(NT),
+                           pl.lds_bytes, st, a, pl.tg);
     else
-        hipLaunchKernelGGL((dcn_forward_tiled<T, KT, NT, SM, false>), dim3((uint32_t)pl.blocks), dim3(NT),
+        hipLaunchKernelGGL((dcn_forward_tiled<T, KT, NT, SM, false, GATE>), dim3((uint32_t)pl.blocks), dim3(NT),
                            pl.lds_bytes, st, a, pl.tg);
     return launch_status();
 }
@@ -248,6 +248,11 @@ int forward_tiled(const FwdArgs& base, const Call& c, const TilePlan& pl, hipStr
 {
     FwdArgs a = base;
     a.geo = make_geometry(c, 32 / (int)sizeof(T));
+    if (a.gate) {   // raw mask only (the caller checks)
+        if (pl.threads == 512)
+            return c.k3() ? launch_tiled<T, 3, 512, false, true>(a, pl, st) : launch_tiled<T, 0, 512, false, true>(a, pl, st);
+        return c.k3() ? launch_tiled<T, 3, 256, false, true>(a, pl, st) : launch_tiled<T, 0, 256, false, true>(a, pl, st);
+    }
     if (pl.threads == 512)
         return c.softmax ? forward_tiled_k<T, 512, true>(a, c, pl, st) : forward_tiled_k<T, 512, false>(a, c, pl, st);
     return c.softmax ? forward_tiled_k<T, 256, true>(a, c, pl, st) : forward_tiled_k<T, 256, false>(a, c, pl, st);
@@ -261,6 +266,7 @@ int forward_typed(const FwdArgs& a, const Call& c, hipStream_t st)
 {
     TilePlan pl;
     if (DCN_USE_TILES && plan_tiles(c, a.input, a.output, pl)) return forward_tiled<T>(a, c, pl, st);
+    if (a.gate) return DCN_ERR_UNSUPPORTED;   // the gate is fused into the tiled kernel only
     const int row = c.Cg * (int)sizeof(T);
     auto ok = [&](int lb) {
         return row % lb == 0 && aligned(a.input, lb) && aligned(a.output, lb);
@@ -569,7 +575,7 @@ int resolve_records(const Call& c, const void* offset, const void* mask, const v
 }
 
 int forward_call(const Call& c, const void* input, const void* offset, const void* mask, void* output,
-                 void* stream)
+                 void* stream, const void* gate = nullptr, void* core_out = nullptr)
 {
     if (c.N == 0) return DCN_OK;
     if (!input || !offset || !output) return DCN_ERR_INVALID_ARG;
@@ -577,6 +583,7 @@ int forward_call(const Call& c, const void* input, const void* offset, const voi
     const int rc = resolve_records(c, offset, mask, &a.offset, &a.mask);
     if (rc != DCN_OK) return rc;
     a.input = input; a.output = output;
+    a.gate = gate; a.core_out = core_out;
     hipStream_t st = (hipStream_t)stream;
     switch (c.dtype) {
     case DCN_F32: return forward_typed<float>(a, c, st);
@@ -653,6 +660,24 @@ extern "C" int dcn_core_forward_ex(const void* input, const void* offset, const 
     const int rc = validate_ex(c, N, H, W, G, Cg, K, stride, pad, dilation, offset_scale, flags, dtype);
     if (rc != DCN_OK) return rc;
     return forward_call(c, input, offset, mask, output, stream);
+}
+
+extern "C" int dcn_core_forward_gated(const void* input, const void* offset, const void* mask,
+                                      const void* gate_logits, void* output, void* core_output, int N, int H,
+                                      int W, int G, int Cg, int K, int stride, int pad, int dilation,
+                                      float offset_scale, int flags, int dtype, void* stream)
+{
+    Call c;
+    const int rc = validate_ex(c, N, H, W, G, Cg, K, stride, pad, dilation, offset_scale, flags, dtype);
+    if (rc != DCN_OK) return rc;
+    // the output pixel's own input pixel is the centre of its taps: odd K,
+    // stride 1, pad = dilation (K - 1) / 2; a raw mask
+    if (K % 2 == 0 || stride != 1 || pad != dilation * (K - 1) / 2 || c.softmax) return DCN_ERR_UNSUPPORTED;
+    if (N == 0) return DCN_OK;
+    if (!gate_logits || !aligned(gate_logits, (uintptr_t)c.ebytes) ||
+        (core_output && !aligned(core_output, 16)))
+        return DCN_ERR_INVALID_ARG;
+    return forward_call(c, input, offset, mask, output, stream, gate_logits, core_output);
 }
 
 extern "C" int dcn_core_forward(const void* input, const void* offset, const void* mask, void* output,

@@ -40,21 +40,8 @@ __device__ __forceinline__ void gate_load(const char* p, float* f)
     }
 }
 
-struct GateWeights {
-    float s, t, st;   // s, 1 - s, s * (1 - s)
-};
-
-__device__ __forceinline__ GateWeights gate_weights(float z)
-{
-    const float e = expf(-fabsf(z));
-    const float inv = 1.0f / (1.0f + e);
-    const float big = inv, small = e * inv;          // the larger and the smaller of s, 1 - s
-    GateWeights w;                                   // a NaN logit makes all three NaN
-    w.s = z >= 0.f ? big : small;
-    w.t = z >= 0.f ? small : big;
-    w.st = small * inv;
-    return w;
-}
+// (gate_weights, the s, 1 - s and s (1 - s) of a logit, is in dcn_kernels.hpp:
+// the tiled forward applies the same gate in its epilogue.)
 
 template <typename T, int VB>
 __global__ __launch_bounds__(kGateBlock) void dcn_gate_forward_kernel(const char* y, const char* v, const char* z,

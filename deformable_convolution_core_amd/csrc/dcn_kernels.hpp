@@ -229,7 +229,29 @@ struct FwdArgs {
     const void* mask;
     void* output;
     Geometry geo;
+    const void* gate;        // centre-feature gate logits (N, Ho, Wo, G), or null
+    void* core_out;          // with a gate: the sampled result before the gate, or null
 };
+
+// The centre-feature gate of the DCNv4 layer: s = 1 / (1 + exp(-z)) and 1 - s
+// from e = exp(-|z|) in (0, 1] as 1/(1+e) and e/(1+e) (swapped for z < 0), so
+// neither loses relative precision when the other approaches 1 and nothing
+// overflows; st = s (1 - s).  A NaN logit makes all three NaN.
+struct GateWeights {
+    float s, t, st;
+};
+
+__device__ __forceinline__ GateWeights gate_weights(float z)
+{
+    const float e = expf(-fabsf(z));
+    const float inv = 1.0f / (1.0f + e);
+    const float big = inv, small = e * inv;          // the larger and the smaller of s, 1 - s
+    GateWeights w;
+    w.s = z >= 0.f ? big : small;
+    w.t = z >= 0.f ? small : big;
+    w.st = small * inv;
+    return w;
+}
 
 struct BwdArgs {
     const void* input;
@@ -818,7 +840,11 @@ __device__ __forceinline__ void stage_rows(const Geometry& G, const TileGeo& tg,
 // LDS, then each lane accumulates 32 bytes of channels of one output pixel.
 // The lane's offset/mask record is requested before the wait for the region,
 // so the two memory latencies overlap.
-template <typename T, int KT, int NT, bool SOFTMAX, bool WHOLE>
+// GATE: the DCNv4 layer's centre-feature gate in the epilogue, out = y (1 - s)
+// + v s with y the sampled result, v the input at the output pixel itself (in
+// the staged region: stride 1, taps centred on the pixel) and s the sigmoid
+// of the (pixel, group)'s logit; y may also be stored before the gate.
+template <typename T, int KT, int NT, bool SOFTMAX, bool WHOLE, bool GATE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DCN_TILE_WAVES_PER_EU)))
 void dcn_forward_tiled(FwdArgs a, TileGeo tg)
 {
@@ -869,6 +895,11 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
     auto mval = [&](uint32_t raw) {
         return Elem<T>::bytes == 4 ? __uint_as_float(raw) : Elem<T>::widen(raw);
     };
+    float zval = 0.f;
+    if constexpr (GATE) {
+        // the gate logit, in flight with the record and the region
+        if (active) zval = ld1((const T*)a.gate + (size_t)cur.n * G.Ho * G.Wo * G.groups + pg_img);
+    }
     float acc[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
@@ -963,8 +994,31 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
 
     if (active) {
         // store the lane's 32 bytes, undoing the half swap
-        char* out = (char*)a.output + ((size_t)cur.n * G.Ho * G.Wo + (size_t)ho * G.Wo + wo) * G.C * EB +
-                    cur.slab * 128u + (uint32_t)sub * 32u;
+        const size_t at = ((size_t)cur.n * G.Ho * G.Wo + (size_t)ho * G.Wo + wo) * G.C * EB + cur.slab * 128u +
+                          (uint32_t)sub * 32u;
+        if constexpr (GATE) {
+            if (a.core_out) {
+                char* co = (char*)a.core_out + at;
+                store<T, 16>(co + swp * 16, &acc[0]);
+                store<T, 16>(co + (swp ^ 1) * 16, &acc[EPR]);
+            }
+            // the output pixel's own input row, read in the lane's order
+            const GateWeights gw = gate_weights(zval);
+            const uint32_t ac = ((uint32_t)(ho - L.y_lo) * L.RW + (uint32_t)(wo - L.x_lo)) * 128u + L.lane_first;
+            const uint4 v0 = *(const uint4*)(lds + ac);
+            const uint4 v1 = *(const uint4*)(lds + (ac ^ 16u));
+            const uint32_t cv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                if constexpr (EB == 4) {
+                    acc[c] = fmaf(gw.s, __uint_as_float(cv[c]), gw.t * acc[c]);
+                } else {
+                    acc[2 * c] = fmaf(gw.s, Elem<T>::widen(cv[c] & 0xffffu), gw.t * acc[2 * c]);
+                    acc[2 * c + 1] = fmaf(gw.s, Elem<T>::widen(cv[c] >> 16), gw.t * acc[2 * c + 1]);
+                }
+            }
+        }
+        char* out = (char*)a.output + at;
         store<T, 16>(out + swp * 16, &acc[0]);
         store<T, 16>(out + (swp ^ 1) * 16, &acc[EPR]);
     }

@@ -11,7 +11,9 @@ mask; the constructor's arguments follow the DCNv4 module of
                                              2P offsets then P raw mask values
     y   = core(v, om)                        HIP sampling core, packed layout
     y   = y * (1 - s) + v * s,  s = sigmoid(x @ Wc.T + bc)
-                                             optional centre-feature gate (HIP)
+                                             optional centre-feature gate (HIP,
+                                             fused into the core's epilogue
+                                             where the tiled kernel runs)
     out = y @ Wo.T + bo
 
 The four projections and their input gradients run in this package's
@@ -29,7 +31,8 @@ from __future__ import annotations
 import torch
 import torch.nn.functional as F
 
-from . import DCNError, center_gate, dcnv4_core, linear, linear_weight_grad, points
+from . import (DCNError, DCNv4GatedFunction, center_gate, dcnv4_core, forward_packed_gated, linear,
+               linear_weight_grad, points)
 
 
 _WGRAD_ROWS = 2048   # rows per chunk of the weight-gradient reduction
@@ -144,12 +147,32 @@ class DCNv4(torch.nn.Module):
         x = x.contiguous()
         v = project(x, self.value_proj)
         om = project(x, self.offset_mask)
-        y = dcnv4_core(v, om, self.kernel_size, 1, self.pad, self.dilation, self.offset_scale, self.group,
-                       self.remove_center)
         if self.center_feature_scale_proj is not None:
             z = project(x, self.center_feature_scale_proj)
-            y = center_gate(y, v, z, self.group)
+            y = self._gated_core(v, om, z)
+        else:
+            y = dcnv4_core(v, om, self.kernel_size, 1, self.pad, self.dilation, self.offset_scale, self.group,
+                           self.remove_center)
         return project(y, self.output_proj)
+
+    def _gated_core(self, v, om, z):
+        """The core with the centre-feature gate fused into its epilogue
+        (HIP), keeping the pre-gate result only when a backward will need
+        it; the core and the gate as two kernels for shapes the fused kernel
+        does not take."""
+        args = (self.kernel_size, self.dilation, self.offset_scale, self.group, self.remove_center)
+        try:
+            if torch.is_grad_enabled() and (v.requires_grad or om.requires_grad or z.requires_grad):
+                return DCNv4GatedFunction.apply(v, om, z, *args)
+            return forward_packed_gated(v, om, z, kernel_size=self.kernel_size, dilation=self.dilation,
+                                        offset_scale=self.offset_scale, group=self.group,
+                                        remove_center=self.remove_center)[0]
+        except DCNError as e:
+            if e.status != 2:        # only "unsupported shape" falls through
+                raise
+        y = dcnv4_core(v, om, self.kernel_size, 1, self.pad, self.dilation, self.offset_scale, self.group,
+                       self.remove_center)
+        return center_gate(y, v, z, self.group)
 
     def numpy_params(self) -> dict:
         """The parameters as float64 numpy arrays, keyed Wv, bv, Wom, bom, Wc, bc, Wo, bo."""

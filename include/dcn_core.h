@@ -187,6 +187,28 @@ int dcn_core_backward_ws(const void* input, const void* offset, const void* mask
                          int pad, int dilation, float offset_scale, int flags, int dtype,
                          void* workspace, long long workspace_bytes, void* stream);
 
+/* dcn_core_forward_ex followed by the DCNv4 layer's centre-feature gate
+ * (dcn_center_gate_forward) in one pass, for the layer's geometry: odd K,
+ * stride 1, pad = dilation * (K - 1) / 2 (so Ho = H, Wo = W and output
+ * pixel (h, w) is centred on input pixel (h, w)) and a raw mask
+ * (DCN_FLAG_SOFTMAX is DCN_ERR_UNSUPPORTED).  gate_logits is (N, H, W, G) in
+ * the dtype (2-byte aligned for half types); with y the sampled result and
+ * s = 1 / (1 + exp(-gate_logits[n, h, w, g])):
+ *
+ *   output[n, h, w, g*Cg + c] = y * (1 - s) + input[n, h, w, g*Cg + c] * s
+ *
+ * computed in binary32 from the unrounded y and rounded once.  core_output,
+ * if not NULL (16-byte aligned), receives y rounded to the dtype (what the
+ * gate's backward needs).  Only shapes the tiled kernel serves are taken
+ * (see dcn_core_backward for the tiled shapes); others return
+ * DCN_ERR_UNSUPPORTED, and a caller then runs dcn_core_forward_ex and
+ * dcn_center_gate_forward.  Other arguments and errors as
+ * dcn_core_forward_ex. */
+int dcn_core_forward_gated(const void* input, const void* offset, const void* mask, const void* gate_logits,
+                           void* output, void* core_output, int N, int H, int W, int G, int Cg, int K,
+                           int stride, int pad, int dilation, float offset_scale, int flags, int dtype,
+                           void* stream);
+
 /* Centre-feature gate of the DCNv4 layer ([FB] section 3: an optional sigmoid
  * gate blends the centre pixel's projected features with the sampling
  * result).  For M pixels of G groups of Cg channels:

@@ -90,6 +90,26 @@ def test_forward_empty_batch_is_noop():
     assert fwd(lib, N=0, ptrs=(0, 0, 0, 0)) == OK
 
 
+def test_gated_forward_validation():
+    lib = dcn.load_library()
+    vp = ctypes.c_void_p
+    p = [vp(0x10000 * (i + 1)) for i in range(6)]
+    geo = [1, 8, 8, 4, 16]
+    one = ctypes.c_float(1.0)
+    PK = 4                                                      # packed record flag
+    # K even, stride 2, pad off-centre, softmax: not the layer's geometry
+    assert lib.dcn_core_forward_gated(p[0], p[1], None, p[3], p[4], None, *geo, 4, 1, 1, 1, one, PK, 0, None) == UNSUPPORTED
+    assert lib.dcn_core_forward_gated(p[0], p[1], None, p[3], p[4], None, *geo, 3, 2, 1, 1, one, PK, 0, None) == UNSUPPORTED
+    assert lib.dcn_core_forward_gated(p[0], p[1], None, p[3], p[4], None, *geo, 3, 1, 0, 1, one, PK, 0, None) == UNSUPPORTED
+    assert lib.dcn_core_forward_gated(p[0], p[1], None, p[3], p[4], None, *geo, 3, 1, 1, 1, one, PK | 1, 0, None) == UNSUPPORTED
+    # no logits, misaligned logits or pre-gate output
+    assert lib.dcn_core_forward_gated(p[0], p[1], None, None, p[4], None, *geo, 3, 1, 1, 1, one, PK, 0, None) == INVALID
+    assert lib.dcn_core_forward_gated(p[0], p[1], None, vp(0x30001), p[4], None, *geo, 3, 1, 1, 1, one, PK, 1, None) == INVALID
+    assert lib.dcn_core_forward_gated(p[0], p[1], None, p[3], p[4], vp(0x50008), *geo, 3, 1, 1, 1, one, PK, 0, None) == INVALID
+    # an empty batch is a no-op
+    assert lib.dcn_core_forward_gated(None, None, None, None, None, None, 0, 8, 8, 4, 16, 3, 1, 1, 1, one, PK, 0, None) == OK
+
+
 def test_weight_grad_entry_points():
     lib = dcn.load_library()
     vp = ctypes.c_void_p

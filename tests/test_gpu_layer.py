@@ -101,6 +101,7 @@ LAYER = [  # N, H, W, G, Cg, K, remove_center, center_feature_scale, offset_scal
     (2, 14, 13, 4, 16, 3, False, True, 1.0),
     (1, 12, 12, 4, 16, 3, True, True, 0.8),
     (1, 11, 12, 2, 32, 5, False, True, 1.0),
+    (1, 9, 10, 3, 8, 3, False, True, 1.0),      # C = 24: not tiled, core and gate as two kernels
 ]
 
 
@@ -162,16 +163,16 @@ def test_layer_fp32_matches_oracle(case):
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_layer_half_stagewise(dt):
     """Half precision: the layer's output equals its stages composed by hand
-    (bit for bit), and the projections, the HIP core and the gate match the
-    float64 definitions on the layer's own intermediates."""
+    (bit for bit; the core and the gate as the one fused call the layer
+    makes), and the projections, the HIP core and the gate match the float64
+    definitions on the layer's own intermediates."""
     N, H, W, G, Cg, K = 2, 14, 14, 4, 16, 3
     layer, x, gout = make_layer(N, H, W, G, Cg, K, False, True, 1.0, dt, 6400)
     out = layer(x)
     v = dcn.linear(x, layer.value_proj.weight, layer.value_proj.bias)
     om = dcn.linear(x, layer.offset_mask.weight, layer.offset_mask.bias)
-    y = dcn.forward_packed(v, om, kernel_size=K, pad=1, group=G)
     z = dcn.linear(x, layer.center_feature_scale_proj.weight, layer.center_feature_scale_proj.bias)
-    yg = dcn.center_gate_forward(y, v, z, group=G)
+    yg, y = dcn.forward_packed_gated(v, om, z, kernel_size=K, group=G, keep_core_output=True)
     want = dcn.linear(yg, layer.output_proj.weight, layer.output_proj.bias)
     torch.cuda.synchronize()
     assert torch.equal(out, want)
@@ -189,10 +190,11 @@ def test_layer_half_stagewise(dt):
                             softmax=False, group=G)
     st = tolerance.compare(f64(y), ref, S, 4 * P, dt)
     assert st["ok"], ("core", st)
-    Y, V, Z = f64(y), f64(v), f64(z)
+    # the fused gate takes the unrounded y: against the gate of the oracle's y
+    V, Z = f64(v), f64(z)
     s, t = om_oracle.sigmoid(Z)[..., None], om_oracle.sigmoid(-Z)[..., None]
-    S_g = (np.abs(Y).reshape(N, H, W, G, Cg) * t + np.abs(V).reshape(N, H, W, G, Cg) * s).reshape(Y.shape)
-    st = tolerance.compare(f64(yg), om_oracle.gate_forward(Y, V, Z, G), S_g, 2, dt)
+    S_g = (S.reshape(N, H, W, G, Cg) * t + np.abs(V).reshape(N, H, W, G, Cg) * s).reshape(ref.shape)
+    st = tolerance.compare(f64(yg), om_oracle.gate_forward(ref, V, Z, G), S_g, 4 * P + 2, dt)
     assert st["ok"], ("gate", st)
     # the backward runs end to end in half precision
     xi = x.clone().requires_grad_(True)
