@@ -142,6 +142,13 @@ int forward_variant(const FwdArgs& base, const Call& c, hipStream_t st)
 #define DCN_TILE_FORCE_TH 0
 #endif
 constexpr int64_t kMaxTileLds = 96 * 1024;
+// The forward planner may take a region of all of LDS with as few as 4
+// resident waves per CU: measured on the stride-2 stage (c4 s2), a 154 KB
+// region with one block of 512 lanes per CU beats the direct gather by 1.5x
+// (larger regions overfetch less at stride 2); the stride-1 stages keep
+// their plans, which the cost model still prefers.
+constexpr int64_t kMaxFwdTileLds = 160 * 1024;
+constexpr int kMinFwdTileWaves = 4;
 
 struct TilePlan {
     TileGeo tg;
@@ -265,7 +272,8 @@ template <typename T>
 int forward_typed(const FwdArgs& a, const Call& c, hipStream_t st)
 {
     TilePlan pl;
-    if (DCN_USE_TILES && plan_tiles(c, a.input, a.output, pl)) return forward_tiled<T>(a, c, pl, st);
+    if (DCN_USE_TILES && plan_tiles(c, a.input, a.output, pl, kMinFwdTileWaves, kMaxFwdTileLds))
+        return forward_tiled<T>(a, c, pl, st);
     if (a.gate) return DCN_ERR_UNSUPPORTED;   // the gate is fused into the tiled kernel only
     const int row = c.Cg * (int)sizeof(T);
     auto ok = [&](int lb) {
