@@ -161,7 +161,9 @@ struct TilePlan {
 // and 128-byte slabs tile the channel row: Cg*b in {32, 64, 128}, C*b a
 // multiple of 128, 16-byte aligned input and output.  Among tile shapes with
 // at most 128 pixels it picks the cheapest by a simple cost model: lane slots
-// issued (idle lanes of ragged tiles count) plus region chunks staged.
+// issued (idle lanes of ragged tiles count, weighted up below 16 resident
+// waves per CU) plus region chunks staged.  min_waves and max_lds are the
+// caller's limits (the forward's are kMinFwdTileWaves and kMaxFwdTileLds).
 bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan, int min_waves = 12,
                 int64_t max_lds = kMaxTileLds)
 {
@@ -204,7 +206,7 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan, 
             // waves per CU the latency of the corner reads shows
             const int per_cu = (int)(160 * 1024 / lds) < 2048 / nt ? (int)(160 * 1024 / lds) : 2048 / nt;
             const int waves = per_cu * nt / 64;
-            if (waves < min_waves) continue;   // too few resident waves: the untiled kernel does better
+            if (waves < min_waves) continue;   // too few resident waves for this caller's kernel
             const double occ_penalty = waves >= 16 ? 1.0 : 16.0 / (double)waves;
             const double cost = (double)tiles * ((double)lanes * 900.0 * occ_penalty + (double)rh * rw * 8 * 3.0);
             if (best < 0 || cost < best) {
