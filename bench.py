@@ -28,6 +28,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import math
 import os
 import sys
@@ -53,10 +54,20 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_hash() -> str:
+def code_text(src: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed: what
+    the compiler sees, so a comment edit keeps the hash (string literals in
+    these sources hold no comment markers)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def kernel_hash(sources=None) -> str:
+    """First 16 hex digits of the sha256 of the kernel sources' code text."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        h.update(open(p, "rb").read())
+    for text in (sources if sources is not None else [open(p).read() for p in KERNEL_SOURCES]):
+        h.update(code_text(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -67,6 +67,13 @@ def test_traffic_counters_are_used_only_for_the_kernel_they_were_taken_on(tmp_pa
     assert bench.traffic_record("c2_dcnv4_f16_56", 1) is None
 
 
+def test_kernel_hash_ignores_comments_and_spacing_but_not_code():
+    a = "int f(int x) { return x + 1; }  // one\n"
+    b = "/* the same\n function */ int f(int x)\n{\n    return x + 1;   // more\n}\n"
+    c = "int f(int x) { return x + 2; }\n"
+    assert bench.kernel_hash([a]) == bench.kernel_hash([b]) != bench.kernel_hash([c])
+
+
 def test_counter_record_follows_the_same_gate(tmp_path, monkeypatch):
     f = tmp_path / "traffic.json"
     rec = {"hbm_bytes_per_launch": 1, "valu_busy_pct": 50.0, "occupancy_pct": 30.0, "lds_util_pct": 20.0,
