@@ -112,3 +112,49 @@ def test_gated_forward_and_weight_grad_replay():
     torch.cuda.synchronize()
     g, got = capture(wg)
     replay_and_check(g, got, want)
+
+
+def test_concurrent_threads_on_their_own_streams():
+    """The library keeps no state: two host threads, each on a stream of its
+    own (default priority), run forward and backward on different inputs at
+    the same time; every result equals the same call made alone."""
+    import threading
+    cases = []
+    for k in range(2):
+        w = inputs.Workload(name=f"thread{k}", N=2, H=24, W=22, G=4, Cg=16, Ho=24, Wo=22, dtype="f32",
+                            seed_base=88300 + 17 * k, backward=True)
+        cases.append({n: v.to(DEV) for n, v in inputs.make(w, with_grad=True).items()})
+    want = []
+    for t in cases:
+        out = dcn.forward(t["input"], t["offset"], t["mask"], group=4)
+        _, goff, gm = dcn.backward(t["input"], t["offset"], t["mask"], t["grad_out"], group=4)
+        want.append((out, goff, gm))
+    torch.cuda.synchronize()
+    got = [[] for _ in cases]
+    errors = []
+
+    def work(k):
+        try:
+            s = torch.cuda.Stream()
+            t = cases[k]
+            with torch.cuda.stream(s):
+                for _ in range(10):
+                    out = dcn.forward(t["input"], t["offset"], t["mask"], group=4)
+                    _, goff, gm = dcn.backward(t["input"], t["offset"], t["mask"], t["grad_out"], group=4)
+                    got[k].append((out, goff, gm))
+            s.synchronize()
+        except Exception as e:          # reported on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(len(cases))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for k in range(len(cases)):
+        assert len(got[k]) == 10
+        for res in got[k]:
+            for a, b in zip(res, want[k]):
+                assert torch.equal(a, b), k
