@@ -298,6 +298,15 @@ int forward_typed(const FwdArgs& a, const Call& c, hipStream_t st)
 #ifndef DCN_OWNER_REACH
 #define DCN_OWNER_REACH 4     // corners of offsets up to this many pixels are added by owners
 #endif
+#ifndef DCN_OWNER_FORCE_TW
+#define DCN_OWNER_FORCE_TW 0  // nonzero: the owner planner considers only this tile (tuning builds)
+#endif
+#ifndef DCN_OWNER_FORCE_TH
+#define DCN_OWNER_FORCE_TH 0
+#endif
+#ifndef DCN_OWNER_FORCE_NT
+#define DCN_OWNER_FORCE_NT 0
+#endif
 constexpr int64_t kMaxOwnerLds = 160 * 1024;
 
 struct OwnerPlan {
@@ -330,6 +339,9 @@ bool plan_owner(const Call& c, const void* gout, const void* gin, OwnerPlan& pl)
     for (int nt = 256; nt <= 1024; nt *= 2) {
         for (int tw = 1; tw <= 64 && tw <= c.W; ++tw)
             for (int th = 1; th <= 64 && th <= c.H; ++th) {
+                if (DCN_OWNER_FORCE_TW && (tw != DCN_OWNER_FORCE_TW || th != DCN_OWNER_FORCE_TH ||
+                                           nt != DCN_OWNER_FORCE_NT))
+                    continue;
                 const int64_t lds = (int64_t)th * tw * kOwnerStride * 4;
                 if (lds > kMaxOwnerLds) continue;
                 const int per_cu = (int)(160 * 1024 / lds) < 2048 / nt ? (int)(160 * 1024 / lds) : 2048 / nt;

@@ -1600,9 +1600,7 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
         uint32_t gw[2 * EB];                  // the lane's 8 upstream-gradient elements
         PointRecord<T, (KT > 0 ? KT * KT : 1)> rec;
     };
-    auto fetch = [&](int e, Pending& pd) {
-        const int eh = e / EW, ew = e - eh * EW;
-        const int ho = hlo + eh, wo = wlo + ew;
+    auto fetch = [&](int ho, int wo, Pending& pd) {
         const size_t pix = ((size_t)n * G.Ho + ho) * G.Wo + wo;
         const uint4* gp = (const uint4*)((const char*)a.grad_out + (pix * G.C + ch0) * EB);
 #pragma unroll
@@ -1620,14 +1618,27 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
         return EB == 4 ? __uint_as_float(raw) : Elem<T>::widen(raw);
     };
 
-    // The 16 pixel slots of a wave take pixels NT/64 apart, so that two
-    // lanes of one LDS instruction rarely add into the same address.
-    const int e0 = (((t & 63) >> 2) * (NT / 64)) + (t >> 6);
+    // Visit order: the rows of the visited window split into four phases
+    // (row mod 4); within a phase, column by column.  A wave's 16 pixel
+    // slots are consecutive in this order, so they share a column: the
+    // window's margin columns, whose samples rarely reach the tile, fill
+    // waves of their own that skip most corners together (mixing them into
+    // every wave cost 16% more time on the 56x56 fp32 stage).  The slots sit
+    // 4 rows apart, so two lanes of one LDS instruction rarely add into one
+    // address.
+    const int EH = E > 0 ? E / EW : 0;
+    int cum[5];
+    cum[0] = 0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) cum[p + 1] = cum[p] + EW * ((EH - p + 3) >> 2);
+    const int e0 = t >> 2;
     for (int e = e0; e < E; e += NT / 4) {
+        const int ph = (e >= cum[1]) + (e >= cum[2]) + (e >= cum[3]);   // cum[ph] <= e < cum[ph + 1]
+        const int cnt = (EH - ph + 3) >> 2, local = e - cum[ph];
+        const int col = local / cnt, k = local - col * cnt;
+        const int ho = hlo + ph + 4 * k, wo = wlo + col;
         Pending cur;
-        fetch(e, cur);
-        const int eh = e / EW, ew = e - eh * EW;
-        const int ho = hlo + eh, wo = wlo + ew;
+        fetch(ho, wo, cur);
         const int bxi = wo * G.stride - G.pad + G.c0, byi = ho * G.stride - G.pad + G.c0;
         float go[8];
 #pragma unroll
