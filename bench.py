@@ -271,7 +271,8 @@ def layer_record(w, steps, warmup):
     centre-feature gate: value and offset+mask projections (matrix-core
     GEMM), HIP core on the packed records, HIP gate, output projection.
     Random weights (no checkpoint).  Forward in a graph; forward + backward
-    eager (autograd).  Also the gate kernel and the value projection alone,
+    eager (autograd), and the same forward + backward captured in a graph.
+    Also the gate kernel and the value projection alone,
     against HBM (the projection also on the platform BLAS)."""
     from deformable_convolution_core_amd.layer import DCNv4
     dt = inputs.DTYPES[w.dtype]
@@ -292,6 +293,13 @@ def layer_record(w, steps, warmup):
         xi.grad = None
         layer(xi).backward(gout)
     fb_ms = eager_time(fwd_bwd, max(5, steps // 4), 3)
+    # the same step captured in a graph: its GPU time without the host's
+    # per-call autograd and launch work (the eager figure is bound by that)
+    fb_graph_ms, fb_graph_note = None, None
+    try:
+        fb_graph_ms = graph_time(fwd_bwd, max(5, steps // 4), 3)
+    except RuntimeError as e:
+        fb_graph_note = f"capture refused: {e}"[:200]
     # the gate alone: read y, v, z; write out
     M = w.N * w.H * w.W
     y = torch.randn(M, w.C, device="cuda", dtype=dt)
@@ -320,6 +328,8 @@ def layer_record(w, steps, warmup):
     return dict(workload=f"DCNv4 layer (value, offset+mask, gate, output projections + core) at {w.name}",
                 dtype=w.dtype, center_feature_scale=True, forward_us=round(fwd_ms * 1e3, 2),
                 forward_backward_us_eager=round(fb_ms * 1e3, 2),
+                forward_backward_us_graph=None if fb_graph_ms is None else round(fb_graph_ms * 1e3, 2),
+                **({} if fb_graph_note is None else {"forward_backward_graph_note": fb_graph_note}),
                 images_per_s_forward=round(w.N / (fwd_ms * 1e-3), 1),
                 gate_kernel=dict(us=round(gate_ms * 1e3, 3), min_bytes=gate_bytes,
                                  GBps=round(gate_bytes / (gate_ms * 1e-3) / 1e9, 1),
@@ -517,7 +527,8 @@ def main():
         extra["backward_half"] = halves
         lay = layer_record(inputs.WORKLOADS[inputs.HEADLINE], max(20, args.steps // 4), 5)
         extra["dcnv4_layer"] = lay
-        log(f"DCNv4 layer at c2: forward {lay['forward_us']} us, forward+backward {lay['forward_backward_us_eager']} us; "
+        log(f"DCNv4 layer at c2: forward {lay['forward_us']} us, forward+backward {lay['forward_backward_us_eager']} us "
+            f"eager, {lay['forward_backward_us_graph']} us in a graph; "
             f"gate {lay['gate_kernel']['us']} us ({lay['gate_kernel']['GBps']} GB/s); value projection "
             f"{lay['value_projection']['us']} us ({lay['value_projection']['GBps']} GB/s, platform BLAS "
             f"{lay['value_projection']['platform_blas_us']} us); offset+mask weight gradient "
