@@ -513,7 +513,7 @@ def main():
                                  min_bytes=w5.min_bytes_backward(),
                                  GBps=round(w5.min_bytes_backward() / (bms * 1e-3) / 1e9, 1),
                                  frac_hbm=round(w5.min_bytes_backward() / (bms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4))
-        log(f"backward c5: {extra['backward']['us']} us")
+        log(f"backward {w5.name} f32: {extra['backward']['us']} us")
         # the same shape in half precision (binary32 arithmetic, half storage)
         halves = []
         for dt in ("f16", "bf16"):
@@ -523,11 +523,11 @@ def main():
                                eager_us=round(heager * 1e3, 3), min_bytes=wh.min_bytes_backward(),
                                GBps=round(wh.min_bytes_backward() / (hms * 1e-3) / 1e9, 1),
                                frac_hbm=round(wh.min_bytes_backward() / (hms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)))
-            log(f"backward c5 {dt}: {halves[-1]['us']} us")
+            log(f"backward {w5.name} {dt}: {halves[-1]['us']} us")
         extra["backward_half"] = halves
         lay = layer_record(inputs.WORKLOADS[inputs.HEADLINE], max(20, args.steps // 4), 5)
         extra["dcnv4_layer"] = lay
-        log(f"DCNv4 layer at c2: forward {lay['forward_us']} us, forward+backward {lay['forward_backward_us_eager']} us "
+        log(f"DCNv4 layer at {inputs.HEADLINE}: forward {lay['forward_us']} us, forward+backward {lay['forward_backward_us_eager']} us "
             f"eager, {lay['forward_backward_us_graph']} us in a graph; "
             f"gate {lay['gate_kernel']['us']} us ({lay['gate_kernel']['GBps']} GB/s); value projection "
             f"{lay['value_projection']['us']} us ({lay['value_projection']['GBps']} GB/s, platform BLAS "
