@@ -1344,8 +1344,15 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
             const float gd[2] = {G.alpha * m * gdx, G.alpha * m * gdy};
             store_pair<T>(goff + 2 * q, gd[0], gd[1]);
         }
-        // corners beyond the owners' reach
-        if (active && pt.inmap) {
+        // corners beyond the owners' reach: x0 and x0 + 1 both lie within
+        // M of the base exactly when x0 - base + M is in [0, 2M) (likewise
+        // y), which one test per axis settles for all four corners
+        // (unsigned arithmetic: off-map samples carry saturated floors and
+        // are excluded below)
+        const uint32_t nm = (uint32_t)a.near_m;
+        const bool all_near = a.near_m >= 0 && (uint32_t)pt.x0 - (uint32_t)bxi + nm < M2 &&
+                              (uint32_t)pt.y0 - (uint32_t)byi + nm < M2;
+        if (active && pt.inmap && !all_near) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int qx = pt.x0 + (k & 1), qy = pt.y0 + (k >> 1);

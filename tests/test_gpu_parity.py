@@ -373,6 +373,11 @@ OWNER_SWEEP = [  # name, N, H, W, G, Cg, K, stride, pad, dil, alpha, softmax, si
     ("own_far_40", 1, 19, 21, 2, 16, 3, 1, 1, 1, 1.0, True, 40.0),
     ("own_cg64", 2, 11, 13, 2, 64, 3, 1, 1, 1, 1.0, False, 3.0),
     ("big_alpha_atomic", 1, 12, 12, 4, 8, 3, 1, 1, 1, 9.0, False, 1.0),
+    # visited windows of one to three rows (row phases left empty) and of one column
+    ("own_h1", 2, 1, 40, 4, 8, 3, 1, 1, 1, 1.0, False, 1.5),
+    ("own_h2", 1, 2, 33, 2, 16, 3, 1, 1, 1, 1.0, True, 1.5),
+    ("own_h3_s2", 1, 5, 30, 4, 8, 3, 2, 1, 1, 1.0, False, 1.5),
+    ("own_w1", 2, 29, 1, 4, 8, 3, 1, 1, 1, 1.0, False, 1.5),
 ]
 
 
