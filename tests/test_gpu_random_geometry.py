@@ -26,7 +26,7 @@ from tests import tolerance
 from tests.test_gpu_parity import DEV, cfg_of, oracle_bwd, oracle_fwd
 
 pytestmark = pytest.mark.gpu
-NCASES = 96
+NCASES = 160
 
 
 @pytest.fixture(autouse=True)
