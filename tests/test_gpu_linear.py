@@ -2,6 +2,7 @@
 DCNv4 layer, against the float64 product, element by element:
     |gpu - ref| <= rtol |ref| + (K + 32) 2^-24 S,   S = |x| |w|^T + |b|
 (binary32 accumulation of K exact products, one rounding to the dtype)."""
+import random
 import sys
 
 import numpy as np
@@ -34,13 +35,7 @@ CASES = [  # M, N, K, bias
 ]
 
 
-@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"M{c[0]}_N{c[1]}_K{c[2]}")
-def test_linear_matches_float64(case, dt):
-    M, N, K, has_bias = case
-    if dt == "f32" and K > 636:
-        pytest.skip("binary32 takes K <= 636")
-    seed = 7000 + M + N + K
+def check_linear(M, N, K, has_bias, dt, seed):
     x = inputs.normal((M, K), seed, 1.0, dt)
     w = inputs.normal((N, K), seed + 1, 1.0 / np.sqrt(K), dt)
     b = inputs.normal((N,), seed + 2, 0.5, dt) if has_bias else None
@@ -51,7 +46,32 @@ def test_linear_matches_float64(case, dt):
     ref = X @ Wm.T + B
     S = np.abs(X) @ np.abs(Wm).T + np.abs(B)
     st = tolerance.compare(y.float().cpu().numpy(), ref, S, K + 1, dt)
-    assert st["ok"], st
+    assert st["ok"], ((M, N, K, has_bias, dt), st)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"M{c[0]}_N{c[1]}_K{c[2]}")
+def test_linear_matches_float64(case, dt):
+    M, N, K, has_bias = case
+    if dt == "f32" and K > 636:
+        pytest.skip("binary32 takes K <= 636")
+    check_linear(M, N, K, has_bias, dt, 7000 + M + N + K)
+
+
+def draw_linear(case):
+    """Seeded random shape: rows around the 16-row tile and 64-row block
+    edges or anywhere up to 4000, any N up to 300, K a multiple of 4 up to
+    320, with or without bias."""
+    r = random.Random(5150 + 131 * case)
+    dt = r.choice(["f32", "f16", "bf16"])
+    M = r.choice([1, 2, 15, 16, 17, 63, 64, 65, 129]) if r.random() < 0.3 else r.randint(1, 4000)
+    return M, r.randint(1, 300), 4 * r.randint(1, 80), r.random() < 0.6, dt
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_linear_random_shapes(case):
+    M, N, K, has_bias, dt = draw_linear(case)
+    check_linear(M, N, K, has_bias, dt, 7500 + 17 * case)
 
 
 def test_linear_batched_rows_and_empty():

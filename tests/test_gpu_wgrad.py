@@ -7,6 +7,7 @@ length of any chain of additions).  The result is binary32 for every input
 dtype.  The chunked sum is added in a fixed order, so repeated calls agree
 bit for bit."""
 import ctypes
+import random
 import sys
 
 import numpy as np
@@ -59,6 +60,27 @@ def test_weight_grad_matches_float64(case, dt):
     x = inputs.normal((M, I), seed + 1, 1.0, dt)
     dw, db = dcn.linear_weight_grad(g.to(DEV), x.to(DEV))
     torch.cuda.synchronize()
+    check(g, x, dw, db, dt)
+
+
+def draw_wgrad(case):
+    """Seeded random shape: rows around the 64-row chunk edges or anywhere up
+    to 20000, O up to 260 (several 128-row blocks of dw), I up to 200, with or
+    without the bias sum."""
+    r = random.Random(6160 + 137 * case)
+    dt = r.choice(["f32", "f16", "bf16"])
+    M = r.choice([1, 3, 63, 64, 65, 127, 128, 129]) if r.random() < 0.3 else r.randint(1, 20000)
+    return M, r.randint(1, 260), r.randint(1, 200), r.random() < 0.7, dt
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_weight_grad_random_shapes(case):
+    M, O, I, bias, dt = draw_wgrad(case)
+    g = inputs.normal((M, O), 8300 + 17 * case, 1.0, dt)
+    x = inputs.normal((M, I), 8301 + 17 * case, 1.0, dt)
+    dw, db = dcn.linear_weight_grad(g.to(DEV), x.to(DEV), bias=bias)
+    torch.cuda.synchronize()
+    assert (db is None) == (not bias)
     check(g, x, dw, db, dt)
 
 
