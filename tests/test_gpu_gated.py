@@ -10,6 +10,7 @@ unrounded).  The pre-gate output must equal the plain forward bit for bit,
 and the fused output must agree with the two-kernel path (core, then gate)
 to the tolerance as well; the autograd wrapper's gradients are compared
 with the two-kernel path's autograd."""
+import random
 import sys
 
 import numpy as np
@@ -48,7 +49,30 @@ def sigmoid(z):
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
 def test_gated_forward_matches_oracle(case):
-    name, N, H, W, G, Cg, K, d, alpha, rc, dt = case
+    check_gated(*case)
+
+
+def draw_gated(case):
+    """Seeded random shape the fused kernel serves: group rows of 32, 64 or
+    128 bytes, channel rows a multiple of 128 bytes, odd K, dilation 1-2,
+    offset_scale of either sign, remove_center, any dtype."""
+    r = random.Random(97000 + 389 * case)
+    dt = r.choice(["f32", "f16", "bf16"])
+    b = 4 if dt == "f32" else 2
+    Cg = r.choice([32, 64, 128]) // b
+    G = r.choice([g for g in (1, 2, 3, 4, 6, 8) if (g * Cg * b) % 128 == 0])
+    K = r.choice([1, 3, 3, 5, 7])
+    d = r.choice([1, 1, 2])
+    return (f"rand{case}", r.choice([1, 2]), r.randint(1, 24), r.randint(1, 24), G, Cg, K, d,
+            r.choice([1.0, 0.6, -1.3]), K >= 3 and r.random() < 0.3, dt)
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_gated_forward_random_shapes(case):
+    check_gated(*draw_gated(case))
+
+
+def check_gated(name, N, H, W, G, Cg, K, d, alpha, rc, dt):
     pad = d * (K - 1) // 2
     w = inputs.Workload(name=name, N=N, H=H, W=W, G=G, Cg=Cg, Ho=H, Wo=W, K=K, stride=1, pad=pad, dilation=d,
                         offset_scale=alpha, softmax=False, dtype=dt, offset_sigma=1.5, mask_sigma=0.5,
