@@ -14,6 +14,7 @@ layer's own intermediates against the oracle, with the core's and the gate's
 element-wise bounds, and the layer's output against the same stages
 composed by hand.
 """
+import random
 import sys
 
 import numpy as np
@@ -138,8 +139,26 @@ def normwise_ok(got, want, tol):
 @pytest.mark.parametrize("case", LAYER, ids=lambda c: f"N{c[0]}_{c[1]}x{c[2]}_G{c[3]}_Cg{c[4]}_K{c[5]}"
                                                           f"_rc{int(c[6])}_cfs{int(c[7])}")
 def test_layer_fp32_matches_oracle(case):
+    check_layer_fp32(case, 6100 + 7 * case[5] + case[1])
+
+
+def draw_layer(case):
+    """Seeded random layer: sizes 3-16, G 1-4, Cg 4-32, K 3 or 5, with or
+    without the centre tap and the gate, offset_scale of either sign."""
+    r = random.Random(61700 + 211 * case)
+    K = r.choice([3, 3, 5])
+    return (r.choice([1, 2]), r.randint(3, 16), r.randint(3, 16), r.choice([1, 2, 3, 4]), r.choice([4, 8, 16, 32]),
+            K, r.random() < 0.3, r.random() < 0.6, r.choice([1.0, 0.7, -1.2]))
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_layer_fp32_random_shapes(case):
+    check_layer_fp32(draw_layer(case), 6300 + 13 * case)
+
+
+def check_layer_fp32(case, seed):
     N, H, W, G, Cg, K, rc, cfs, alpha = case
-    layer, x, gout = make_layer(*case, "f32", 6100 + 7 * K + H)
+    layer, x, gout = make_layer(*case, "f32", seed)
     xi = x.clone().requires_grad_(True)
     out = layer(xi)
     out.backward(gout)
