@@ -90,7 +90,7 @@ def load_library(path: str | None = None):
     lib.dcn_linear_forward.restype = i
     lib.dcn_core_forward_gated.argtypes = [vp] * 6 + [i] * 9 + [f, i, i, vp]
     lib.dcn_core_forward_gated.restype = i
-    lib.dcn_linear_weight_grad.argtypes = [vp] * 4 + [ll, i, i, i, vp, ll, vp]
+    lib.dcn_linear_weight_grad.argtypes = [vp] * 4 + [ll, i, i, i, i, vp, ll, vp]
     lib.dcn_linear_weight_grad.restype = i
     lib.dcn_linear_weight_grad_workspace_size.argtypes = [ll, i, i]
     lib.dcn_linear_weight_grad_workspace_size.restype = ll
@@ -343,30 +343,30 @@ def linear(x, weight, bias=None, *, out=None) -> torch.Tensor:
     return out
 
 
-def linear_weight_grad(g, x, *, bias: bool = True):
+def linear_weight_grad(g, x, *, bias: bool = True, out_dtype=torch.float32):
     """Weight and bias gradients of y = x @ weight.T + bias on the matrix cores
     (HIP): g (..., O) the gradient of y, x (..., I) the input.  Returns
-    (dw (O, I), db (O,) or None) in binary32; the sums over rows are
+    (dw (O, I), db (O,) or None) in out_dtype: binary32 sums over rows,
     deterministic (fixed-order chunk partials, kept in a workspace allocated
-    here)."""
+    here), rounded once to out_dtype."""
     if g.shape[:-1] != x.shape[:-1]:
         raise ValueError("g (..., O) and x (..., I) must share their leading dimensions")
     _check_tensor("g", g, g)
     _check_tensor("x", x, g)
-    if g.dtype not in _DTYPE:
-        raise ValueError(f"unsupported dtype {g.dtype}")
+    if g.dtype not in _DTYPE or out_dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {g.dtype} / {out_dtype}")
     O, I = g.shape[-1], x.shape[-1]
     M = g.numel() // O if O else 0
     lib = load_library()
     need = lib.dcn_linear_weight_grad_workspace_size(M, O, I)
     if need < 0:
         _check(int(-need), "dcn_linear_weight_grad_workspace_size")
-    dw = torch.empty(O, I, dtype=torch.float32, device=g.device)
-    db = torch.empty(O, dtype=torch.float32, device=g.device) if bias else None
+    dw = torch.empty(O, I, dtype=out_dtype, device=g.device)
+    db = torch.empty(O, dtype=out_dtype, device=g.device) if bias else None
     ws = torch.empty((need + 3) // 4, dtype=torch.float32, device=g.device) if need > 0 else None
     with torch.cuda.device(g.device):
         rc = lib.dcn_linear_weight_grad(_ptr(g), _ptr(x), _ptr(dw), None if db is None else _ptr(db), M, O, I,
-                                        _DTYPE[g.dtype], None if ws is None else _ptr(ws),
+                                        _DTYPE[g.dtype], _DTYPE[out_dtype], None if ws is None else _ptr(ws),
                                         0 if ws is None else ws.numel() * 4, _stream(g.device))
     _check(rc, "dcn_linear_weight_grad")
     return dw, db

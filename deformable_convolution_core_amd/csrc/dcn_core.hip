@@ -969,20 +969,55 @@ extern "C" long long dcn_linear_weight_grad_workspace_size(long long M, int O, i
     return (long long)p.workspace_bytes;
 }
 
-extern "C" int dcn_linear_weight_grad(const void* g, const void* x, float* dw, float* db, long long M, int O, int I,
-                                      int dtype, void* workspace, long long workspace_bytes, void* stream)
+template <typename OutT>
+int wgrad_zero(OutT* p, int64_t n, hipStream_t st)
 {
-    const int eb = elem_bytes(dtype);
-    if (eb == 0 || M < 0 || O < 1 || I < 1 || workspace_bytes < 0 || !dw) return DCN_ERR_INVALID_ARG;
-    if (!aligned(dw, 4) || (db && !aligned(db, 4))) return DCN_ERR_INVALID_ARG;
+    if (n <= 0) return DCN_OK;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(dcn_wgrad_zero<OutT>, dim3((uint32_t)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, st, p, n);
+    return launch_status();
+}
+
+template <typename OutT>
+int wgrad_finish(const WgPlan& p, const void* workspace, void* dw, void* db, int O, int I, hipStream_t st)
+{
+    const int64_t groups = (int64_t)O * (p.part_ld / 4);
+    const uint64_t rb = (uint64_t)((groups + kWgRedCols - 1) / kWgRedCols);
+    if (rb >= (1ull << 31)) return DCN_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(dcn_wgrad_reduce<OutT>, dim3((uint32_t)rb), dim3(kWgRedCols * kWgRedGroups), 0, st,
+                       (const float*)workspace, (OutT*)dw, (OutT*)db, O, I, p.part_rows, p.part_ld,
+                       (uint32_t)p.nchunks);
+    return launch_status();
+}
+
+extern "C" int dcn_linear_weight_grad(const void* g, const void* x, void* dw, void* db, long long M, int O, int I,
+                                      int dtype, int out_dtype, void* workspace, long long workspace_bytes,
+                                      void* stream)
+{
+    const int eb = elem_bytes(dtype), ob = elem_bytes(out_dtype);
+    if (eb == 0 || ob == 0 || M < 0 || O < 1 || I < 1 || workspace_bytes < 0 || !dw) return DCN_ERR_INVALID_ARG;
+    if (!aligned(dw, (uintptr_t)ob) || (db && !aligned(db, (uintptr_t)ob))) return DCN_ERR_INVALID_ARG;
     hipStream_t st = (hipStream_t)stream;
     // staging offsets within 64 rows are 32-bit
     if ((int64_t)O * I >= (1ll << 40) || (int64_t)(O > I ? O : I) * eb * kWgRows >= (1ll << 31))
         return DCN_ERR_UNSUPPORTED;
     if (M == 0) {
         // sums over no rows
-        int rc = zero_fill(dw, (int64_t)O * I, st);
-        if (rc == DCN_OK && db) rc = zero_fill(db, O, st);
+        int rc = DCN_OK;
+        switch (out_dtype) {
+        case DCN_F32:
+            rc = zero_fill((float*)dw, (int64_t)O * I, st);
+            if (rc == DCN_OK && db) rc = zero_fill((float*)db, O, st);
+            break;
+        case DCN_F16:
+            rc = wgrad_zero((_Float16*)dw, (int64_t)O * I, st);
+            if (rc == DCN_OK && db) rc = wgrad_zero((_Float16*)db, O, st);
+            break;
+        default:
+            rc = wgrad_zero((__bf16*)dw, (int64_t)O * I, st);
+            if (rc == DCN_OK && db) rc = wgrad_zero((__bf16*)db, O, st);
+            break;
+        }
         return rc;
     }
     if (!g || !x || !aligned(g, (uintptr_t)eb) || !aligned(x, (uintptr_t)eb)) return DCN_ERR_INVALID_ARG;
@@ -1010,10 +1045,9 @@ extern "C" int dcn_linear_weight_grad(const void* g, const void* x, float* dw, f
     }
     int rc = launch_status();
     if (rc != DCN_OK) return rc;
-    const int64_t groups = (int64_t)O * (p.part_ld / 4);
-    const uint64_t rb = (uint64_t)((groups + kWgRedCols - 1) / kWgRedCols);
-    if (rb >= (1ull << 31)) return DCN_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(dcn_wgrad_reduce, dim3((uint32_t)rb), dim3(kWgRedCols * kWgRedGroups), 0, st,
-                       (const float*)workspace, dw, db, O, I, p.part_rows, p.part_ld, (uint32_t)p.nchunks);
-    return launch_status();
+    switch (out_dtype) {
+    case DCN_F32: return wgrad_finish<float>(p, workspace, dw, db, O, I, st);
+    case DCN_F16: return wgrad_finish<_Float16>(p, workspace, dw, db, O, I, st);
+    default: return wgrad_finish<__bf16>(p, workspace, dw, db, O, I, st);
+    }
 }

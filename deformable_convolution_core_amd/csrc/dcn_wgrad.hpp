@@ -255,12 +255,14 @@ __global__ __launch_bounds__(kWgBlock) void dcn_wgrad_kernel(WgArgs a)
 constexpr int kWgRedCols = 8;      // 4-column groups per reduction block
 constexpr int kWgRedGroups = 32;   // chunk groups per column group (kWgRedCols * kWgRedGroups threads)
 
-// dw[o][i] (binary32) = sum over chunks c of part[c][o][i], c in a fixed
-// order: group k sums chunks k, k + 32, k + 64, ..., then the 32 group sums
-// are added in order; db[o] likewise from the bias column.  A thread reads
-// four consecutive partials of a row (16 bytes) per chunk, eight threads a
-// 128-byte row segment; the padded columns are read and dropped.
-__global__ __launch_bounds__(kWgRedCols * kWgRedGroups) void dcn_wgrad_reduce(const float* part, float* dw, float* db,
+// dw[o][i] = sum over chunks c of part[c][o][i], c in a fixed order: group
+// k sums chunks k, k + 32, k + 64, ..., then the 32 group sums are added in
+// order; db[o] likewise from the bias column.  The binary32 sums are stored
+// rounded once to OutT.  A thread reads four consecutive partials of a row
+// (16 bytes) per chunk, eight threads a 128-byte row segment; the padded
+// columns are read and dropped.
+template <typename OutT>
+__global__ __launch_bounds__(kWgRedCols * kWgRedGroups) void dcn_wgrad_reduce(const float* part, OutT* dw, OutT* db,
                                                                               int O, int I, int part_rows,
                                                                               int part_ld, uint32_t nchunks)
 {
@@ -301,10 +303,17 @@ __global__ __launch_bounds__(kWgRedCols * kWgRedGroups) void dcn_wgrad_reduce(co
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int col = c0 + e;
-            if (col < I) dw[(int64_t)o * I + col] = rv[e];
-            else if (db && col == part_ld - 16) db[o] = rv[e];
+            if (col < I) dw[(int64_t)o * I + col] = (OutT)rv[e];
+            else if (db && col == part_ld - 16) db[o] = (OutT)rv[e];
         }
     }
+}
+
+// Zeros of dw and db for a call over no rows, in any output type.
+template <typename OutT>
+__global__ __launch_bounds__(256) void dcn_wgrad_zero(OutT* p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = (OutT)0.f;
 }
 
 }  // namespace dcn

@@ -101,7 +101,7 @@ def _param_grads(g2, x2, want_w, want_b):
     if not (want_w or want_b):
         return None, None
     try:
-        dw, db = linear_weight_grad(g2, x2, bias=want_b)
+        dw, db = linear_weight_grad(g2, x2, bias=want_b, out_dtype=g2.dtype)
     except DCNError as e:
         if e.status != 2:        # only "unsupported shape" falls through
             raise

@@ -254,23 +254,26 @@ int dcn_linear_forward(const void* x, const void* w, const void* bias, void* y, 
 
 /* Weight and bias gradients of a projection (the same layer as
  * dcn_linear_forward), for g (M, O), the gradient of the projection's output,
- * and x (M, I), its input, dense row-major in one dtype:
+ * and x (M, I), its input, dense row-major in dtype:
  *
- *   dw[o, i] = sum_m g[m, o] * x[m, i]      (O, I) row-major, binary32
- *   db[o]    = sum_m g[m, o]                (O) binary32, skipped if db is NULL
+ *   dw[o, i] = sum_m g[m, o] * x[m, i]      (O, I) row-major, in out_dtype
+ *   db[o]    = sum_m g[m, o]                (O) in out_dtype, skipped if db is NULL
  *
  * Products and sums are binary32 (half-precision products are exact); the
  * rows are summed in chunks whose binary32 partials are added in a fixed
- * order, so a call gives the same bits on every run.  The partials live in a
- * caller-owned device workspace of at least
+ * order, so a call gives the same bits on every run.  Each sum is rounded
+ * once to out_dtype (DCN_F32 keeps it; DCN_F16 / DCN_BF16 round to nearest
+ * even, the parameters' own type in a half-precision layer).  The partials
+ * live in a caller-owned device workspace of at least
  * dcn_linear_weight_grad_workspace_size(M, O, I) bytes, 16-byte aligned
  * (overwritten; contents afterwards unspecified).  dw and db are overwritten,
  * also for M == 0 (zeros; g, x and workspace may then be NULL).  M >= 0,
- * O, I >= 1.  Returns DCN_OK, DCN_ERR_INVALID_ARG (bad size or dtype, a NULL
- * or misaligned pointer, a workspace too small), DCN_ERR_UNSUPPORTED (O * I
- * of 2^40 or more, or a size the chunking cannot index) or DCN_ERR_HIP. */
-int dcn_linear_weight_grad(const void* g, const void* x, float* dw, float* db, long long M, int O, int I,
-                           int dtype, void* workspace, long long workspace_bytes, void* stream);
+ * O, I >= 1.  Returns DCN_OK, DCN_ERR_INVALID_ARG (bad size, dtype or
+ * out_dtype, a NULL or misaligned pointer, a workspace too small),
+ * DCN_ERR_UNSUPPORTED (O * I of 2^40 or more, or a size the chunking cannot
+ * index) or DCN_ERR_HIP. */
+int dcn_linear_weight_grad(const void* g, const void* x, void* dw, void* db, long long M, int O, int I,
+                           int dtype, int out_dtype, void* workspace, long long workspace_bytes, void* stream);
 
 /* Workspace bytes dcn_linear_weight_grad needs (0 for M == 0), or minus a
  * dcn_status for invalid sizes. */

@@ -123,14 +123,19 @@ def test_weight_grad_entry_points():
     assert small >= 128 * 80 * 4 and big >= small and big % 16 == 0
     p = [vp(0x10000), vp(0x20000), vp(0x30000), vp(0x40000)]
     ws = vp(0x100000)
-    assert lib.dcn_linear_weight_grad(*p, 64, 8, 8, 7, ws, 1 << 20, None) == INVALID            # dtype
-    assert lib.dcn_linear_weight_grad(*p, -1, 8, 8, 0, ws, 1 << 20, None) == INVALID            # M
-    assert lib.dcn_linear_weight_grad(p[0], p[1], None, None, 64, 8, 8, 0, ws, 1 << 20, None) == INVALID
-    assert lib.dcn_linear_weight_grad(*p, 64, 8, 8, 0, None, 0, None) == INVALID               # no workspace
+    assert lib.dcn_linear_weight_grad(*p, 64, 8, 8, 7, 0, ws, 1 << 20, None) == INVALID         # dtype
+    assert lib.dcn_linear_weight_grad(*p, 64, 8, 8, 0, 3, ws, 1 << 20, None) == INVALID         # out_dtype
+    assert lib.dcn_linear_weight_grad(*p, 64, 8, 8, 0, -1, ws, 1 << 20, None) == INVALID
+    assert lib.dcn_linear_weight_grad(*p, -1, 8, 8, 0, 0, ws, 1 << 20, None) == INVALID         # M
+    assert lib.dcn_linear_weight_grad(p[0], p[1], None, None, 64, 8, 8, 0, 0, ws, 1 << 20, None) == INVALID
+    assert lib.dcn_linear_weight_grad(*p, 64, 8, 8, 0, 0, None, 0, None) == INVALID            # no workspace
     need = lib.dcn_linear_weight_grad_workspace_size(64, 8, 8)
-    assert lib.dcn_linear_weight_grad(*p, 64, 8, 8, 0, ws, need - 1, None) == INVALID          # too small
-    assert lib.dcn_linear_weight_grad(*p, 64, 8, 8, 0, vp(0x100008), need, None) == INVALID    # misaligned
-    assert lib.dcn_linear_weight_grad(vp(0x10001), p[1], p[2], p[3], 64, 8, 8, 1, ws, need, None) == INVALID
+    assert lib.dcn_linear_weight_grad(*p, 64, 8, 8, 0, 0, ws, need - 1, None) == INVALID       # too small
+    assert lib.dcn_linear_weight_grad(*p, 64, 8, 8, 0, 0, vp(0x100008), need, None) == INVALID # misaligned
+    assert lib.dcn_linear_weight_grad(vp(0x10001), p[1], p[2], p[3], 64, 8, 8, 1, 0, ws, need, None) == INVALID
+    # outputs aligned to their own element: 2-byte dw is fine in half precision, not in binary32
+    assert lib.dcn_linear_weight_grad(p[0], p[1], vp(0x30002), p[3], 64, 8, 8, 0, 0, ws, need, None) == INVALID
+    assert lib.dcn_linear_weight_grad(p[0], p[1], vp(0x30001), p[3], 64, 8, 8, 0, 1, ws, need, None) == INVALID
 
 
 def test_backward_workspace_entry_points():

@@ -84,6 +84,25 @@ def test_weight_grad_random_shapes(case):
     check(g, x, dw, db, dt)
 
 
+@pytest.mark.parametrize("out", ["f16", "bf16"])
+@pytest.mark.parametrize("case", [(777, 108, 64), (130, 864, 72), (64, 7, 3), (1, 16, 16)],
+                         ids=lambda c: f"M{c[0]}_O{c[1]}_I{c[2]}")
+def test_weight_grad_in_half_precision_is_the_binary32_sum_rounded(case, out):
+    """dw and db stored in a half-precision type are the binary32 sums rounded
+    once to nearest even: bit for bit what the binary32 call gives, converted."""
+    M, O, I = case
+    odt = inputs.DTYPES[out]
+    g = inputs.normal((M, O), 8400 + M + O, 1.0, out).to(DEV)
+    x = inputs.normal((M, I), 8401 + M + I, 1.0, out).to(DEV)
+    dw32, db32 = dcn.linear_weight_grad(g, x)
+    dwh, dbh = dcn.linear_weight_grad(g, x, out_dtype=odt)
+    zw, zb = dcn.linear_weight_grad(g[:0], x[:0], out_dtype=odt)
+    torch.cuda.synchronize()
+    assert dwh.dtype == odt and dbh.dtype == odt
+    assert torch.equal(dwh, dw32.to(odt)) and torch.equal(dbh, db32.to(odt))
+    assert torch.equal(zw, torch.zeros(O, I, dtype=odt, device=DEV)) and torch.equal(zb, torch.zeros(O, dtype=odt, device=DEV))
+
+
 def test_weight_grad_at_the_layer_shape_is_deterministic():
     """The headline layer's offset+mask projection (200,704 rows): within the
     bound, and two calls give the same bits."""
@@ -123,6 +142,6 @@ def test_weight_grad_rejects_a_small_workspace():
     need = lib.dcn_linear_weight_grad_workspace_size(256, 16, 16)
     ws = torch.empty(need // 4, device=DEV)
     vp = ctypes.c_void_p
-    rc = lib.dcn_linear_weight_grad(vp(g.data_ptr()), vp(x.data_ptr()), vp(dw.data_ptr()), None, 256, 16, 16, 0,
+    rc = lib.dcn_linear_weight_grad(vp(g.data_ptr()), vp(x.data_ptr()), vp(dw.data_ptr()), None, 256, 16, 16, 0, 0,
                                     vp(ws.data_ptr()), need - 4, None)
     assert rc == 1
