@@ -958,15 +958,11 @@ void launch_wgrad(int vg, int vx, dim3 grid, const WgArgs& a, hipStream_t st)
     else hipLaunchKernelGGL((dcn_wgrad_kernel<T, 0, 0>), grid, dim3(kWgBlock), 0, st, a);
 }
 
-}  // namespace
-
-extern "C" long long dcn_linear_weight_grad_workspace_size(long long M, int O, int I)
+// blocks of the fixed-order reduction: one per kWgRedCols 4-column groups of dw
+uint64_t wgrad_reduce_blocks(const WgPlan& p, int O)
 {
-    if (M < 0 || O < 1 || I < 1) return -(long long)DCN_ERR_INVALID_ARG;
-    if (M == 0) return 0;
-    WgPlan p;
-    if (!plan_wgrad(M, O, I, p)) return -(long long)DCN_ERR_UNSUPPORTED;
-    return (long long)p.workspace_bytes;
+    const int64_t groups = (int64_t)O * (p.part_ld / 4);
+    return (uint64_t)((groups + kWgRedCols - 1) / kWgRedCols);
 }
 
 template <typename OutT>
@@ -981,13 +977,22 @@ int wgrad_zero(OutT* p, int64_t n, hipStream_t st)
 template <typename OutT>
 int wgrad_finish(const WgPlan& p, const void* workspace, void* dw, void* db, int O, int I, hipStream_t st)
 {
-    const int64_t groups = (int64_t)O * (p.part_ld / 4);
-    const uint64_t rb = (uint64_t)((groups + kWgRedCols - 1) / kWgRedCols);
-    if (rb >= (1ull << 31)) return DCN_ERR_UNSUPPORTED;
+    const uint64_t rb = wgrad_reduce_blocks(p, O);
     hipLaunchKernelGGL(dcn_wgrad_reduce<OutT>, dim3((uint32_t)rb), dim3(kWgRedCols * kWgRedGroups), 0, st,
                        (const float*)workspace, (OutT*)dw, (OutT*)db, O, I, p.part_rows, p.part_ld,
                        (uint32_t)p.nchunks);
     return launch_status();
+}
+
+}  // namespace
+
+extern "C" long long dcn_linear_weight_grad_workspace_size(long long M, int O, int I)
+{
+    if (M < 0 || O < 1 || I < 1) return -(long long)DCN_ERR_INVALID_ARG;
+    if (M == 0) return 0;
+    WgPlan p;
+    if (!plan_wgrad(M, O, I, p) || wgrad_reduce_blocks(p, O) >= (1ull << 31)) return -(long long)DCN_ERR_UNSUPPORTED;
+    return (long long)p.workspace_bytes;
 }
 
 extern "C" int dcn_linear_weight_grad(const void* g, const void* x, void* dw, void* db, long long M, int O, int I,
@@ -1022,7 +1027,7 @@ extern "C" int dcn_linear_weight_grad(const void* g, const void* x, void* dw, vo
     }
     if (!g || !x || !aligned(g, (uintptr_t)eb) || !aligned(x, (uintptr_t)eb)) return DCN_ERR_INVALID_ARG;
     WgPlan p;
-    if (!plan_wgrad(M, O, I, p)) return DCN_ERR_UNSUPPORTED;
+    if (!plan_wgrad(M, O, I, p) || wgrad_reduce_blocks(p, O) >= (1ull << 31)) return DCN_ERR_UNSUPPORTED;
     if (!workspace || !aligned(workspace, 16) || (uint64_t)workspace_bytes < p.workspace_bytes)
         return DCN_ERR_INVALID_ARG;
     // widest staging read that divides a row of g and of x and keeps every
