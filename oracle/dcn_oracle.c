@@ -239,7 +239,8 @@ int oracle_backward(const double* input, const double* offset, const double* mas
                 gm[p] = 0.0; gm_abs[p] = 0.0;
                 double x = coord(wo, stride, pad, c0, i, dil, alpha, off[2 * p], coord_mode);
                 double y = coord(ho, stride, pad, c0, j, dil, alpha, off[2 * p + 1], coord_mode);
-                if (sample_touches_map(x, y, H, W)) {
+                const int touches = sample_touches_map(x, y, H, W);
+                if (touches) {
                     double fx = floor(x), fy = floor(y);
                     int x0 = (int)fx, y0 = (int)fy;
                     double lx = x - fx, ly = y - fy;
@@ -266,12 +267,16 @@ int oracle_backward(const double* input, const double* offset, const double* mas
                         }
                     }
                 }
+                /* A skipped sample adds nothing to the output whatever its
+                 * offsets are (nearby offsets are skipped too), so its offset
+                 * gradient is exactly zero -- also for an Inf or NaN mask
+                 * value, which the skipped sample never multiplies. */
                 double* god = grad_offset + pg * P * 2;
-                god[2 * p] = alpha * m[p] * gdx;
-                god[2 * p + 1] = alpha * m[p] * gdy;
+                god[2 * p] = touches ? alpha * m[p] * gdx : 0.0;
+                god[2 * p + 1] = touches ? alpha * m[p] * gdy : 0.0;
                 if (goff_abs) {
-                    goff_abs[pg * P * 2 + 2 * p] = fabs(alpha * m[p]) * adx;
-                    goff_abs[pg * P * 2 + 2 * p + 1] = fabs(alpha * m[p]) * ady;
+                    goff_abs[pg * P * 2 + 2 * p] = touches ? fabs(alpha * m[p]) * adx : 0.0;
+                    goff_abs[pg * P * 2 + 2 * p + 1] = touches ? fabs(alpha * m[p]) * ady : 0.0;
                 }
             }
             double* gmk = grad_mask + pg * P;

@@ -125,6 +125,39 @@ def test_skipped_samples_have_zero_gradient():
     assert not np.any(r["grad_input"]) and not np.any(r["grad_offset"]) and not np.any(r["grad_mask"])
 
 
+@pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan, 1e300])
+def test_skipped_sample_gradients_ignore_its_mask_value(bad):
+    """A sample the skip rule drops adds nothing to the output for any mask
+    value, and moving its offsets a little keeps it dropped, so the output
+    equals the one with that mask value set to 0 (checked on the forward)
+    and every gradient equals that call's: grad_input and grad_offset
+    unchanged, zero offset and mask gradients at the dropped sample (no
+    Inf * 0 from the mask it never multiplies)."""
+    rng = np.random.default_rng(37)
+    N, H, W, G, Cg, K = 1, 6, 7, 2, 3, 3
+    x, off, m, g = setup(rng, N, H, W, G, Cg, K, 1, 1, 1, 1.0)
+    off = off.reshape(N, H, W, G, 9, 2)
+    m = m.reshape(N, H, W, G, 9)
+    drop = rng.random((N, H, W, G, 9)) < 0.3
+    off[drop] = np.array([-50.5, 3.25])            # x far left of the map: skipped
+    m_bad, m_zero = m.copy(), m.copy()
+    m_bad[drop] = bad
+    m_zero[drop] = 0.0
+    off = off.reshape(N, H, W, -1)
+    kw = dict(K=K, stride=1, pad=1, dilation=1, offset_scale=1.0, softmax=False, group=G)
+    o_bad, _ = oracle.forward(x, off, m_bad.reshape(N, H, W, -1), **kw)
+    o_zero, _ = oracle.forward(x, off, m_zero.reshape(N, H, W, -1), **kw)
+    assert np.array_equal(o_bad, o_zero)
+    r_bad = oracle.backward(x, off, m_bad.reshape(N, H, W, -1), g, **kw)
+    r_zero = oracle.backward(x, off, m_zero.reshape(N, H, W, -1), g, **kw)
+    assert np.array_equal(r_bad["grad_input"], r_zero["grad_input"])
+    assert np.array_equal(r_bad["grad_offset"], r_zero["grad_offset"])
+    assert np.array_equal(r_bad["grad_mask"], r_zero["grad_mask"])
+    goff = r_bad["grad_offset"].reshape(N, H, W, G, 9, 2)
+    assert not np.any(goff[drop]) and not np.any(r_bad["grad_mask"].reshape(N, H, W, G, 9)[drop])
+    assert np.any(goff[~drop])                      # the kept samples do have gradients
+
+
 def test_binary32_mode_matches_exact_away_from_integers():
     """The binary32 coordinate mode only moves coordinates by ~|x|*2^-24; away
     from integers both modes give nearly the same gradients."""

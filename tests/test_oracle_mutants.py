@@ -44,7 +44,9 @@ MUTANTS = {
     "bwd_softmax_jacobian_missing_m": ("gmk[p] = m[p] * (gm[p] - dot);", "gmk[p] = gm[p] - dot;"),
     "bwd_scatter_wrong_pixel": ("long base = (((long)n * H + yy) * W + xx) * C + (long)g * Cg;",
                                 "long base = (((long)n * H + yy) * W + (W - 1 - xx)) * C + (long)g * Cg;"),
-    "bwd_alpha_missing": ("god[2 * p] = alpha * m[p] * gdx;", "god[2 * p] = m[p] * gdx;"),
+    "bwd_alpha_missing": ("god[2 * p] = touches ? alpha * m[p] * gdx : 0.0;", "god[2 * p] = touches ? m[p] * gdx : 0.0;"),
+    "bwd_skipped_offset_grad_uses_mask": ("god[2 * p] = touches ? alpha * m[p] * gdx : 0.0;",
+                                          "god[2 * p] = alpha * m[p] * gdx;"),
 }
 
 
@@ -69,6 +71,8 @@ def battery():
         checks.append(lambda g=geom: tg.test_grad_offset_finite_difference(g))
     checks += [tg.test_grad_mask_raw_adjoint, lambda: tg.test_grad_mask_finite_difference(False),
                lambda: tg.test_grad_mask_finite_difference(True), tg.test_skipped_samples_have_zero_gradient]
+    for bad in (float("inf"), float("nan")):
+        checks.append(lambda b=bad: tg.test_skipped_sample_gradients_ignore_its_mask_value(b))
     return checks
 
 
