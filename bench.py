@@ -86,6 +86,8 @@ def rotating_sets(w, backward=False, packed=False):
             d["gi"] = torch.empty_like(d["input"])
             d["goff"] = torch.empty_like(d["offset"])
             d["gm"] = torch.empty_like(d["mask"]) if "mask" in d else None
+            if w.dtype != "f32":   # half precision sums grad_input in a binary32 workspace
+                d["ws"] = torch.empty(d["input"].numel(), dtype=torch.float32, device="cuda")
         else:
             d["out"] = torch.empty(w.shapes()["output"], dtype=d["input"].dtype, device="cuda")
         sets.append(d)
@@ -113,10 +115,12 @@ def launcher(w, backward=False, packed=False):
             raise dcn.DCNError(rc, lib.dcn_status_string(rc).decode())
 
     def bwd(d, stream):
-        rc = lib.dcn_core_backward_ex(ptr(d["input"]), ptr(d["offset"]), ptr(d.get("mask")),
+        ws = d.get("ws")
+        rc = lib.dcn_core_backward_ws(ptr(d["input"]), ptr(d["offset"]), ptr(d.get("mask")),
                                       ptr(d["grad_out"]), ptr(d["gi"]), ptr(d["goff"]), ptr(d["gm"]),
                                       w.N, w.H, w.W, w.G, w.Cg, w.K, w.stride, w.pad, w.dilation,
-                                      float(w.offset_scale), flags, dt, vp(stream))
+                                      float(w.offset_scale), flags, dt, ptr(ws),
+                                      0 if ws is None else ws.numel() * 4, vp(stream))
         if rc:
             raise dcn.DCNError(rc, lib.dcn_status_string(rc).decode())
 

@@ -163,9 +163,11 @@ struct TilePlan {
 // at most 128 pixels it picks the cheapest by a simple cost model: lane slots
 // issued (idle lanes of ragged tiles count, weighted up below 16 resident
 // waves per CU) plus region chunks staged.  min_waves and max_lds are the
-// caller's limits (the forward's are kMinFwdTileWaves and kMaxFwdTileLds).
+// caller's limits (the forward's are kMinFwdTileWaves and kMaxFwdTileLds);
+// zero_block reserves the forward's 2x2 block of zero pixels after a
+// partial region.
 bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan, int min_waves = 12,
-                int64_t max_lds = kMaxTileLds)
+                int64_t max_lds = kMaxTileLds, bool zero_block = false)
 {
     const int eb = c.ebytes, rowg = c.Cg * eb, rowc = c.G * c.Cg * eb;
     if (!(rowg == 32 || rowg == 64 || rowg == 128) || rowc % 128 != 0) return false;
@@ -197,7 +199,9 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan, 
             if (rh > c.H + 2) rh = c.H + 2;
             if (rw > c.W + 2) rw = c.W + 2;
             if (whole) rh = c.H + 3;
-            const int64_t lds = (int64_t)rh * rw * 128;
+            // the forward's block of zero pixels after a partial region (two
+            // more rows' worth of address range, of which 2x2 pixels are used)
+            const int64_t lds = ((int64_t)rh * rw + (zero_block && !whole ? rw + 2 : 0)) * 128;
             if (lds > max_lds) continue;
             const uint64_t tx = (uint64_t)((c.Wo + tw - 1) / tw), ty = (uint64_t)((c.Ho + th - 1) / th);
             const uint64_t tiles = tx * ty * slabs * (uint64_t)c.N;
@@ -274,7 +278,7 @@ template <typename T>
 int forward_typed(const FwdArgs& a, const Call& c, hipStream_t st)
 {
     TilePlan pl;
-    if (DCN_USE_TILES && plan_tiles(c, a.input, a.output, pl, kMinFwdTileWaves, kMaxFwdTileLds))
+    if (DCN_USE_TILES && plan_tiles(c, a.input, a.output, pl, kMinFwdTileWaves, kMaxFwdTileLds, true))
         return forward_tiled<T>(a, c, pl, st);
     if (a.gate) return DCN_ERR_UNSUPPORTED;   // the gate is fused into the tiled kernel only
     const int row = c.Cg * (int)sizeof(T);
@@ -420,11 +424,16 @@ int backward_grad_tiled(const BwdArgs& base, const Call& c, const TilePlan& pl, 
     return c.k3() ? launch_grad_tiled<T, 3, 256>(a, c, pl, st) : launch_grad_tiled<T, 0, 256>(a, c, pl, st);
 }
 
-// Half precision: the owner kernel writes grad_input (binary32 sums rounded
-// once) and the tiled gradient kernel does the rest; shapes outside what the
-// two kernels cover are not supported.
+int zero_fill(float* p, int64_t n, hipStream_t st);
+
+// Half precision on the tiled shapes, every grad_input element a binary32 sum
+// rounded once: the workspace (a binary32 image of grad_input) is zeroed, the
+// tiled gradient kernel writes grad_offset and grad_mask and adds the corners
+// beyond the owners' reach into the workspace, and the owner kernel starts
+// its tiles from the workspace, adds the near corners and stores each
+// element once in the dtype.
 template <typename T>
-int backward_half(BwdArgs a, const Call& c, hipStream_t st)
+int backward_half(BwdArgs a, const Call& c, float* ws, hipStream_t st)
 {
     OwnerPlan op;
     TilePlan tp;
@@ -432,23 +441,25 @@ int backward_half(BwdArgs a, const Call& c, hipStream_t st)
     // any tile that fits the LDS will do
     if (!plan_owner(c, a.grad_out, a.grad_input, op) || !plan_tiles(c, a.input, a.grad_out, tp, 1, 160 * 1024))
         return DCN_ERR_UNSUPPORTED;
-    a.geo = make_geometry(c, 8);
-    int rc = c.k3() ? launch_owner<T, 3>(a, op, st) : launch_owner<T, 0>(a, op, st);
+    int rc = zero_fill(ws, (int64_t)c.N * c.H * c.W * c.G * c.Cg, st);
     if (rc != DCN_OK) return rc;
     a.near_m = op.og.M;
-    return backward_grad_tiled<T>(a, c, tp, st);
+    a.far_ws = ws;
+    rc = backward_grad_tiled<T>(a, c, tp, st);
+    if (rc != DCN_OK) return rc;
+    a.geo = make_geometry(c, 8);
+    a.gi_init = ws;
+    return c.k3() ? launch_owner<T, 3>(a, op, st) : launch_owner<T, 0>(a, op, st);
 }
 
 // Whether the tiled half-precision kernels take this call (both planners
-// accept it); otherwise a half-precision backward needs the workspace path.
+// accept it); otherwise the untiled workspace kernel runs it.
 bool half_tiled_ok(const Call& c, const void* input, const void* gout, const void* gin)
 {
     OwnerPlan op;
     TilePlan tp;
     return plan_owner(c, gout, gin, op) && plan_tiles(c, input, gout, tp, 1, 160 * 1024);
 }
-
-int zero_fill(float* p, int64_t n, hipStream_t st);
 
 // Half-precision backward on any shape whose group splits into a power of
 // two of lanes: binary32 atomics into the zeroed workspace, then one
@@ -632,17 +643,18 @@ int backward_call(const Call& c, const void* input, const void* offset_in, const
     if (!aligned(input, eb) || !aligned(grad_output, eb) || !aligned(grad_input, eb)) return DCN_ERR_INVALID_ARG;
     const int dtype = c.dtype;
     if (dtype != DCN_F32) {
+        // half precision accumulates grad_input in a binary32 workspace
+        if (!workspace) return DCN_ERR_UNSUPPORTED;
+        if (workspace_bytes < (long long)N * H * W * G * Cg * 4 || !aligned(workspace, 16)) return DCN_ERR_INVALID_ARG;
         BwdArgs a{};
         a.input = input; a.offset = offset; a.mask = mask; a.grad_out = grad_output;
         a.grad_input = grad_input; a.grad_offset = grad_offset; a.grad_mask = grad_mask;
         a.near_m = -1;
         hipStream_t st = (hipStream_t)stream;
+        float* ws = (float*)workspace;
         if (half_tiled_ok(c, input, grad_output, grad_input))
-            return dtype == DCN_F16 ? backward_half<_Float16>(a, c, st) : backward_half<__bf16>(a, c, st);
-        if (!workspace) return DCN_ERR_UNSUPPORTED;
-        if (workspace_bytes < (long long)N * H * W * G * Cg * 4 || !aligned(workspace, 4)) return DCN_ERR_INVALID_ARG;
-        return dtype == DCN_F16 ? backward_generic<_Float16>(a, c, (float*)workspace, st)
-                                : backward_generic<__bf16>(a, c, (float*)workspace, st);
+            return dtype == DCN_F16 ? backward_half<_Float16>(a, c, ws, st) : backward_half<__bf16>(a, c, ws, st);
+        return dtype == DCN_F16 ? backward_generic<_Float16>(a, c, ws, st) : backward_generic<__bf16>(a, c, ws, st);
     }
     int LB, L;
     if (Cg % 4 == 0 && pow2(Cg / 4) && Cg / 4 <= 64 && aligned(input, 16) && aligned(grad_input, 16)) {
@@ -734,7 +746,8 @@ extern "C" long long dcn_core_backward_workspace_size(const void* input, const v
     Call c;
     const int rc = validate_ex(c, N, H, W, G, Cg, K, stride, pad, dilation, offset_scale, flags, dtype);
     if (rc != DCN_OK) return -(long long)rc;
-    if (dtype == DCN_F32 || N == 0 || half_tiled_ok(c, input, grad_output, grad_input)) return 0;
+    (void)input; (void)grad_output; (void)grad_input;
+    if (dtype == DCN_F32 || N == 0) return 0;
     return (long long)N * H * W * G * Cg * 4;
 }
 

@@ -264,6 +264,12 @@ struct BwdArgs {
     int near_m;                   // >= 0: corners within this many pixels of the sampling
                                   // base were added by the owner kernel; -1: none were
     Geometry geo;
+    // Half precision: the gradient kernel adds the corners that are not near
+    // into this binary32 image of grad_input (zeroed first), and the owner
+    // kernel starts its tiles from it (gi_init), so every grad_input element
+    // is a binary32 sum rounded once.  Null for binary32 calls.
+    float* far_ws;
+    const float* gi_init;
 };
 
 // The (image, pixel, group, channel chunk) a lane owns.
@@ -470,12 +476,6 @@ __device__ __forceinline__ int cvt_flr(float x)
     return r;
 }
 
-// Neither argument is NaN.
-__device__ __forceinline__ bool ordered(float x, float y)
-{
-    return !__builtin_isunordered(x, y);
-}
-
 // Offset pair (dx, dy) and mask value of point q of a (pixel, group), read
 // through per-image buffer resources with the point in the scalar offset.
 // The raw forms keep the loaded bits (one dword per offset pair for half
@@ -642,79 +642,122 @@ struct TiledLane {
     uint32_t lane_first;          // this lane's first 16-byte slot in a pixel slab
     uint32_t RW, RWB;             // region width in pixels and in bytes
     uint32_t gl_first, gl_second; // the two halves inside an input pixel row
+    // Fast-path bounds: lox < x < hix and loy < y < hiy hold exactly when the
+    // sample is on the map (x > -1, x < W, likewise y) and its four corners
+    // lie in the staged region (x_lo <= floor(x) <= x_lo + RW - 2).  A NaN
+    // coordinate fails them.
+    float lox, hix, loy, hiy;
+    uint32_t zero_a0;             // this lane's slot in a 2x2 block of zero pixels
 };
 
-// Coordinates, weights and corner reads of one point: from the staged region
-// when all four corners lie inside it, else gathered from global memory with
-// the untiled kernel's off-map rules.  xt, yt: the tap's part of the
-// coordinates, fmaf(alpha, tap, base).
-template <typename T>
-__device__ __forceinline__ TiledPoint tiled_fetch(const Geometry& G, const TiledLane& L, const char* lds,
-                                                  __amdgpu_buffer_rsrc_t rin, float xt, float yt,
-                                                  float2 d, float m)
+// Strict lower bound equivalent to "x >= lo and x > -1" for an integer lo:
+// the float just below lo (lo >= 1), -1 (lo <= -1).  For lo = 0 the bound is
+// -0.0, which also turns away x = 0 itself; such a sample takes the slower
+// path, which gives the same result.
+__device__ __forceinline__ float fast_lower_bound(int lo)
 {
-    TiledPoint pt;
-    const float x = fmaf(G.alpha, d.x, xt);
-    const float y = fmaf(G.alpha, d.y, yt);
-    // Floor and fraction come from the absolute coordinate (x - x_lo is not
-    // exact when x_lo < 0); the region test is on the integer floor.
-    // cvt_flr saturates +-Inf to out-of-range values; NaN is rejected by the
-    // ordered compare.
-    const uint32_t ix = (uint32_t)(cvt_flr(x) - L.x_lo), iy = (uint32_t)(cvt_flr(y) - L.y_lo);
-    float lx, ly, mm = m;
-    if ((ix < L.xlim) & (iy < L.ylim) & ordered(x, y)) {
-        lx = __builtin_amdgcn_fractf(x);
-        ly = __builtin_amdgcn_fractf(y);
-        const uint32_t a0 = (__umul24(iy, L.RW) + ix) * 128u + L.lane_first;
-        const uint32_t a1 = a0 ^ 16u;
-        const uint32_t ca[4] = {0u, 128u, L.RWB, L.RWB + 128u};
+    return lo >= 1 ? __int_as_float(__float_as_int((float)lo) - 1) : (lo == 0 ? -0.0f : -1.0f);
+}
+
+__device__ __forceinline__ void set_fast_bounds(TiledLane& L, const Geometry& G, uint32_t RH)
+{
+    L.lox = fast_lower_bound(L.x_lo);
+    L.loy = fast_lower_bound(L.y_lo);
+    const int hx = L.x_lo + (int)L.RW - 1, hy = L.y_lo + (int)RH - 1;
+    L.hix = (float)(hx < G.W ? hx : G.W);
+    L.hiy = (float)(hy < G.H ? hy : G.H);
+    L.zero_a0 = RH * L.RWB + L.lane_first;
+}
+
+// Bilinear weights with the modulation folded in; each is formed with
+// relative error <= 2 ulp (the one-minus factors are fused, so a weight near
+// zero is not the difference of two rounded values).
+__device__ __forceinline__ void modulated_weights(float mm, float lx, float ly, float* w)
+{
+    const float mly = mm * ly, mhy = fmaf(-mm, ly, mm);
+    w[0] = fmaf(-mhy, lx, mhy);
+    w[1] = mhy * lx;
+    w[2] = fmaf(-mly, lx, mly);
+    w[3] = mly * lx;
+}
+
+template <typename T>
+__device__ __forceinline__ void accumulate_corner(const uint32_t (&raw)[8], float w, float* acc)
+{
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint4 v0 = *(const uint4*)(lds + a0 + ca[k]);
-            const uint4 v1 = *(const uint4*)(lds + a1 + ca[k]);
-            pt.raw[k][0] = v0.x; pt.raw[k][1] = v0.y; pt.raw[k][2] = v0.z; pt.raw[k][3] = v0.w;
-            pt.raw[k][4] = v1.x; pt.raw[k][5] = v1.y; pt.raw[k][6] = v1.z; pt.raw[k][7] = v1.w;
-        }
-    } else {
-        // outside the staged region: gather from memory, or nothing at all
-        // for a sample with no corner on the map (or a NaN coordinate)
-        float fx = floorf(x), fy = floorf(y);
-        lx = x - fx;
-        ly = y - fy;
-        const bool inmap = x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H;
-        if (!inmap) { fx = -2.0f; fy = -2.0f; lx = 0.f; ly = 0.f; mm = 0.f; }
-        const int x0 = (int)fx, y0 = (int)fy;
-        const bool vx0 = (uint32_t)x0 < (uint32_t)G.W, vx1 = (uint32_t)(x0 + 1) < (uint32_t)G.W;
-        const bool vy0 = (uint32_t)y0 < (uint32_t)G.H, vy1 = (uint32_t)(y0 + 1) < (uint32_t)G.H;
-        const bool vk[4] = {vy0 && vx0, vy0 && vx1, vy1 && vx0, vy1 && vx1};
-        const uint32_t a00 = (uint32_t)y0 * G.in_line_bytes + (uint32_t)x0 * G.in_row_bytes;
-        const uint32_t ck[4] = {0u, G.in_row_bytes, G.in_line_bytes, G.in_line_bytes + G.in_row_bytes};
-        if (inmap) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t o0 = vk[k] ? a00 + ck[k] + L.gl_first : kOOB;
-                const uint32_t o1 = vk[k] ? a00 + ck[k] + L.gl_second : kOOB;
-                const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rin, o0, 0, 0);
-                const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rin, o1, 0, 0);
-                pt.raw[k][0] = v0[0]; pt.raw[k][1] = v0[1]; pt.raw[k][2] = v0[2]; pt.raw[k][3] = v0[3];
-                pt.raw[k][4] = v1[0]; pt.raw[k][5] = v1[1]; pt.raw[k][6] = v1[2]; pt.raw[k][7] = v1[3];
-            }
+    for (int c = 0; c < 8; ++c) {
+        if constexpr (Elem<T>::bytes == 4) {
+            acc[c] = fmaf(w, __uint_as_float(raw[c]), acc[c]);
         } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-                for (int c = 0; c < 8; ++c) pt.raw[k][c] = 0u;
+            acc[2 * c] = fmaf(w, Elem<T>::widen(raw[c] & 0xffffu), acc[2 * c]);
+            acc[2 * c + 1] = fmaf(w, Elem<T>::widen(raw[c] >> 16), acc[2 * c + 1]);
         }
     }
-    // bilinear weights with the modulation folded in; each is formed with
-    // relative error <= 2 ulp (the one-minus factors are fused, so a weight
-    // near zero is not the difference of two rounded values)
-    const float mly = mm * ly, mhy = fmaf(-mm, ly, mm);
-    pt.w[0] = fmaf(-mhy, lx, mhy);
-    pt.w[1] = mhy * lx;
-    pt.w[2] = fmaf(-mly, lx, mly);
-    pt.w[3] = mly * lx;
+}
+
+// Coordinates, weights and corner reads of one point from the staged region.
+// A sample that the region does not serve -- off the map (the definition
+// skips it), NaN, or on the map beyond the region -- reads the block of
+// zeros with zero weights instead, so an Inf or NaN in the input can never
+// meet a zero weight here; far is set for the last kind, whose corners the
+// caller gathers from memory (far_accumulate).  xt, yt: the tap's part of
+// the coordinates, fmaf(alpha, tap, base).
+template <typename T>
+__device__ __forceinline__ TiledPoint tiled_fetch(const Geometry& G, const TiledLane& L, const char* lds, float xt,
+                                                  float yt, float2 d, float m, bool& far, float& x, float& y)
+{
+    TiledPoint pt;
+    x = fmaf(G.alpha, d.x, xt);
+    y = fmaf(G.alpha, d.y, yt);
+    const bool ok = (x > L.lox) & (x < L.hix) & (y > L.loy) & (y < L.hiy);
+    // Floor and fraction come from the absolute coordinate (x - x_lo is not
+    // exact when x_lo < 0).
+    const uint32_t ix = (uint32_t)(cvt_flr(x) - L.x_lo), iy = (uint32_t)(cvt_flr(y) - L.y_lo);
+    const uint32_t a0 = ok ? (__umul24(iy, L.RW) + ix) * 128u + L.lane_first : L.zero_a0;
+    const uint32_t a1 = a0 ^ 16u;
+    const uint32_t ca[4] = {0u, 128u, L.RWB, L.RWB + 128u};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint4 v0 = *(const uint4*)(lds + a0 + ca[k]);
+        const uint4 v1 = *(const uint4*)(lds + a1 + ca[k]);
+        pt.raw[k][0] = v0.x; pt.raw[k][1] = v0.y; pt.raw[k][2] = v0.z; pt.raw[k][3] = v0.w;
+        pt.raw[k][4] = v1.x; pt.raw[k][5] = v1.y; pt.raw[k][6] = v1.z; pt.raw[k][7] = v1.w;
+    }
+    const float lx = ok ? __builtin_amdgcn_fractf(x) : 0.f, ly = ok ? __builtin_amdgcn_fractf(y) : 0.f;
+    far = !ok && x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H;
+    modulated_weights(ok ? m : 0.f, lx, ly, pt.w);
     return pt;
+}
+
+// A sample on the map whose corners fall outside the staged region: gather
+// its four corner rows from memory (off-map corners read zeros through the
+// buffer resource) and accumulate them.  Self-contained, so the loads' wait
+// stays inside this rarely taken branch.
+template <typename T>
+__device__ __forceinline__ void far_accumulate(const Geometry& G, const TiledLane& L, __amdgpu_buffer_rsrc_t rin,
+                                               float x, float y, float m, float* acc)
+{
+    const float fx = floorf(x), fy = floorf(y);
+    float w[4];
+    modulated_weights(m, x - fx, y - fy, w);
+    const int x0 = (int)fx, y0 = (int)fy;
+    const bool vx0 = (uint32_t)x0 < (uint32_t)G.W, vx1 = (uint32_t)(x0 + 1) < (uint32_t)G.W;
+    const bool vy0 = (uint32_t)y0 < (uint32_t)G.H, vy1 = (uint32_t)(y0 + 1) < (uint32_t)G.H;
+    const bool vk[4] = {vy0 && vx0, vy0 && vx1, vy1 && vx0, vy1 && vx1};
+    const uint32_t a00 = (uint32_t)y0 * G.in_line_bytes + (uint32_t)x0 * G.in_row_bytes;
+    const uint32_t ck[4] = {0u, G.in_row_bytes, G.in_line_bytes, G.in_line_bytes + G.in_row_bytes};
+    uint32_t raw[4][8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t o0 = vk[k] ? a00 + ck[k] + L.gl_first : kOOB;
+        const uint32_t o1 = vk[k] ? a00 + ck[k] + L.gl_second : kOOB;
+        const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rin, o0, 0, 0);
+        const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rin, o1, 0, 0);
+        raw[k][0] = v0[0]; raw[k][1] = v0[1]; raw[k][2] = v0[2]; raw[k][3] = v0[3];
+        raw[k][4] = v1[0]; raw[k][5] = v1[1]; raw[k][6] = v1[2]; raw[k][7] = v1[3];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) accumulate_corner<T>(raw[k], w[k], acc);
 }
 
 // tiled_fetch for a region holding the whole map, a one-pixel zero border
@@ -744,11 +787,7 @@ __device__ __forceinline__ TiledPoint whole_fetch(const Geometry& G, const Tiled
         pt.raw[k][0] = v0.x; pt.raw[k][1] = v0.y; pt.raw[k][2] = v0.z; pt.raw[k][3] = v0.w;
         pt.raw[k][4] = v1.x; pt.raw[k][5] = v1.y; pt.raw[k][6] = v1.z; pt.raw[k][7] = v1.w;
     }
-    const float mly = mm * ly, mhy = fmaf(-mm, ly, mm);
-    pt.w[0] = fmaf(-mhy, lx, mhy);
-    pt.w[1] = mhy * lx;
-    pt.w[2] = fmaf(-mly, lx, mly);
-    pt.w[3] = mly * lx;
+    modulated_weights(mm, lx, ly, pt.w);
     return pt;
 }
 
@@ -756,17 +795,7 @@ template <typename T, int CPL>
 __device__ __forceinline__ void tiled_accumulate(const TiledPoint& pt, float* acc)
 {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            if constexpr (Elem<T>::bytes == 4) {
-                acc[c] = fmaf(pt.w[k], __uint_as_float(pt.raw[k][c]), acc[c]);
-            } else {
-                acc[2 * c] = fmaf(pt.w[k], Elem<T>::widen(pt.raw[k][c] & 0xffffu), acc[2 * c]);
-                acc[2 * c + 1] = fmaf(pt.w[k], Elem<T>::widen(pt.raw[k][c] >> 16), acc[2 * c + 1]);
-            }
-        }
-    }
+    for (int k = 0; k < 4; ++k) accumulate_corner<T>(pt.raw[k], pt.w[k], acc);
 }
 
 // Image, slab and region origin of one tile (wave-uniform values).
@@ -857,6 +886,14 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
 
     const TileCoord cur = tile_coord(G, tg, xcd_remap(blockIdx.x, gridDim.x));
     stage_rows<NT>(G, tg, a.input, cur, region, 0, tg.RH, t);
+    if constexpr (!WHOLE) {
+        // the 2x2 block of zero pixels after the region (rows RH and RH + 1,
+        // columns 0 and 1 at the region's row stride): 32 lanes, 16 bytes each
+        if (t < 32) {
+            const int k = t >> 3;
+            region[((tg.RH + (k >> 1)) * tg.RW + (k & 1)) * 8 + (t & 7)] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
 
     // ---- this lane: 32 bytes of channels of one output pixel of the tile
     const int p = t >> 2, sub = t & 3;
@@ -890,20 +927,34 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
     L.y_lo = cur.y_lo;
     L.gl_first = cur.slab * 128u + L.lane_first;
     L.gl_second = L.gl_first ^ 16u;
+    set_fast_bounds(L, G, (uint32_t)tg.RH);
     const char* lds = (const char*)region;
+    float acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+    auto acc_ref = [&]() -> float* { return acc; };
 
     auto mval = [&](uint32_t raw) {
         return Elem<T>::bytes == 4 ? __uint_as_float(raw) : Elem<T>::widen(raw);
+    };
+    // one point: its corners from the staged region (the whole-map variant
+    // needs nothing else), plus the memory gather of a sample on the map
+    // beyond the region
+    auto point = [&](float xt, float yt, float2 d, float m) {
+        if constexpr (WHOLE) {
+            tiled_accumulate<T, CPL>(whole_fetch<T>(G, L, lds, xt, yt, d, m), acc_ref());
+        } else {
+            bool far;
+            float x, y;
+            tiled_accumulate<T, CPL>(tiled_fetch<T>(G, L, lds, xt, yt, d, m, far, x, y), acc_ref());
+            if (far) far_accumulate<T>(G, L, rin, x, y, m, acc_ref());
+        }
     };
     float zval = 0.f;
     if constexpr (GATE) {
         // the gate logit, in flight with the record and the region
         if (active) zval = ld1((const T*)a.gate + (size_t)cur.n * G.Ho * G.Wo * G.groups + pg_img);
     }
-    float acc[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
-
     if constexpr (KT > 0) {
         // K fixed: the (pixel, group)'s offset and mask records come in once
         // (a per-point load would re-touch the same cache lines P times)
@@ -935,10 +986,7 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
             if (active) {
                 float m = mval(rec.mask[q]);
                 if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
-                const TiledPoint pt =
-                    WHOLE ? whole_fetch<T>(G, L, lds, xt[q / KT], yt[q % KT], record_pair<T, PK>(rec, q), m)
-                          : tiled_fetch<T>(G, L, lds, rin, xt[q / KT], yt[q % KT], record_pair<T, PK>(rec, q), m);
-                tiled_accumulate<T, CPL>(pt, acc);
+                point(xt[q / KT], yt[q % KT], record_pair<T, PK>(rec, q), m);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -953,42 +1001,20 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
             for (int q = 0; q < P; ++q) sum += __expf(load_mask_value<T>(rmk, vmk, q) - mx);
             inv = 1.0f / sum;
         }
-        auto fetch = [&](int q, const RawPair<T>& d, uint32_t mraw) {
-            float m = mval(mraw);
-            if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
-            const float xt = fmaf(G.alpha, tg.tap_x[q], L.bx), yt = fmaf(G.alpha, tg.tap_y[q], L.by);
-            return WHOLE ? whole_fetch<T>(G, L, lds, xt, yt, widen_pair<T>(d), m)
-                         : tiled_fetch<T>(G, L, lds, rin, xt, yt, widen_pair<T>(d), m);
-        };
-
-        // Software pipeline over the points, two per (rolled) iteration: the
-        // corner reads of point q+1 are in flight while point q accumulates,
-        // and each point's offsets and mask are requested two points ahead.
-        // Rolled, the compiler cannot hoist further points' reads and run
-        // out of registers.
-        RawPair<T> dA, dB;
-        uint32_t mA = 0u, mB = 0u;
-        dA = load_offset_raw<T>(roff, voff, 0, odd);
-        mA = load_mask_raw<T>(rmk, vmk, 0);
-        if (P > 1) { dB = load_offset_raw<T>(roff, voff, 1, odd); mB = load_mask_raw<T>(rmk, vmk, 1); }
-        TiledPoint ptA, ptB;
-        if (active) ptA = fetch(0, dA, mA);
-        if (P > 2) { dA = load_offset_raw<T>(roff, voff, 2, odd); mA = load_mask_raw<T>(rmk, vmk, 2); }
-        int q = 0;
+        // one point per (rolled) iteration; its offset pair and mask value
+        // are requested one point ahead
+        RawPair<T> dn = load_offset_raw<T>(roff, voff, 0, odd);
+        uint32_t mn = load_mask_raw<T>(rmk, vmk, 0);
         DCN_UNROLL(1)
-        for (; q + 1 < P; q += 2) {
-            // here: ptA = point q (reads issued), dB = point q+1, dA = point q+2
-            if (active) ptB = fetch(q + 1, dB, mB);
-            if (q + 3 < P) { dB = load_offset_raw<T>(roff, voff, q + 3, odd); mB = load_mask_raw<T>(rmk, vmk, q + 3); }
-            if (active) tiled_accumulate<T, CPL>(ptA, acc);
-            if (q + 2 < P) {
-                if (active) ptA = fetch(q + 2, dA, mA);
-                if (q + 4 < P) { dA = load_offset_raw<T>(roff, voff, q + 4, odd); mA = load_mask_raw<T>(rmk, vmk, q + 4); }
+        for (int q = 0; q < P; ++q) {
+            const RawPair<T> d = dn;
+            const uint32_t mraw = mn;
+            if (q + 1 < P) { dn = load_offset_raw<T>(roff, voff, q + 1, odd); mn = load_mask_raw<T>(rmk, vmk, q + 1); }
+            if (active) {
+                float m = mval(mraw);
+                if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
+                point(fmaf(G.alpha, tg.tap_x[q], L.bx), fmaf(G.alpha, tg.tap_y[q], L.by), widen_pair<T>(d), m);
             }
-            if (active) tiled_accumulate<T, CPL>(ptB, acc);
-        }
-        if (q < P) {   // odd number of points: the last one is in ptA
-            if (active) tiled_accumulate<T, CPL>(ptA, acc);
         }
     }
 
@@ -1125,9 +1151,12 @@ __global__ __launch_bounds__(kBlock) void dcn_backward_kernel(BwdArgs a)
             gm = group_sum<L>(gm);
             gdx = group_sum<L>(gdx);
             gdy = group_sum<L>(gdy);
+            // a skipped sample has zero gradients whatever its mask value
+            // (an Inf or NaN it never multiplies must not meet the zeros)
             if (!s.inmap) { gm = 0.f; gdx = 0.f; gdy = 0.f; }
+            const float am = s.inmap ? G.alpha * m : 0.f;
             if (act && leader) {
-                *(float2*)(goff + 2 * p) = make_float2(G.alpha * m * gdx, G.alpha * m * gdy);
+                *(float2*)(goff + 2 * p) = make_float2(am * gdx, am * gdy);
                 gmk[p] = gm;
             }
             dot = fmaf(m, gm, dot);
@@ -1208,22 +1237,6 @@ __device__ __forceinline__ float quad_xor1(float v)
 __device__ __forceinline__ float quad_xor2(float v)
 {
     return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-}
-
-// Packed atomic add of two adjacent half-precision elements (each add rounds
-// once to the dtype).
-template <typename T>
-__device__ __forceinline__ void atomic_add_pair(void* p, float x, float y)
-{
-    if constexpr (std::is_same<T, _Float16>::value) {
-        typedef _Float16 v2 __attribute__((ext_vector_type(2)));
-        const v2 v = {(_Float16)x, (_Float16)y};
-        __builtin_amdgcn_global_atomic_fadd_v2f16((__attribute__((address_space(1))) v2*)p, v);
-    } else {
-        typedef __bf16 v2 __attribute__((ext_vector_type(2)));
-        const v2 v = {(__bf16)x, (__bf16)y};
-        __builtin_amdgcn_global_atomic_fadd_v2bf16((__attribute__((address_space(1))) v2*)p, v);
-    }
 }
 
 template <typename T, int KT, int NT, bool SOFTMAX>
@@ -1339,10 +1352,11 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
             gdx = quad_xor2(gdx);
             gdy = quad_xor2(gdy);
         }
+        // a skipped sample has zero gradients whatever its mask value
         if (!pt.inmap) { gm = 0.f; gdx = 0.f; gdy = 0.f; }
         if (active && leader) {
-            const float gd[2] = {G.alpha * m * gdx, G.alpha * m * gdy};
-            store_pair<T>(goff + 2 * q, gd[0], gd[1]);
+            const float am = pt.inmap ? G.alpha * m : 0.f;
+            store_pair<T>(goff + 2 * q, am * gdx, am * gdy);
         }
         // corners beyond the owners' reach: x0 and x0 + 1 both lie within
         // M of the base exactly when x0 - base + M is in [0, 2M) (likewise
@@ -1361,19 +1375,20 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
                                   (uint32_t)(qy - byi + a.near_m) <= M2;
                 if (valid && !near) {
                     const float mw = m * wb[k];
-                    char* px0 = gin + (size_t)qy * G.in_line_bytes + (size_t)qx * G.in_row_bytes;
+                    const size_t pix_el = (size_t)qy * G.W * G.C + (size_t)qx * G.C;   // elements
                     if constexpr (EB == 4) {
+                        float* px0 = (float*)gin + pix_el;
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) atomicAdd((float*)(px0 + L.gl_first) + c, mw * go[c]);
+                        for (int c = 0; c < 4; ++c) atomicAdd(px0 + L.gl_first / 4 + c, mw * go[c]);
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) atomicAdd((float*)(px0 + L.gl_second) + c, mw * go[4 + c]);
+                        for (int c = 0; c < 4; ++c) atomicAdd(px0 + L.gl_second / 4 + c, mw * go[4 + c]);
                     } else {
+                        // binary32 adds into the workspace image of grad_input
+                        float* px0 = a.far_ws + (size_t)cur.n * G.H * G.W * G.C + pix_el;
 #pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            atomic_add_pair<T>(px0 + L.gl_first + 4 * c, mw * go[2 * c], mw * go[2 * c + 1]);
+                        for (int c = 0; c < 8; ++c) atomicAdd(px0 + L.gl_first / 2 + c, mw * go[c]);
 #pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            atomic_add_pair<T>(px0 + L.gl_second + 4 * c, mw * go[8 + 2 * c], mw * go[9 + 2 * c]);
+                        for (int c = 0; c < 8; ++c) atomicAdd(px0 + L.gl_second / 2 + c, mw * go[8 + c]);
                     }
                 }
             }
@@ -1545,7 +1560,23 @@ void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
     const int tw = og.TW < G.W - qx0 ? og.TW : G.W - qx0;     // ragged last column / row of tiles
     const int th = og.TH < G.H - qy0 ? og.TH : G.H - qy0;
 
-    for (int i = t; i < og.TH * og.TW * kOwnerStride; i += NT) owner_tile[i] = 0.f;
+    if (a.gi_init) {
+        // start from the binary32 partial sums already in the workspace (the
+        // corners beyond the owners' reach), 4 floats per lane and step
+        const float* src = a.gi_init + (size_t)n * G.H * G.W * G.C + slab * 32u;
+        for (int i = t; i < og.TH * og.TW * 8; i += NT) {
+            const int px = i >> 3, q4 = i & 7;
+            const int cy = px / og.TW, cx = px - cy * og.TW;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (cy < th && cx < tw)
+                v = *(const float4*)(src + ((size_t)(qy0 + cy) * G.W + (qx0 + cx)) * G.C + q4 * 4);
+            float* dst = owner_tile + px * kOwnerStride + q4 * 4;
+            *(float2*)dst = make_float2(v.x, v.y);
+            *(float2*)(dst + 2) = make_float2(v.z, v.w);
+        }
+    } else {
+        for (int i = t; i < og.TH * og.TW * kOwnerStride; i += NT) owner_tile[i] = 0.f;
+    }
     __syncthreads();
 
     int wlo, whi, hlo, hhi;
@@ -1803,9 +1834,11 @@ __global__ __launch_bounds__(kBlock) void dcn_backward_generic(BwdArgs a, float*
             gm = group_sum_rt(gm, L);
             gdx = group_sum_rt(gdx, L);
             gdy = group_sum_rt(gdy, L);
+            // a skipped sample has zero gradients whatever its mask value
             if (!s.inmap) { gm = 0.f; gdx = 0.f; gdy = 0.f; }
+            const float am = s.inmap ? G.alpha * m : 0.f;
             if (act && leader) {
-                store_pair<T>(goff + 2 * p, G.alpha * m * gdx, G.alpha * m * gdy);
+                store_pair<T>(goff + 2 * p, am * gdx, am * gdy);
                 store<T, EB>(gmk + p, &gm);
             }
             dot = fmaf(m, gm, dot);

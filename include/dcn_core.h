@@ -8,6 +8,7 @@
  *   [V4]  "DCNv4高效实践指南：掌握可变形卷积的3倍速度提升技术"
  *         (DCNv4 practice guide), seekfood.cn
  *   [A100] "告别DCNv3的卡顿：实测DCNv4在A100上3倍提速…", framerc.cn
+ *   [FII] FlashInternImage image-classification guide, m.nxbn.cn
  *
  * The operation ([FB] section 4, steps 1-5; the DCNv4 variant drops the
  * softmax, [V4] core-architecture section, [A100] section 1):
@@ -106,14 +107,10 @@ int dcn_core_forward(const void* input, const void* offset, const void* mask, vo
  * three outputs are overwritten, never accumulated into.  The pages print
  * no gradient formulas; these are the derivatives of the definition.
  * Same arguments and errors as dcn_core_forward.  The arithmetic is binary32
- * for every dtype; each gradient is rounded once to the dtype, except that in
- * half precision a grad_input element that also receives corners far from
- * their sample's base (offsets beyond about 4 pixels times offset_scale) gets
- * them through half-precision atomic adds, one rounding each.  Half precision
- * needs group rows of 32, 64 or 128 bytes, channel rows a multiple of 128
- * bytes, 16-byte aligned input, grad_output and grad_input, stride <= 4 and
- * K <= 7; other half-precision calls return DCN_ERR_UNSUPPORTED here and run in
- * dcn_core_backward_ws with a workspace. */
+ * for every dtype and each gradient is rounded once to the dtype.  This call
+ * takes no workspace, so it serves binary32 only: a half-precision grad_input
+ * is summed in a binary32 workspace, which dcn_core_backward_ws takes from
+ * the caller (DCN_ERR_UNSUPPORTED here for fp16 and bf16). */
 int dcn_core_backward(const void* input, const void* offset, const void* mask,
                       const void* grad_output, void* grad_input, void* grad_offset,
                       void* grad_mask, int N, int H, int W, int G, int Cg, int K, int stride,
@@ -161,26 +158,30 @@ int dcn_core_backward_ex(const void* input, const void* offset, const void* mask
                          void* stream);
 
 /* Bytes of device workspace dcn_core_backward_ws needs for this call: 0 when
- * the call runs without one (binary32, an empty batch, or half precision on
- * the shapes dcn_core_backward takes), else N*H*W*G*Cg*4 (one binary32
- * accumulator per grad_input element).  The pointers are the ones the call
- * will use (only their alignment is read).  Returns minus a dcn_status for
- * invalid arguments. */
+ * the call runs without one (binary32 or an empty batch), else N*H*W*G*Cg*4
+ * (one binary32 accumulator per grad_input element: every half-precision
+ * call).  The pointers are the ones the call will use.  Returns minus a
+ * dcn_status for invalid arguments. */
 long long dcn_core_backward_workspace_size(const void* input, const void* grad_output, const void* grad_input,
                                            int N, int H, int W, int G, int Cg, int K, int stride, int pad,
                                            int dilation, float offset_scale, int flags, int dtype);
 
 /* dcn_core_backward_ex with a caller-owned device workspace (workspace_bytes
- * of it, at least what dcn_core_backward_workspace_size returns, 4-byte
- * aligned; NULL and 0 when none is needed).  It extends half-precision
- * backward to every shape whose channels per group split into a power-of-two
- * number of lanes: each grad_input contribution is added by a binary32 atomic
- * into the zeroed workspace, which is then rounded once into grad_input (the
- * workspace is overwritten; its contents after the call are unspecified).
- * Other shapes behave as in dcn_core_backward_ex.  Returns
- * DCN_ERR_INVALID_ARG for a workspace that is too small or misaligned,
- * DCN_ERR_UNSUPPORTED if one is needed and none is given or if the group
- * width does not split. */
+ * of it, at least what dcn_core_backward_workspace_size returns, 16-byte
+ * aligned; NULL and 0 when none is needed): the half-precision backward
+ * (mixed-precision training is the pages' main use of the core, and [FII]
+ * section 5.3 traces its NaN and loss trouble to half-precision numerics,
+ * so no sum is kept in a half type).  The workspace holds a
+ * binary32 image of grad_input: every contribution to a grad_input element
+ * is summed in binary32 (on-chip per input tile for corners near their
+ * sample's base, binary32 atomics into the workspace for the rest) and the
+ * element is rounded once to the dtype.  The workspace is overwritten; its
+ * contents after the call are unspecified.  Half precision runs on every
+ * shape whose channels per group split into a power-of-two number of lanes.
+ * Binary32 calls ignore the workspace and behave as dcn_core_backward_ex.
+ * Returns DCN_ERR_INVALID_ARG for a workspace that is too small or
+ * misaligned, DCN_ERR_UNSUPPORTED if one is needed and none is given or if
+ * the group width does not split. */
 int dcn_core_backward_ws(const void* input, const void* offset, const void* mask,
                          const void* grad_output, void* grad_input, void* grad_offset,
                          void* grad_mask, int N, int H, int W, int G, int Cg, int K, int stride,

@@ -144,22 +144,30 @@ def test_backward_workspace_entry_points():
     p3 = [vp(0x1000), vp(0x2000), vp(0x3000)]
     geo = (1, 8, 8, 2, 8, 3, 1, 1, 1, ctypes.c_float(1.0), 0)
     assert lib.dcn_core_backward_workspace_size(*p3, *geo, 0) == 0            # binary32 needs none
-    assert lib.dcn_core_backward_workspace_size(*p3, *geo, 1) == 8 * 8 * 16 * 4   # C = 16 half: not tiled
+    assert lib.dcn_core_backward_workspace_size(*p3, *geo, 1) == 8 * 8 * 16 * 4   # C = 16 half
+    geo64 = (2, 8, 8, 4, 16, 3, 1, 1, 1, ctypes.c_float(1.0), 0)
+    assert lib.dcn_core_backward_workspace_size(*p3, *geo64, 2) == 2 * 8 * 8 * 64 * 4   # tiled half too
+    assert lib.dcn_core_backward_workspace_size(*p3, *geo64, 0) == 0
     assert lib.dcn_core_backward_workspace_size(*p3, 1, 8, 8, 2, 8, 0, 1, 1, 1, ctypes.c_float(1.0), 0, 1) == -1
     ptrs = [vp(0x1000 * (i + 1)) for i in range(7)]
     ws = vp(0x100000)
     args = (1, 8, 8, 2, 8, 3, 1, 1, 1, ctypes.c_float(1.0), 0, 1)
     assert lib.dcn_core_backward_ws(*ptrs, *args, ws, 8 * 8 * 16 * 4 - 4, None) == INVALID   # too small
     assert lib.dcn_core_backward_ws(*ptrs, *args, vp(0x100002), 8 * 8 * 16 * 4, None) == INVALID   # misaligned
+    assert lib.dcn_core_backward_ws(*ptrs, *args, vp(0x100008), 8 * 8 * 16 * 4, None) == INVALID   # not 16-byte
     assert lib.dcn_core_backward_ws(*ptrs, *args, None, 0, None) == UNSUPPORTED   # needs one, none given
     assert lib.dcn_core_backward_ws(*ptrs, *args, ws, -1, None) == INVALID
 
 
 def test_backward_validation():
     lib = dcn.load_library()
-    # half precision needs the tiled shapes: C = 16 is not a multiple of 32
+    # half precision sums grad_input in a binary32 workspace, which only
+    # dcn_core_backward_ws takes: the plain call declines fp16 and bf16,
+    # on the tiled channel widths (C = 64) as well
     assert bwd(lib, dtype=1) == UNSUPPORTED
     assert bwd(lib, dtype=2) == UNSUPPORTED
+    assert bwd(lib, dtype=1, G=4, Cg=16) == UNSUPPORTED
+    assert bwd(lib, dtype=2, G=4, Cg=16) == UNSUPPORTED
     assert bwd(lib, K=0) == INVALID
     assert bwd(lib, null=True) == INVALID
     assert bwd(lib, N=0, null=True) == OK

@@ -308,24 +308,20 @@ def oracle_bwd(t, w):
                            coord_mode=oracle.COORD_BINARY32, remove_center=w.remove_center)
 
 
-def check_backward(w, far_roundings=1):
-    """far_roundings (half precision only): roundings of a grad_input partial
-    sum besides the final one -- the owner's binary32 sum is stored once,
-    then each corner beyond the owners' reach is added by a half-precision
-    atomic."""
+def check_backward(w):
+    """Every gradient, element by element; half precision included: its
+    grad_input is a binary32 sum rounded once, which rtol covers."""
     t = inputs.make(w, with_grad=True)
     d = {k: v.to(DEV) for k, v in t.items()}
     gi, goff, gm = dcn.backward(d["input"], d["offset"], d["mask"], d["grad_out"], **cfg_of(w))
     torch.cuda.synchronize()
     r = oracle_bwd(t, w)
     Cg, P = w.Cg, w.P
-    half = w.dtype != "f32"
     stats = {}
-    for key, got, S, n, extra in (("grad_input", gi, r["gi_abs"], r["gi_cnt"], far_roundings if half else 0),
-                                  ("grad_offset", goff, r["goff_abs"], 4 * Cg, 0),
-                                  ("grad_mask", gm, r["gmask_abs"], 4 * Cg * (P + 1) if w.softmax else 4 * Cg, 0)):
-        st = tolerance.compare(got.float().cpu().numpy().reshape(r[key].shape), r[key], S, n, w.dtype,
-                               store_roundings=extra)
+    for key, got, S, n in (("grad_input", gi, r["gi_abs"], r["gi_cnt"]),
+                           ("grad_offset", goff, r["goff_abs"], 4 * Cg),
+                           ("grad_mask", gm, r["gmask_abs"], 4 * Cg * (P + 1) if w.softmax else 4 * Cg)):
+        st = tolerance.compare(got.float().cpu().numpy().reshape(r[key].shape), r[key], S, n, w.dtype)
         assert st["ok"], (w.name, key, st)
         stats[key] = st
     return stats
@@ -391,34 +387,42 @@ def test_backward_owner_sweep(case):
     check_backward(w)
 
 
-# Half-precision backward: binary32 arithmetic, every gradient rounded once
-# to the dtype (grad_input again per far corner, added by a packed atomic).
-HALF_BWD = [  # name, N, H, W, G, Cg, K, stride, pad, dil, alpha, softmax, dtype, sigma, far_roundings
-    ("h_c5_f16", 4, 56, 56, 4, 16, 3, 1, 1, 1, 1.0, False, "f16", 1.5, 1),
-    ("h_c5_bf16", 4, 56, 56, 4, 16, 3, 1, 1, 1, 1.0, False, "bf16", 1.5, 1),
-    ("h_softmax_bf16", 2, 23, 29, 4, 16, 3, 1, 1, 1, 1.0, True, "bf16", 2.0, 1),
-    ("h_k5_f16", 1, 21, 19, 2, 32, 5, 1, 2, 1, 0.8, True, "f16", 2.0, 1),
-    ("h_s2_d2_f16", 1, 25, 23, 4, 16, 3, 2, 2, 2, 1.2, False, "f16", 2.0, 1),
-    ("h_cg32_bf16", 2, 17, 20, 4, 32, 3, 1, 1, 1, -1.1, True, "bf16", 1.5, 1),
-    # offsets far beyond the owners' reach: many corners go through atomics
-    ("h_far_f16", 1, 19, 21, 4, 16, 3, 1, 1, 1, 1.0, False, "f16", 6.0, 40),
+# Half-precision backward on the tiled shapes: binary32 arithmetic, every
+# gradient rounded once to the dtype; corners beyond the owners' reach are
+# summed in the binary32 workspace before the owners round each element.
+HALF_BWD = [  # name, N, H, W, G, Cg, K, stride, pad, dil, alpha, softmax, dtype, sigma
+    ("h_c5_f16", 4, 56, 56, 4, 16, 3, 1, 1, 1, 1.0, False, "f16", 1.5),
+    ("h_c5_bf16", 4, 56, 56, 4, 16, 3, 1, 1, 1, 1.0, False, "bf16", 1.5),
+    ("h_softmax_bf16", 2, 23, 29, 4, 16, 3, 1, 1, 1, 1.0, True, "bf16", 2.0),
+    ("h_k5_f16", 1, 21, 19, 2, 32, 5, 1, 2, 1, 0.8, True, "f16", 2.0),
+    ("h_s2_d2_f16", 1, 25, 23, 4, 16, 3, 2, 2, 2, 1.2, False, "f16", 2.0),
+    ("h_cg32_bf16", 2, 17, 20, 4, 32, 3, 1, 1, 1, -1.1, True, "bf16", 1.5),
+    # offsets far beyond the owners' reach: many corners go through the workspace
+    ("h_far_f16", 1, 19, 21, 4, 16, 3, 1, 1, 1, 1.0, False, "f16", 6.0),
+    ("h_far_bf16", 2, 24, 20, 4, 16, 3, 1, 1, 1, 1.0, True, "bf16", 8.0),
 ]
 
 
 @pytest.mark.parametrize("case", HALF_BWD, ids=lambda c: c[0])
 def test_backward_half_precision(case):
-    name, N, H, W, G, Cg, K, s, p, d, a, sm, dt, sigma, far = case
+    name, N, H, W, G, Cg, K, s, p, d, a, sm, dt, sigma = case
     Ho, Wo = oracle.out_size(H, K, s, p, d), oracle.out_size(W, K, s, p, d)
     w = inputs.Workload(name=name, N=N, H=H, W=W, G=G, Cg=Cg, Ho=Ho, Wo=Wo, K=K, stride=s, pad=p,
                         dilation=d, offset_scale=a, softmax=sm, dtype=dt, offset_sigma=sigma,
                         mask_sigma=1.0 if sm else 0.5, seed_base=94000 + 41 * len(name), backward=True)
-    check_backward(w, far_roundings=far)
+    check_backward(w)
 
 
-def test_backward_half_outside_the_tiled_shapes_needs_the_workspace():
-    """dcn_core_backward itself still declines a half-precision call outside
-    the tiled shapes (C = 16 here); the binding then runs it with a binary32
-    workspace (parity of that path: test_backward_half_generic)."""
+def test_half_backward_full_size_c5_shape():
+    """The c5 shape (N=32, 56x56, C=64) in fp16 and bf16 at full size."""
+    for dt in ("f16", "bf16"):
+        check_backward(inputs.scaled(inputs.WORKLOADS["c5_dcnv4_f32_56_fwdbwd"], dtype=dt))
+
+
+def test_backward_half_needs_the_workspace():
+    """dcn_core_backward (no workspace argument) declines half precision; the
+    binding runs it through dcn_core_backward_ws with a binary32 workspace
+    (parity of that path: test_backward_half_generic and the tiled cases)."""
     import ctypes
     x = torch.randn(1, 8, 8, 16, device=DEV, dtype=torch.float16)
     off = torch.zeros(1, 8, 8, 2 * 9 * 2, device=DEV, dtype=torch.float16)

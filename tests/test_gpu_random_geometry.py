@@ -7,11 +7,10 @@ compares every output with the binary64 oracle, element by element, to the
 bounds of tests/tolerance.py.  The draws are a fixed function of the case
 number, so a failure names a reproducible geometry.
 
-Half-precision grad_input is compared with the worst case of its rounding:
-each of an element's contributions may arrive through a half-precision
-atomic add that rounds once (store_roundings = the oracle's per-element
-contribution count); a softmax grad_mask of half precision carries one more
-rounding (the raw mask gradient stored in the dtype and read back).
+Half-precision grad_input is a binary32 sum rounded once (the bounds' rtol
+covers that rounding, no store_roundings); a softmax grad_mask of half
+precision may carry one more rounding (the untiled kernel stores the raw mask
+gradient in the dtype and reads it back for the Jacobian).
 """
 import random
 import sys
@@ -96,7 +95,7 @@ def test_random_geometry(case):
     r = oracle_bwd(t, w)
     half = w.dtype != "f32"
     for key, got, S, n, extra in (
-            ("grad_input", gi, r["gi_abs"], r["gi_cnt"], r["gi_cnt"] if half else 0),
+            ("grad_input", gi, r["gi_abs"], r["gi_cnt"], 0),
             ("grad_offset", goff, r["goff_abs"], 4 * w.Cg, 0),
             ("grad_mask", gm, r["gmask_abs"], 4 * w.Cg * (w.P + 1) if w.softmax else 4 * w.Cg,
              1 if half and w.softmax else 0)):

@@ -139,8 +139,7 @@ def test_packed_layout(case):
     assert torch.equal(goff_p, goff_s), w.name
     assert torch.equal(gm_p, gm_s), w.name
     r = oracle_bwd(t, w)
-    half = w.dtype != "f32"
-    for key, got, S, n, extra in (("grad_input", gi_p, r["gi_abs"], r["gi_cnt"], 1 if half else 0),
+    for key, got, S, n, extra in (("grad_input", gi_p, r["gi_abs"], r["gi_cnt"], 0),
                                   ("grad_offset", goff_p, r["goff_abs"], 4 * w.Cg, 0),
                                   ("grad_mask", gm_p, r["gmask_abs"],
                                    4 * w.Cg * (w.P + 1) if w.softmax else 4 * w.Cg, 0)):
