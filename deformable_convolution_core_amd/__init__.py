@@ -42,9 +42,10 @@ _DTYPE = {torch.float32: DCN_F32, torch.float16: DCN_F16, torch.bfloat16: DCN_BF
 EXPORTED = ("dcn_core_out_size", "dcn_core_forward", "dcn_core_backward", "dcn_core_forward_ex",
             "dcn_core_backward_ex", "dcn_core_backward_workspace_size", "dcn_core_backward_ws",
             "dcn_center_gate_forward", "dcn_center_gate_backward", "dcn_linear_forward", "dcn_linear_weight_grad", "dcn_linear_weight_grad_workspace_size",
-            "dcn_core_forward_gated",
+            "dcn_core_forward_gated", "dcn_core_backward_static",
             "dcn_status_string")
 FLAG_SOFTMAX, FLAG_REMOVE_CENTER, FLAG_PACKED = 1, 2, 4
+STATIC_SCRATCH_BYTES = 64 << 20   # DCN_STATIC_SCRATCH_BYTES of the C header
 
 
 class DCNError(RuntimeError):
@@ -94,6 +95,8 @@ def load_library(path: str | None = None):
     lib.dcn_linear_weight_grad.restype = i
     lib.dcn_linear_weight_grad_workspace_size.argtypes = [ll, i, i]
     lib.dcn_linear_weight_grad_workspace_size.restype = ll
+    lib.dcn_core_backward_static.argtypes = [vp] * 7 + [i] * 9 + [f, i, i, vp]
+    lib.dcn_core_backward_static.restype = i
     lib.dcn_status_string.argtypes = [i]
     lib.dcn_status_string.restype = ctypes.c_char_p
     if path is None:

@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
@@ -778,6 +779,58 @@ extern "C" int dcn_core_backward(const void* input, const void* offset, const vo
     return backward_call(c, input, offset, mask, grad_output, grad_input, grad_offset, grad_mask, stream);
 }
 
+// ---------------------------------------------------------------------------
+// dcn_core_backward_static: dcn_core_backward_ws with a fixed device array as
+// its workspace, for callers that cannot allocate.  Each GPU the library runs
+// on holds its own copy of the array until the process ends.  Host code must
+// not pass `scratch` itself to a kernel (its host-side name is not a device
+// address); the device address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that pointer is used.
+constexpr long long kScratchBytes = DCN_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxScratchDevices];   // device address of `scratch`, per device
+
+// The current device's copy of the array (looked up on its first use there).
+int device_scratch(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return DCN_ERR_HIP;
+    if (dev < 0 || dev >= kMaxScratchDevices) return DCN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DCN_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return DCN_OK;
+}
+}  // namespace
+
+extern "C" int dcn_core_backward_static(const void* input, const void* offset, const void* mask,
+                                        const void* grad_output, void* grad_input, void* grad_offset,
+                                        void* grad_mask, int N, int H, int W, int G, int Cg, int K, int stride,
+                                        int pad, int dilation, float offset_scale, int flags, int dtype,
+                                        void* stream)
+{
+    Call c;
+    const int rc = validate_ex(c, N, H, W, G, Cg, K, stride, pad, dilation, offset_scale, flags, dtype);
+    if (rc != DCN_OK) return rc;
+    if (dtype == DCN_F32 || N == 0)   // no workspace needed
+        return backward_call(c, input, offset, mask, grad_output, grad_input, grad_offset, grad_mask, stream);
+    const long long need = (long long)N * H * W * G * Cg * 4;
+    if (need > kScratchBytes) return DCN_ERR_SCRATCH_LIMIT;
+    void* ws = nullptr;
+    const int src = device_scratch(&ws);
+    if (src != DCN_OK) return src;
+    return backward_call(c, input, offset, mask, grad_output, grad_input, grad_offset, grad_mask, stream, ws,
+                         kScratchBytes);
+}
+
 extern "C" const char* dcn_status_string(int status)
 {
     switch (status) {
@@ -785,6 +838,9 @@ extern "C" const char* dcn_status_string(int status)
     case DCN_ERR_INVALID_ARG: return "DCN_ERR_INVALID_ARG: invalid size, geometry, dtype, pointer or alignment";
     case DCN_ERR_UNSUPPORTED: return "DCN_ERR_UNSUPPORTED: valid request outside what this build implements";
     case DCN_ERR_HIP: return "DCN_ERR_HIP: the HIP runtime reported an error";
+    case DCN_ERR_SCRATCH_LIMIT:
+        return "DCN_ERR_SCRATCH_LIMIT: the call needs more than the library's static scratch "
+               "(DCN_STATIC_SCRATCH_BYTES); use dcn_core_backward_ws";
     default: return "unknown dcn_status";
     }
 }

@@ -65,7 +65,8 @@ enum dcn_status {
     DCN_OK = 0,
     DCN_ERR_INVALID_ARG = 1,  /* bad size, geometry, dtype or null pointer */
     DCN_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement */
-    DCN_ERR_HIP = 3           /* the HIP runtime reported an error at launch */
+    DCN_ERR_HIP = 3,          /* the HIP runtime reported an error at launch */
+    DCN_ERR_SCRATCH_LIMIT = 4 /* dcn_core_backward_static: larger than its static scratch */
 };
 
 /* Output extent along one axis of a K-tap sampling grid with the given
@@ -187,6 +188,31 @@ int dcn_core_backward_ws(const void* input, const void* offset, const void* mask
                          void* grad_mask, int N, int H, int W, int G, int Cg, int K, int stride,
                          int pad, int dilation, float offset_scale, int flags, int dtype,
                          void* workspace, long long workspace_bytes, void* stream);
+
+/* Size in bytes of dcn_core_backward_static's static scratch. */
+#define DCN_STATIC_SCRATCH_BYTES (64ll << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * dcn_core_backward_ws with the library's own static device array as the
+ * binary32 workspace, so the caller passes only inputs and outputs.  The
+ * array is DCN_STATIC_SCRATCH_BYTES (64 MiB: a half-precision call with
+ * N*H*W*G*Cg up to 16,777,216 elements); each GPU holds its own
+ * copy from the library's first use of it on that device (the device current
+ * when the call is made, which must be the stream's) until the process ends.
+ * The call allocates and frees nothing.  Every call on one GPU shares that
+ * GPU's array, which keeps the last call's contents (each call clears what it
+ * needs with a kernel on `stream`): calls that overlap on one GPU -- on two
+ * streams, or from two host threads -- race and give wrong gradients; calls
+ * on different GPUs do not.  Binary32 calls and N == 0 use no scratch and
+ * behave as dcn_core_backward_ex.  Same arguments, results and errors as
+ * dcn_core_backward_ws, plus DCN_ERR_SCRATCH_LIMIT for a call that needs
+ * more than the array. */
+int dcn_core_backward_static(const void* input, const void* offset, const void* mask,
+                             const void* grad_output, void* grad_input, void* grad_offset,
+                             void* grad_mask, int N, int H, int W, int G, int Cg, int K, int stride,
+                             int pad, int dilation, float offset_scale, int flags, int dtype,
+                             void* stream);
 
 /* dcn_core_forward_ex followed by the DCNv4 layer's centre-feature gate
  * (dcn_center_gate_forward) in one pass, for the layer's geometry: odd K,

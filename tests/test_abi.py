@@ -277,10 +277,26 @@ def test_layer_rejects_grid_changing_geometry():
     assert layer.center_feature_scale_proj.out_features == 4
 
 
+def test_static_scratch_backward_rejects_on_the_host():
+    """dcn_core_backward_static validates before any HIP call: invalid
+    arguments, and half-precision calls whose binary32 image of grad_input
+    exceeds the static scratch (64 MiB), come back without a launch."""
+    lib = dcn.load_library()
+    vp = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(7)]
+    f = ctypes.c_float(1.0)
+    # 64 x 56 x 56 x 128 half elements need 102.8 MB of binary32 accumulators
+    assert lib.dcn_core_backward_static(*vp, 64, 56, 56, 8, 16, 3, 1, 1, 1, f, 0, 1, None) == 4
+    assert lib.dcn_core_backward_static(*vp, 64, 56, 56, 8, 16, 3, 1, 1, 1, f, 0, 2, None) == 4
+    assert dcn.STATIC_SCRATCH_BYTES == 64 << 20
+    assert lib.dcn_core_backward_static(*vp, 1, 8, 8, 2, 8, 0, 1, 1, 1, f, 0, 1, None) == INVALID   # K = 0
+    assert lib.dcn_core_backward_static(*vp, 1, 8, 8, 2, 8, 3, 1, 1, 1, f, 8, 1, None) == INVALID   # bad flag
+    assert lib.dcn_core_backward_static(*vp, 0, 8, 8, 2, 8, 3, 1, 1, 1, f, 0, 1, None) == OK        # empty batch
+
+
 def test_status_strings():
     lib = dcn.load_library()
     for code, prefix in ((0, b"DCN_OK"), (1, b"DCN_ERR_INVALID_ARG"), (2, b"DCN_ERR_UNSUPPORTED"),
-                         (3, b"DCN_ERR_HIP"), (99, b"unknown")):
+                         (3, b"DCN_ERR_HIP"), (4, b"DCN_ERR_SCRATCH_LIMIT"), (99, b"unknown")):
         assert lib.dcn_status_string(code).startswith(prefix)
 
 
