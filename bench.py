@@ -3,23 +3,29 @@
 
 Headline: DCN core forward effective GB/s (input + offset + mask + output
 bytes per launch / launch time), as a fraction of the 8 TB/s HBM3E peak, and
-Gsamples/s, on the FlashInternImage-T stage-1 shape (DCNv4, fp16 with fp32
-accumulation, N=64, 56x56, C=64, G=4, K=3).  One step = one forward launch
-over the whole batch.  Beside it, in the same JSON line: the bf16 sweep over
-the four FlashInternImage-T stage shapes, the core op of a whole
-FlashInternImage-T forward (the stage shapes at their depths, 30 launches),
-the DCNv3 large-channel stage at stride 1 and 2, the DCNv4 stage-1 shapes
-with DCNv4's packed offset+mask tensor, the fp32 forward + backward, the
-half-precision backward, the whole DCNv4 layer around the core (projections,
-core, centre-feature gate) at the headline shape, and the CPU oracle timed on
-the host cores.
+Gsamples/s, on the FlashInternImage-T stage-1 shape in bf16 (DCNv4 with
+fp32 accumulation, N=64, 56x56, C=64, G=4, K=3, offsets N(0, 2^2) px).  One
+step = one forward launch over the whole batch.  Beside it, in the same JSON
+line: the byte-weighted aggregate of the bf16 sweep over the four
+FlashInternImage-T stage shapes (and each stage), the same shape in fp16,
+the core op of a whole FlashInternImage-T forward (the stage shapes at their
+depths, 30 launches), the DCNv3 large-channel stage at stride 1 and 2, the
+DCNv4 stage-1 shapes with DCNv4's packed offset+mask tensor, the fp32
+forward + backward and the half-precision backward, the whole DCNv4 layer
+around the core (projections, core, centre-feature gate) at the fp16 shape,
+and the CPU oracle timed on the host cores (which also checks the headline
+batch element by element).
 
 Inputs are seeded synthetic tensors (no dataset, no weights).  Timing uses
 R rotating copies of every tensor (R * bytes > 512 MB, twice the 256 MB
 Infinity Cache) so each launch reads its inputs from HBM, and the K timed
 launches are captured in one HIP graph replayed between two events on the
 stream the kernels run on, so host launch overhead does not pad the small
-kernels.  Eager-launch timing is reported too.
+kernels.  Eager-launch timing is reported too, with the p10 / median / p90
+of the launches timed one by one.  Per-workload rocprofv3 counters (HBM
+bytes, L2 hit, VALU busy and instruction counts, occupancy, LDS use) come
+from the committed profiles/traffic_counters.json when it was taken on the
+current kernel sources.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 """
@@ -127,9 +133,15 @@ def launcher(w, backward=False, packed=False):
     return bwd if backward else fwd
 
 
+LAST_SPREAD = {}
+
+
 def time_launches(w, steps, warmup, backward=False, packed=False):
     """Mean per-launch time (ms) of `steps` launches over rotating buffers:
-    graph-replayed (primary) and eager."""
+    graph-replayed (primary) and eager.  The eager launches are also timed
+    one by one (an event after each, on the kernels' stream; the host runs
+    ahead, so consecutive events bracket one kernel each): their p10, median
+    and p90 land in LAST_SPREAD."""
     sets = rotating_sets(w, backward, packed)
     R = len(sets)
     launch = launcher(w, backward, packed)
@@ -140,13 +152,18 @@ def time_launches(w, steps, warmup, backward=False, packed=False):
             launch(sets[i % R], h)
         torch.cuda.synchronize()
         # eager
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
         for i in range(steps):
             launch(sets[i % R], h)
-        e1.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        eager_ms = e0.elapsed_time(e1) / steps
+        eager_ms = ev[0].elapsed_time(ev[-1]) / steps
+        each = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        q = lambda f: each[min(len(each) - 1, int(f * len(each)))]
+        LAST_SPREAD.clear()
+        LAST_SPREAD.update(p10_us=round(q(0.1) * 1e3, 3), median_us=round(q(0.5) * 1e3, 3),
+                           p90_us=round(q(0.9) * 1e3, 3))
     # graph of exactly `steps` launches
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
@@ -172,14 +189,18 @@ def time_launches(w, steps, warmup, backward=False, packed=False):
 def forward_record(w, steps, warmup, packed=False):
     ms, eager_ms, R = time_launches(w, steps, warmup, packed=packed)
     gbps = w.min_bytes_forward() / (ms * 1e-3) / 1e9
-    return dict(workload=w.name, dtype=w.dtype, softmax=bool(w.softmax),
-                layout="packed offset+mask" if packed else "separate offset and mask",
-                shape=dict(N=w.N, H=w.H, W=w.W, C=w.C, G=w.G, Cg=w.Cg, K=w.K, stride=w.stride,
-                           Ho=w.Ho, Wo=w.Wo),
-                us=round(ms * 1e3, 3), eager_us=round(eager_ms * 1e3, 3),
-                min_bytes=w.min_bytes_forward(), GBps=round(gbps, 1),
-                frac_hbm=round(gbps / HBM_PEAK_GBPS, 4),
-                Gsamples_s=round(w.samples() / (ms * 1e-3) / 1e9, 3), rotating_sets=R)
+    rec = dict(workload=w.name, dtype=w.dtype, softmax=bool(w.softmax),
+               layout="packed offset+mask" if packed else "separate offset and mask",
+               shape=dict(N=w.N, H=w.H, W=w.W, C=w.C, G=w.G, Cg=w.Cg, K=w.K, stride=w.stride,
+                          Ho=w.Ho, Wo=w.Wo),
+               us=round(ms * 1e3, 3), eager_us=round(eager_ms * 1e3, 3), eager_each=dict(LAST_SPREAD),
+               min_bytes=w.min_bytes_forward(), GBps=round(gbps, 1),
+               frac_hbm=round(gbps / HBM_PEAK_GBPS, 4),
+               Gsamples_s=round(w.samples() / (ms * 1e-3) / 1e9, 3), rotating_sets=R)
+    if not packed:
+        rec["counters"] = counter_record(w.name)
+        rec["valu"] = valu_record(w.name, ms)
+    return rec
 
 
 FII_T_DEPTHS = (4, 4, 18, 4)   # DCN layers per FlashInternImage-T stage (the T config's depths)
@@ -366,10 +387,24 @@ def cpu_baseline(w):
             break
     per = el / reps
     cores = oracle.max_threads()
+    # the same batch through the HIP path, compared element by element with
+    # the oracle (binary32 coordinates, the kernels' contract)
+    from tests import tolerance
+    ref, S = oracle.forward(x, o, m, **dict(kw, with_absum=True), coord_mode=oracle.COORD_BINARY32)
+    lib = dcn.load_library()
+    d = {k: v.to("cuda") for k, v in t.items()}
+    out = dcn.forward(d["input"], d["offset"], d["mask"], kernel_size=w.K, stride=w.stride, pad=w.pad,
+                      dilation=w.dilation, offset_scale=w.offset_scale, softmax=w.softmax, group=w.G)
+    torch.cuda.synchronize()
+    st = tolerance.compare(out.float().cpu().numpy(), ref, S, 4 * w.P, w.dtype)
+    del lib
     return dict(value=round(w.min_bytes_forward() / per / 1e9, 3), unit="GB/s", cores=cores,
                 kind="oracle", cpu_model=cpu_model(),
                 sample=f"{reps} full batches of {w.name} (N={w.N}), binary64 C loops with OpenMP, "
-                       f"{per * 1e3:.1f} ms per batch")
+                       f"{per * 1e3:.1f} ms per batch",
+                parity=dict(ok=st["ok"], max_ratio=round(st["max_ratio"], 4), norm_rel=st["norm_rel"],
+                            n_bad=st["n_bad"], n=st["n"],
+                            bound="|gpu - ref| <= 2e-2 |ref| + (n_terms + 32) 2^-24 S per element"))
 
 
 def _counters(name):
@@ -386,6 +421,20 @@ def _counters(name):
     return d.get("workloads", {}).get(name)
 
 
+def backward_counter_record(name, dtype):
+    """Per-kernel counters of the backward at workload `name` in `dtype`
+    (owner and gradient kernels) from the committed record, or None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except ValueError:
+        return None
+    if d.get("kernel_hash") != kernel_hash():
+        return None
+    return d.get("backward", {}).get(f"{name}@{dtype}")
+
+
 def traffic_record(name, min_bytes):
     """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     counters, if they were taken on the current kernel sources."""
@@ -393,13 +442,38 @@ def traffic_record(name, min_bytes):
     return None if e is None else e.get("hbm_bytes_per_launch")
 
 
+COUNTER_KEYS = ("valu_busy_pct", "occupancy_pct", "lds_util_pct", "l2_hit", "hbm_bytes_per_launch",
+                "sq_insts_valu", "sq_insts_lds", "sq_waves")
+
+
 def counter_record(name):
-    """VALU busy, occupancy, LDS utilisation and L2 hit rate of the workload's
-    kernel from the same committed counters (None if stale or missing)."""
+    """VALU busy, occupancy, LDS utilisation, L2 hit rate, HBM bytes and
+    instruction counts of the workload's kernel from the committed rocprofv3
+    counters (None if stale or missing)."""
     e = _counters(name)
     if e is None:
         return None
-    return {k: e.get(k) for k in ("valu_busy_pct", "occupancy_pct", "lds_util_pct", "l2_hit")}
+    return {k: e.get(k) for k in COUNTER_KEYS if k in e}
+
+
+# VALU issue ceiling: 1024 SIMDs (256 CUs x 4) at 2.4 GHz, one wave64
+# instruction per SIMD every 4 clocks (16 lanes per clock).
+VALU_PEAK_G = 1024 * 2.4 / 4.0
+
+
+def valu_record(name, ms):
+    """The workload's VALU wave-instructions per launch (SQ_INSTS_VALU from the
+    committed counters) issued at the measured launch time, against the
+    16-lane issue ceiling.  On this GPU plain binary32 fma/add/mul and bitwise
+    ops with VGPR operands issue up to ~1.45x that ceiling and the
+    mixed-precision, convert and shift ops at ~0.85-0.93x (measured), so the
+    fraction is an issue-rate figure, not a hard bound."""
+    e = _counters(name)
+    if e is None or not e.get("sq_insts_valu"):
+        return None
+    g = e["sq_insts_valu"] / (ms * 1e-3) / 1e9
+    return dict(insts=e["sq_insts_valu"], achieved=round(g, 1), peak=VALU_PEAK_G, unit="G wave-instr/s",
+                frac=round(g / VALU_PEAK_G, 4))
 
 
 def copy_bandwidth(mb=1024, steps=20):
@@ -487,52 +561,51 @@ def main():
 
     extra = {"copy_bandwidth": cp, "frac_measured_copy": round(head["GBps"] / cp["GBps"], 4)}
     if not args.quick:
-        sweep = []
-        for name in inputs.BF16_SWEEP:
-            r = forward_record(inputs.WORKLOADS[name], args.steps, args.warmup)
-            log(f"{name}: {r['us']} us, {r['GBps']} GB/s")
-            sweep.append(r)
+        # the bf16 FlashInternImage-T stage sweep; its byte-weighted aggregate
+        # stands beside the headline (its first stage)
+        sweep = [head if name == w.name else forward_record(inputs.WORKLOADS[name], args.steps, args.warmup)
+                 for name in inputs.BF16_SWEEP]
+        for r in sweep:
+            log(f"{r['workload']}: {r['us']} us, {r['GBps']} GB/s")
         tot_bytes = sum(r["min_bytes"] for r in sweep)
         tot_us = sum(r["us"] for r in sweep)
         extra["bf16_sweep"] = sweep
         extra["bf16_sweep_aggregate"] = dict(
             min_bytes=tot_bytes, us=round(tot_us, 3), GBps=round(tot_bytes / tot_us / 1e3, 1),
             frac_hbm=round(tot_bytes / tot_us / 1e3 / HBM_PEAK_GBPS, 4))
+        log(f"bf16 sweep aggregate {extra['bf16_sweep_aggregate']['GBps']} GB/s "
+            f"({extra['bf16_sweep_aggregate']['frac_hbm']} of HBM)")
         others = []
-        for name in ("c4s1_dcnv3_bf16_128", "c4s2_dcnv3_bf16_128", "c5_dcnv4_f32_56_fwdbwd"):
+        for name in ("c2_dcnv4_f16_56", "c4s1_dcnv3_bf16_128", "c4s2_dcnv3_bf16_128", "c5_dcnv4_f32_56_fwdbwd"):
             r = forward_record(inputs.WORKLOADS[name], args.steps, args.warmup)
             log(f"{name}: {r['us']} us, {r['GBps']} GB/s")
             others.append(r)
         extra["other_forward"] = others
         # DCNv4's own tensor layout: offsets and mask in one record per (pixel, group)
         packed = []
-        for name in (inputs.HEADLINE, "c3a_dcnv4_bf16_56"):
+        for name in ("c2_dcnv4_f16_56", "c3a_dcnv4_bf16_56"):
             r = forward_record(inputs.WORKLOADS[name], args.steps, args.warmup, packed=True)
             log(f"{name} packed: {r['us']} us, {r['GBps']} GB/s")
             packed.append(r)
         extra["packed_forward"] = packed
         w5 = inputs.WORKLOADS["c5_dcnv4_f32_56_fwdbwd"]
-        bms, beager, R = time_launches(w5, max(20, args.steps // 4), min(args.warmup, 10), backward=True)
-        extra["backward"] = dict(workload=w5.name, us=round(bms * 1e3, 3), eager_us=round(beager * 1e3, 3),
-                                 min_bytes=w5.min_bytes_backward(),
-                                 GBps=round(w5.min_bytes_backward() / (bms * 1e-3) / 1e9, 1),
-                                 frac_hbm=round(w5.min_bytes_backward() / (bms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4))
-        log(f"backward {w5.name} f32: {extra['backward']['us']} us")
-        # the same shape in half precision (binary32 arithmetic, half storage)
-        halves = []
-        for dt in ("f16", "bf16"):
-            wh = inputs.scaled(w5, dtype=dt)
-            hms, heager, _ = time_launches(wh, max(20, args.steps // 4), min(args.warmup, 10), backward=True)
-            halves.append(dict(workload=f"{w5.name} ({dt})", dtype=dt, us=round(hms * 1e3, 3),
-                               eager_us=round(heager * 1e3, 3), min_bytes=wh.min_bytes_backward(),
-                               GBps=round(wh.min_bytes_backward() / (hms * 1e-3) / 1e9, 1),
-                               frac_hbm=round(wh.min_bytes_backward() / (hms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)))
-            log(f"backward {w5.name} {dt}: {halves[-1]['us']} us")
-        extra["backward_half"] = halves
-        lay = layer_record(inputs.WORKLOADS[inputs.HEADLINE], max(20, args.steps // 4), 5)
+        bwd = []
+        for dt in ("f32", "f16", "bf16"):
+            wb = w5 if dt == "f32" else inputs.scaled(w5, dtype=dt)
+            bms, beager, R = time_launches(wb, max(20, args.steps // 4), min(args.warmup, 10), backward=True)
+            bwd.append(dict(workload=f"{w5.name} ({dt})", dtype=dt, us=round(bms * 1e3, 3),
+                            eager_us=round(beager * 1e3, 3), eager_each=dict(LAST_SPREAD),
+                            min_bytes=wb.min_bytes_backward(),
+                            GBps=round(wb.min_bytes_backward() / (bms * 1e-3) / 1e9, 1),
+                            frac_hbm=round(wb.min_bytes_backward() / (bms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                            counters=backward_counter_record(w5.name, dt)))
+            log(f"backward {w5.name} {dt}: {bwd[-1]['us']} us")
+        extra["backward"] = bwd[0]
+        extra["backward_half"] = bwd[1:]
+        lay = layer_record(inputs.WORKLOADS["c2_dcnv4_f16_56"], max(20, args.steps // 4), 5)
         extra["dcnv4_layer"] = lay
-        log(f"DCNv4 layer at {inputs.HEADLINE}: forward {lay['forward_us']} us, forward+backward {lay['forward_backward_us_eager']} us "
-            f"eager, {lay['forward_backward_us_graph']} us in a graph; "
+        log(f"DCNv4 layer at c2_dcnv4_f16_56: forward {lay['forward_us']} us, forward+backward "
+            f"{lay['forward_backward_us_eager']} us eager, {lay['forward_backward_us_graph']} us in a graph; "
             f"gate {lay['gate_kernel']['us']} us ({lay['gate_kernel']['GBps']} GB/s); value projection "
             f"{lay['value_projection']['us']} us ({lay['value_projection']['GBps']} GB/s, platform BLAS "
             f"{lay['value_projection']['platform_blas_us']} us); offset+mask weight gradient "
@@ -545,8 +618,9 @@ def main():
     cpu = None
     if not args.quick and not args.no_cpu_baseline:
         cpu = cpu_baseline(w)
-        log(f"cpu oracle {cpu['value']} GB/s on {cpu['cores']} threads")
+        log(f"cpu oracle {cpu['value']} GB/s on {cpu['cores']} threads; headline parity {cpu.get('parity')}")
 
+    agg = extra.get("bf16_sweep_aggregate")
     line = {
         "metric": METRIC,
         "value": head["GBps"],
@@ -560,17 +634,22 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: DCNv4 core forward, fp16 in/out with fp32 accumulation, "
+        "config": {"workload": f"{w.name}: DCNv4 core forward, {w.dtype} in/out with fp32 accumulation, "
                                f"N={w.N}, {w.H}x{w.W}, C={w.C}, G={w.G} (Cg={w.Cg}), K={w.K}, "
-                               f"stride {w.stride}, pad {w.pad}, raw mask",
+                               f"stride {w.stride}, pad {w.pad}, raw mask, offsets N(0, {w.offset_sigma}^2) px "
+                               f"(FlashInternImage-T stage 1)",
                    "global_batch": w.N, "parallelism": "single GPU"},
         "Gsamples_s": head["Gsamples_s"],
         "frac_hbm_peak": head["frac_hbm"],
+        "headline_aggregate": None if agg is None else dict(
+            workload="bf16 FlashInternImage-T stage sweep (56/28/14/7 px), byte-weighted", **agg),
         "eager_ms_per_step": round(head["eager_us"] / 1e3, 6),
+        "eager_each": head["eager_each"],
         "roofline": {"bound": "hbm", "achieved": head["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": head["frac_hbm"],
-                     "traffic": traffic_record(w.name, head["min_bytes"])},
-        "counters": counter_record(w.name),
+                     "traffic": traffic_record(w.name, head["min_bytes"]),
+                     "valu": head.get("valu")},
+        "counters": head.get("counters"),
         "cpu_baseline": cpu,
         "kernel_hash": kernel_hash(),
     }

@@ -71,7 +71,14 @@ template <> struct Elem<float> {
 template <> struct Elem<_Float16> {
     static constexpr int bytes = 2;
     __device__ static float widen(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)u); }
-    __device__ static uint32_t narrow(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+    // The value is pinned first: the compiler may otherwise fuse the last
+    // binary32 fma of a sum with this conversion (v_fma_mixlo_f16, one
+    // rounding straight to fp16), which is not "a binary32 sum rounded once".
+    __device__ static uint32_t narrow(float f)
+    {
+        asm volatile("" : "+v"(f));
+        return __builtin_bit_cast(uint16_t, (_Float16)f);
+    }
 };
 template <> struct Elem<__bf16> {
     static constexpr int bytes = 2;
@@ -634,11 +641,14 @@ struct TiledPoint {
     float w[4];
 };
 
-// Per-lane constants of the tiled kernel's compute phase.
+// Per-lane constants of the tiled kernel's compute phase.  The point loop
+// reads the uniform ones from VGPR copies (vgpr_copy): on gfx950 a VALU
+// instruction with an SGPR operand issues at about 0.6x the rate of the same
+// instruction with VGPR operands only.
 struct TiledLane {
     float bx, by;                 // sampling centre (absolute input coordinates)
     int x_lo, y_lo;               // staged region origin
-    uint32_t xlim, ylim;          // RW-1, RH-1
+    uint32_t xlim, ylim;          // RW-1, RH-1 (the gradient kernel's region test)
     uint32_t lane_first;          // this lane's first 16-byte slot in a pixel slab
     uint32_t RW, RWB;             // region width in pixels and in bytes
     uint32_t gl_first, gl_second; // the two halves inside an input pixel row
@@ -647,8 +657,34 @@ struct TiledLane {
     // lie in the staged region (x_lo <= floor(x) <= x_lo + RW - 2).  A NaN
     // coordinate fails them.
     float lox, hix, loy, hiy;
+    float w_f, h_f;               // W, H
+    float alpha;
+    float rwb_f, addr_base;       // LDS address of pixel (fy, fx) = fy*rwb_f + fx*128 + addr_base
     uint32_t zero_a0;             // this lane's slot in a 2x2 block of zero pixels
 };
+
+// A uniform value copied into a VGPR the compiler cannot see through.
+__device__ __forceinline__ float vgpr_copy(float s)
+{
+    float v;
+    asm volatile("" : "=v"(v) : "0"(s));
+    return v;
+}
+__device__ __forceinline__ uint32_t vgpr_copy(uint32_t s)
+{
+    uint32_t v;
+    asm volatile("" : "=v"(v) : "0"(s));
+    return v;
+}
+
+// v_cvt_u32_f32: in-range non-negative integers convert exactly; anything
+// else (NaN, negative, huge) gives some value the caller then discards.
+__device__ __forceinline__ uint32_t cvt_u32(float x)
+{
+    uint32_t r;
+    asm("v_cvt_u32_f32 %0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
 
 // Strict lower bound equivalent to "x >= lo and x > -1" for an integer lo:
 // the float just below lo (lo >= 1), -1 (lo <= -1).  For lo = 0 the bound is
@@ -659,14 +695,36 @@ __device__ __forceinline__ float fast_lower_bound(int lo)
     return lo >= 1 ? __int_as_float(__float_as_int((float)lo) - 1) : (lo == 0 ? -0.0f : -1.0f);
 }
 
-__device__ __forceinline__ void set_fast_bounds(TiledLane& L, const Geometry& G, uint32_t RH)
+// whole: the region is the whole map with a one-pixel zero border (origin
+// -1, -1) and two zero rows below it, so every sample on the map is inside
+// it and the zero block is rows H + 1, H + 2 of the region; otherwise the
+// zero block follows the region's RH rows.
+__device__ __forceinline__ void set_fast_bounds(TiledLane& L, const Geometry& G, uint32_t RH, bool whole)
 {
-    L.lox = fast_lower_bound(L.x_lo);
-    L.loy = fast_lower_bound(L.y_lo);
-    const int hx = L.x_lo + (int)L.RW - 1, hy = L.y_lo + (int)RH - 1;
-    L.hix = (float)(hx < G.W ? hx : G.W);
-    L.hiy = (float)(hy < G.H ? hy : G.H);
-    L.zero_a0 = RH * L.RWB + L.lane_first;
+    if (whole) {
+        L.lox = -1.0f;
+        L.loy = -1.0f;
+        L.hix = (float)G.W;
+        L.hiy = (float)G.H;
+        L.zero_a0 = (uint32_t)(G.H + 1) * L.RWB + L.lane_first;
+    } else {
+        L.lox = fast_lower_bound(L.x_lo);
+        L.loy = fast_lower_bound(L.y_lo);
+        const int hx = L.x_lo + (int)L.RW - 1, hy = L.y_lo + (int)RH - 1;
+        L.hix = (float)(hx < G.W ? hx : G.W);
+        L.hiy = (float)(hy < G.H ? hy : G.H);
+        L.zero_a0 = RH * L.RWB + L.lane_first;
+    }
+    L.lox = vgpr_copy(L.lox);
+    L.loy = vgpr_copy(L.loy);
+    L.hix = vgpr_copy(L.hix);
+    L.hiy = vgpr_copy(L.hiy);
+    L.zero_a0 = vgpr_copy(L.zero_a0);
+    L.w_f = vgpr_copy((float)G.W);
+    L.h_f = vgpr_copy((float)G.H);
+    L.alpha = vgpr_copy(G.alpha);
+    L.rwb_f = vgpr_copy((float)L.RWB);
+    L.addr_base = (float)L.lane_first - (float)L.y_lo * (float)L.RWB - (float)L.x_lo * 128.0f;
 }
 
 // Bilinear weights with the modulation folded in; each is formed with
@@ -699,33 +757,48 @@ __device__ __forceinline__ void accumulate_corner(const uint32_t (&raw)[8], floa
 // A sample that the region does not serve -- off the map (the definition
 // skips it), NaN, or on the map beyond the region -- reads the block of
 // zeros with zero weights instead, so an Inf or NaN in the input can never
-// meet a zero weight here; far is set for the last kind, whose corners the
-// caller gathers from memory (far_accumulate).  xt, yt: the tap's part of
-// the coordinates, fmaf(alpha, tap, base).
-template <typename T>
-__device__ __forceinline__ TiledPoint tiled_fetch(const Geometry& G, const TiledLane& L, const char* lds, float xt,
-                                                  float yt, float2 d, float m, bool& far, float& x, float& y)
+// meet a zero weight here; far is set for the last kind (never in a
+// whole-map region), whose corners the caller gathers from memory
+// (far_accumulate).  xt, yt: the tap's part of the coordinates,
+// fmaf(alpha, tap, base).  Floor and fraction come from the absolute
+// coordinate; the LDS address is formed in binary32 from the floors, exactly
+// (every term is an integer below 2^24).
+template <typename T, bool WHOLE>
+__device__ __forceinline__ TiledPoint tiled_fetch(const TiledLane& L, const char* lds, float xt, float yt, float2 d,
+                                                  float m, bool& far, float& x, float& y)
 {
     TiledPoint pt;
-    x = fmaf(G.alpha, d.x, xt);
-    y = fmaf(G.alpha, d.y, yt);
+    x = fmaf(L.alpha, d.x, xt);
+    y = fmaf(L.alpha, d.y, yt);
+    const float fx = floorf(x), fy = floorf(y);
     const bool ok = (x > L.lox) & (x < L.hix) & (y > L.loy) & (y < L.hiy);
-    // Floor and fraction come from the absolute coordinate (x - x_lo is not
-    // exact when x_lo < 0).
-    const uint32_t ix = (uint32_t)(cvt_flr(x) - L.x_lo), iy = (uint32_t)(cvt_flr(y) - L.y_lo);
-    const uint32_t a0 = ok ? (__umul24(iy, L.RW) + ix) * 128u + L.lane_first : L.zero_a0;
-    const uint32_t a1 = a0 ^ 16u;
-    const uint32_t ca[4] = {0u, 128u, L.RWB, L.RWB + 128u};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint4 v0 = *(const uint4*)(lds + a0 + ca[k]);
-        const uint4 v1 = *(const uint4*)(lds + a1 + ca[k]);
-        pt.raw[k][0] = v0.x; pt.raw[k][1] = v0.y; pt.raw[k][2] = v0.z; pt.raw[k][3] = v0.w;
-        pt.raw[k][4] = v1.x; pt.raw[k][5] = v1.y; pt.raw[k][6] = v1.z; pt.raw[k][7] = v1.w;
+    float lx = x - fx, ly = y - fy, mm = m;
+    uint32_t a0 = cvt_u32(fmaf(fy, L.rwb_f, fmaf(fx, 128.0f, L.addr_base)));
+    far = false;
+    if (!ok) {
+        a0 = L.zero_a0;
+        lx = 0.f;
+        ly = 0.f;
+        mm = 0.f;
+        if constexpr (!WHOLE) far = (x > -1.0f) & (x < L.w_f) & (y > -1.0f) & (y < L.h_f);
     }
-    const float lx = ok ? __builtin_amdgcn_fractf(x) : 0.f, ly = ok ? __builtin_amdgcn_fractf(y) : 0.f;
-    far = !ok && x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H;
-    modulated_weights(ok ? m : 0.f, lx, ly, pt.w);
+    const uint32_t a1 = a0 ^ 16u;
+    const uint32_t b0 = a0 + L.RWB, b1 = a1 + L.RWB;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t p0 = k ? b0 : a0, p1 = k ? b1 : a1;
+        const uint4 v00 = *(const uint4*)(lds + p0);
+        const uint4 v01 = *(const uint4*)(lds + p1);
+        const uint4 v10 = *(const uint4*)(lds + p0 + 128u);
+        const uint4 v11 = *(const uint4*)(lds + p1 + 128u);
+        uint32_t* r0 = pt.raw[2 * k];
+        uint32_t* r1 = pt.raw[2 * k + 1];
+        r0[0] = v00.x; r0[1] = v00.y; r0[2] = v00.z; r0[3] = v00.w;
+        r0[4] = v01.x; r0[5] = v01.y; r0[6] = v01.z; r0[7] = v01.w;
+        r1[0] = v10.x; r1[1] = v10.y; r1[2] = v10.z; r1[3] = v10.w;
+        r1[4] = v11.x; r1[5] = v11.y; r1[6] = v11.z; r1[7] = v11.w;
+    }
+    modulated_weights(mm, lx, ly, pt.w);
     return pt;
 }
 
@@ -760,35 +833,22 @@ __device__ __forceinline__ void far_accumulate(const Geometry& G, const TiledLan
     for (int k = 0; k < 4; ++k) accumulate_corner<T>(raw[k], w[k], acc);
 }
 
-// tiled_fetch for a region holding the whole map, a one-pixel zero border
-// and one more zero row (origin -1, -1; rows H and H + 1 are zero): every
-// sample with a corner on the map is inside it, and any other sample (or a
-// NaN coordinate) reads the 2x2 block of zeros at the bottom-left with zero
-// weights.  No branch, no gather from memory.
-template <typename T>
-__device__ __forceinline__ TiledPoint whole_fetch(const Geometry& G, const TiledLane& L, const char* lds, float xt,
-                                                  float yt, float2 d, float m)
+// Ordering point between two sampling points: the accumulators pass through
+// it (so this point's fmas come first) and it clobbers memory (so the next
+// point's LDS reads come after).  Without it the compiler issues every
+// point's corner reads up front and spills the rows it cannot hold.
+template <int CPL>
+__device__ __forceinline__ void point_fence(float* acc)
 {
-    TiledPoint pt;
-    const float x = fmaf(G.alpha, d.x, xt);
-    const float y = fmaf(G.alpha, d.y, yt);
-    const bool inmap = x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H;
-    const uint32_t ix = inmap ? (uint32_t)(cvt_flr(x) + 1) : 0u;
-    const uint32_t iy = inmap ? (uint32_t)(cvt_flr(y) + 1) : (uint32_t)(G.H + 1);
-    const float lx = inmap ? __builtin_amdgcn_fractf(x) : 0.f, ly = inmap ? __builtin_amdgcn_fractf(y) : 0.f;
-    const float mm = inmap ? m : 0.f;
-    const uint32_t a0 = (__umul24(iy, L.RW) + ix) * 128u + L.lane_first;
-    const uint32_t a1 = a0 ^ 16u;
-    const uint32_t ca[4] = {0u, 128u, L.RWB, L.RWB + 128u};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint4 v0 = *(const uint4*)(lds + a0 + ca[k]);
-        const uint4 v1 = *(const uint4*)(lds + a1 + ca[k]);
-        pt.raw[k][0] = v0.x; pt.raw[k][1] = v0.y; pt.raw[k][2] = v0.z; pt.raw[k][3] = v0.w;
-        pt.raw[k][4] = v1.x; pt.raw[k][5] = v1.y; pt.raw[k][6] = v1.z; pt.raw[k][7] = v1.w;
+    if constexpr (CPL == 16) {
+        asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]),
+                     "+v"(acc[6]), "+v"(acc[7]), "+v"(acc[8]), "+v"(acc[9]), "+v"(acc[10]), "+v"(acc[11]),
+                     "+v"(acc[12]), "+v"(acc[13]), "+v"(acc[14]), "+v"(acc[15])::"memory");
+    } else {
+        static_assert(CPL == 8, "channels per lane");
+        asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]),
+                     "+v"(acc[6]), "+v"(acc[7])::"memory");
     }
-    modulated_weights(mm, lx, ly, pt.w);
-    return pt;
 }
 
 template <typename T, int CPL>
@@ -927,7 +987,7 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
     L.y_lo = cur.y_lo;
     L.gl_first = cur.slab * 128u + L.lane_first;
     L.gl_second = L.gl_first ^ 16u;
-    set_fast_bounds(L, G, (uint32_t)tg.RH);
+    set_fast_bounds(L, G, (uint32_t)tg.RH, WHOLE);
     const char* lds = (const char*)region;
     float acc[CPL];
 #pragma unroll
@@ -940,13 +1000,13 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
     // one point: its corners from the staged region (the whole-map variant
     // needs nothing else), plus the memory gather of a sample on the map
     // beyond the region
+    // Lanes past the tile (or the map) run the points too, on a valid record
+    // and valid reads, and store nothing: no branch per point.
     auto point = [&](float xt, float yt, float2 d, float m) {
-        if constexpr (WHOLE) {
-            tiled_accumulate<T, CPL>(whole_fetch<T>(G, L, lds, xt, yt, d, m), acc_ref());
-        } else {
-            bool far;
-            float x, y;
-            tiled_accumulate<T, CPL>(tiled_fetch<T>(G, L, lds, xt, yt, d, m, far, x, y), acc_ref());
+        bool far;
+        float x, y;
+        tiled_accumulate<T, CPL>(tiled_fetch<T, WHOLE>(L, lds, xt, yt, d, m, far, x, y), acc_ref());
+        if constexpr (!WHOLE) {
             if (far) far_accumulate<T>(G, L, rin, x, y, m, acc_ref());
         }
     };
@@ -964,31 +1024,36 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
         load_record<T, PK>(rec, roff, voff, rmk, vmk, odd);
         __builtin_amdgcn_s_waitcnt(0);   // the region (and the record) have landed
         __syncthreads();
-        float mx = 0.f, inv = 1.f;
-        if constexpr (SOFTMAX) {
-            mx = mval(rec.mask[0]);
+        // the modulation: raw, or the softmax over the PK points (each
+        // exponential formed once)
+        float mq[PK];
 #pragma unroll
-            for (int q = 1; q < PK; ++q) mx = fmaxf(mx, mval(rec.mask[q]));
+        for (int q = 0; q < PK; ++q) mq[q] = mval(rec.mask[q]);
+        if constexpr (SOFTMAX) {
+            float mx = mq[0];
+#pragma unroll
+            for (int q = 1; q < PK; ++q) mx = fmaxf(mx, mq[q]);
             float sum = 0.f;
 #pragma unroll
-            for (int q = 0; q < PK; ++q) sum += __expf(mval(rec.mask[q]) - mx);
-            inv = 1.0f / sum;
+            for (int q = 0; q < PK; ++q) {
+                mq[q] = __expf(mq[q] - mx);
+                sum += mq[q];
+            }
+            const float inv = 1.0f / sum;
+#pragma unroll
+            for (int q = 0; q < PK; ++q) mq[q] *= inv;
         }
         // the taps' part of the coordinates, once per column and row of taps
         float xt[KT], yt[KT];
 #pragma unroll
         for (int i = 0; i < KT; ++i) {
-            xt[i] = fmaf(G.alpha, tg.tap_x[i * KT], L.bx);
-            yt[i] = fmaf(G.alpha, tg.tap_y[i], L.by);
+            xt[i] = fmaf(L.alpha, tg.tap_x[i * KT], L.bx);
+            yt[i] = fmaf(L.alpha, tg.tap_y[i], L.by);
         }
 #pragma unroll
         for (int q = 0; q < PK; ++q) {
-            if (active) {
-                float m = mval(rec.mask[q]);
-                if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
-                point(xt[q / KT], yt[q % KT], record_pair<T, PK>(rec, q), m);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+            point(xt[q / KT], yt[q % KT], record_pair<T, PK>(rec, q), mq[q]);
+            point_fence<CPL>(acc);
         }
     } else {
         __builtin_amdgcn_s_waitcnt(0);   // the region has landed
@@ -1010,11 +1075,10 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
             const RawPair<T> d = dn;
             const uint32_t mraw = mn;
             if (q + 1 < P) { dn = load_offset_raw<T>(roff, voff, q + 1, odd); mn = load_mask_raw<T>(rmk, vmk, q + 1); }
-            if (active) {
-                float m = mval(mraw);
-                if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
-                point(fmaf(G.alpha, tg.tap_x[q], L.bx), fmaf(G.alpha, tg.tap_y[q], L.by), widen_pair<T>(d), m);
-            }
+            float m = mval(mraw);
+            if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
+            point(fmaf(L.alpha, tg.tap_x[q], L.bx), fmaf(L.alpha, tg.tap_y[q], L.by), widen_pair<T>(d), m);
+            point_fence<CPL>(acc);
         }
     }
 

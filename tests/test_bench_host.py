@@ -80,8 +80,12 @@ def test_counter_record_follows_the_same_gate(tmp_path, monkeypatch):
            "l2_hit": 0.6}
     json.dump({"kernel_hash": bench.kernel_hash(), "workloads": {"c2_dcnv4_f16_56": rec}}, open(f, "w"))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    assert bench.counter_record("c2_dcnv4_f16_56") == {k: rec[k] for k in
-                                                       ("valu_busy_pct", "occupancy_pct", "lds_util_pct", "l2_hit")}
+    assert bench.counter_record("c2_dcnv4_f16_56") == {k: rec[k] for k in bench.COUNTER_KEYS if k in rec}
+    assert bench.valu_record("c2_dcnv4_f16_56", 0.04) is None          # no instruction count in the record
+    rec["sq_insts_valu"] = 12_288_000
+    json.dump({"kernel_hash": bench.kernel_hash(), "workloads": {"c2_dcnv4_f16_56": rec}}, open(f, "w"))
+    v = bench.valu_record("c2_dcnv4_f16_56", 0.04)                    # 12.288 M in 40 us = 307.2 G/s
+    assert v["achieved"] == 307.2 and v["peak"] == 614.4 and v["frac"] == 0.5
     json.dump({"kernel_hash": "0" * 16, "workloads": {"c2_dcnv4_f16_56": rec}}, open(f, "w"))
     assert bench.counter_record("c2_dcnv4_f16_56") is None
 

@@ -150,7 +150,7 @@ def test_packed_layout(case):
 
 def test_packed_headline_shape_matches_split():
     """The 56x56 DCNv4 stage in fp16 (N reduced), packed against split."""
-    w = inputs.scaled(inputs.WORKLOADS[inputs.HEADLINE], N=4)
+    w = inputs.scaled(inputs.WORKLOADS["c2_dcnv4_f16_56"], N=4)
     t = inputs.make(w, with_grad=False)
     om = inputs.pack_offset_mask(t["offset"], t["mask"], w.G, w.P).to(DEV)
     d = {k: v.to(DEV) for k, v in t.items()}
