@@ -1,18 +1,21 @@
 """GPU parity of the DCNv4 layer around the core: the centre-feature gate
 kernel against the float64 gate of the layer oracle (element by element),
-and the whole layer (library GEMMs + HIP core + HIP gate) against the layer
-oracle, forward and backward.
+and the whole layer (projections + HIP core + HIP gate), forward and
+backward, checked stage by stage.
 
-The layer's binary32 run is compared normwise: its projections are BLAS
-GEMMs whose rounding feeds the sampling coordinates, so an element's error
-has no per-element sum to scale with.  For each tensor,
-    max |gpu - ref| <= 1e-5 * max |ref|
-(a few binary32 roundings per stage, each far below 1e-5 of the largest
-element).  In half precision every stage boundary rounds to the dtype, so
-the layer is checked stage by stage instead: the core and the gate on the
-layer's own intermediates against the oracle, with the core's and the gate's
-element-wise bounds, and the layer's output against the same stages
-composed by hand.
+The layer's projections round (in binary32 or half precision), and that
+rounding moves the sampling coordinates, so the layer's output has no
+per-element sum of terms to bound its distance from an all-float64 layer.
+Instead each stage is checked on the layer's own intermediates:
+
+* the layer's output and every gradient equal the same package calls made
+  stage by stage here (bit for bit where the order of additions is fixed,
+  else within one rounding per addition), so the stages are the layer's;
+* each stage -- the four projections and their input, weight and bias
+  gradients, the sampling core and its backward, the gate and its backward
+  -- matches its float64 definition (oracle/module.py's linear and gate
+  formulas, the C oracle for the core) evaluated on that stage's own inputs,
+  element by element to the bounds of tests/tolerance.py.
 """
 import random
 import sys
@@ -130,12 +133,6 @@ def make_layer(N, H, W, G, Cg, K, rc, cfs, alpha, dtype, seed):
     return layer, x, gout
 
 
-def normwise_ok(got, want, tol):
-    err = float(np.max(np.abs(got - want))) if want.size else 0.0
-    scale = float(np.max(np.abs(want))) if want.size else 0.0
-    return err <= tol * scale, err / scale if scale else err
-
-
 @pytest.mark.parametrize("case", LAYER, ids=lambda c: f"N{c[0]}_{c[1]}x{c[2]}_G{c[3]}_Cg{c[4]}_K{c[5]}"
                                                           f"_rc{int(c[6])}_cfs{int(c[7])}")
 def test_layer_fp32_matches_oracle(case):
@@ -157,66 +154,205 @@ def test_layer_fp32_random_shapes(case):
 
 
 def check_layer_fp32(case, seed):
+    check_layer_stages(case, "f32", seed)
+
+
+def _proj_bw(g, a, lin, dt):
+    """The _Projection backward the layer runs: input gradient g @ W and the
+    weight and bias gradients (the package's kernels, or their fallbacks)."""
+    from deformable_convolution_core_amd.layer import _matmul_t, _param_grads
+    g2 = g.reshape(-1, g.shape[-1]).contiguous()
+    gx = _matmul_t(g2, lin.weight.t().contiguous()).view(a.shape)
+    gw, gb = _param_grads(g2, a.reshape(-1, a.shape[-1]), True, True)
+    return gx, gw, gb
+
+
+def layer_stages(layer, x, gout, core_backward):
+    """The layer's forward and backward as the package calls it makes, stage
+    by stage (the same calls as DCNv4.forward and the autograd functions'
+    backward), keeping every intermediate.  core_backward: the (gi, gom) the
+    layer's own backward got from the core -- its grad_input is summed in an
+    unfixed order, so a second call would differ in the last bits."""
+    from deformable_convolution_core_amd.layer import _matmul_t
+    K, G, P = layer.kernel_size, layer.group, dcn.points(layer.kernel_size, layer.remove_center)
+    kw = dict(kernel_size=K, dilation=layer.dilation, offset_scale=layer.offset_scale, group=G,
+              remove_center=layer.remove_center)
+    st = dict(x=x)
+    st["v"] = _matmul_t(x, layer.value_proj.weight, layer.value_proj.bias)
+    st["om"] = _matmul_t(x, layer.offset_mask.weight, layer.offset_mask.bias)
+    gate = layer.center_feature_scale_proj is not None
+    fused = False
+    if gate:
+        st["z"] = _matmul_t(x, layer.center_feature_scale_proj.weight, layer.center_feature_scale_proj.bias)
+        try:
+            st["yg"], st["y"] = dcn.forward_packed_gated(st["v"], st["om"], st["z"], keep_core_output=True, **kw)
+            fused = True
+        except dcn.DCNError as e:
+            assert e.status == 2
+            st["y"] = dcn.forward_packed(st["v"], st["om"], stride=1, pad=layer.pad, **kw)
+            st["yg"] = dcn.center_gate_forward(st["y"], st["v"], st["z"], group=G)
+    else:
+        st["y"] = dcn.forward_packed(st["v"], st["om"], stride=1, pad=layer.pad, **kw)
+        st["yg"] = st["y"]
+    st["out"] = _matmul_t(st["yg"], layer.output_proj.weight, layer.output_proj.bias)
+    # backward, stage by stage
+    st["g_yg"], st["dWo"], st["dbo"] = _proj_bw(gout, st["yg"], layer.output_proj, x.dtype)
+    if gate:
+        st["g_y"], st["gv_gate"], st["gz"] = dcn.center_gate_backward(st["y"], st["v"], st["z"], st["g_yg"],
+                                                                     group=G)
+    else:
+        st["g_y"] = st["g_yg"]
+    st["gi"], st["gom"] = core_backward
+    st["gv"] = st["gi"] + st["gv_gate"] if gate else st["gi"]
+    st["gx_v"], st["dWv"], st["dbv"] = _proj_bw(st["gv"], x, layer.value_proj, x.dtype)
+    st["gx_om"], st["dWom"], st["dbom"] = _proj_bw(st["gom"], x, layer.offset_mask, x.dtype)
+    if gate:
+        st["gx_z"], st["dWc"], st["dbc"] = _proj_bw(st["gz"], x, layer.center_feature_scale_proj, x.dtype)
+    st["fused"] = fused
+    st["P"] = P
+    return st
+
+
+def check_projection(out, a, W, b, dt, what):
+    """out = a @ W.T + b against float64 on the same (rounded) operands."""
+    A, Wt = f64(a).reshape(-1, a.shape[-1]), f64(W)
+    ref = A @ Wt.T + (0.0 if b is None else f64(b))
+    S = np.abs(A) @ np.abs(Wt).T + (0.0 if b is None else np.abs(f64(b)))
+    st = tolerance.compare(f64(out).reshape(ref.shape), ref, S, A.shape[1] + 1, dt)
+    assert st["ok"], (what, st)
+
+
+def check_param_grads(dW, db, g, a, dt, what):
+    """dW = g^T a and db = sum of g over rows, against float64."""
+    G2, A2 = f64(g).reshape(-1, g.shape[-1]), f64(a).reshape(-1, a.shape[-1])
+    ref, S = G2.T @ A2, np.abs(G2).T @ np.abs(A2)
+    st = tolerance.compare(f64(dW), ref, S, G2.shape[0], dt)
+    assert st["ok"], (what + " weight", st)
+    st = tolerance.compare(f64(db), G2.sum(0), np.abs(G2).sum(0), G2.shape[0], dt)
+    assert st["ok"], (what + " bias", st)
+
+
+def check_layer_stages(case, dt, seed):
+    # platform-BLAS fallbacks (shapes the package's GEMM declines) accumulate
+    # in binary32 here, as the bounds assume
+    mm = torch.backends.cuda.matmul
+    saved = (mm.allow_fp16_reduced_precision_reduction, mm.allow_bf16_reduced_precision_reduction)
+    mm.allow_fp16_reduced_precision_reduction = False
+    mm.allow_bf16_reduced_precision_reduction = False
+    try:
+        _check_layer_stages(case, dt, seed)
+    finally:
+        mm.allow_fp16_reduced_precision_reduction, mm.allow_bf16_reduced_precision_reduction = saved
+
+
+def _check_layer_stages(case, dt, seed):
     N, H, W, G, Cg, K, rc, cfs, alpha = case
-    layer, x, gout = make_layer(*case, "f32", seed)
+    layer, x, gout = make_layer(*case, dt, seed)
     xi = x.clone().requires_grad_(True)
     out = layer(xi)
-    out.backward(gout)
+    # the layer's backward calls the core's backward once: keep what it returns
+    calls = []
+    orig = dcn.backward_packed
+
+    def recording(*a, **k):
+        r = orig(*a, **k)
+        calls.append((a, k, r))
+        return r
+    dcn.backward_packed = recording
+    try:
+        out.backward(gout)
+    finally:
+        dcn.backward_packed = orig
     torch.cuda.synchronize()
-    cfg = dict(kernel_size=K, group=G, remove_center=rc, center_feature_scale=cfs, offset_scale=alpha)
-    p = layer.numpy_params()
-    ref = om_oracle.module_forward(f64(x), p, cfg)["out"]
-    ok, r = normwise_ok(f64(out), ref, 1e-5)
-    assert ok, ("out", r)
-    g = om_oracle.module_backward(f64(x), p, cfg, f64(gout))
-    grads = dict(x=xi.grad, Wv=layer.value_proj.weight.grad, bv=layer.value_proj.bias.grad,
-                 Wom=layer.offset_mask.weight.grad, bom=layer.offset_mask.bias.grad,
-                 Wo=layer.output_proj.weight.grad, bo=layer.output_proj.bias.grad)
+    assert len(calls) == 1
+    with torch.no_grad():
+        st = layer_stages(layer, x, gout, calls[0][2])
+    torch.cuda.synchronize()
+    # the core's backward got the stage-wise upstream gradient and inputs
+    a, k, _ = calls[0]
+    assert torch.equal(a[0], st["v"]) and torch.equal(a[1], st["om"]) and torch.equal(a[2], st["g_y"])
+    name = f"{case} {dt}"
+    # the stages are the layer's: output and parameter gradients bit for bit
+    assert torch.equal(out, st["out"]), name
+    pg = [("Wo", layer.output_proj, "dWo", "dbo"), ("Wv", layer.value_proj, "dWv", "dbv"),
+          ("Wom", layer.offset_mask, "dWom", "dbom")]
     if cfs:
-        grads.update(Wc=layer.center_feature_scale_proj.weight.grad, bc=layer.center_feature_scale_proj.bias.grad)
-    for name, got in grads.items():
-        ok, r = normwise_ok(f64(got), g[name], 1e-5)
-        assert ok, (name, r)
+        pg.append(("Wc", layer.center_feature_scale_proj, "dWc", "dbc"))
+    for nm, lin, kw_, kb in pg:
+        assert torch.equal(lin.weight.grad, st[kw_]), (name, nm)
+        assert torch.equal(lin.bias.grad, st[kb]), (name, nm)
+    # the input gradient: autograd adds the projections' three (or two)
+    # input gradients in its own order, one rounding per addition
+    parts = [st["gx_v"], st["gx_om"]] + ([st["gx_z"]] if cfs else [])
+    ref = sum(f64(t) for t in parts)
+    S = sum(np.abs(f64(t)) for t in parts)
+    s_ = tolerance.compare(f64(xi.grad), ref, S, len(parts), dt, store_roundings=len(parts) - 1)
+    assert s_["ok"], (name, "input gradient sum", s_)
+    # each stage against its float64 definition on its own inputs
+    P = st["P"]
+    check_projection(st["v"], x, layer.value_proj.weight, layer.value_proj.bias, dt, "value projection")
+    check_projection(st["om"], x, layer.offset_mask.weight, layer.offset_mask.bias, dt, "offset+mask projection")
+    check_projection(st["out"], st["yg"], layer.output_proj.weight, layer.output_proj.bias, dt, "output projection")
+    core_kw = dict(K=K, stride=1, pad=layer.pad, dilation=1, offset_scale=alpha, softmax=False, group=G,
+                   coord_mode=oracle.COORD_BINARY32, remove_center=rc)
+    off, mask = inputs.unpack_offset_mask(st["om"].cpu(), G, P)
+    yref, S = oracle.forward(f64(st["v"]), f64(off), f64(mask), **core_kw)
+    s_ = tolerance.compare(f64(st["y"]), yref, S, 4 * P, dt)
+    assert s_["ok"], (name, "core", s_)
+    V = f64(st["v"])
+    if cfs:
+        check_projection(st["z"], x, layer.center_feature_scale_proj.weight, layer.center_feature_scale_proj.bias,
+                         dt, "gate projection")
+        Z = f64(st["z"])
+        s, t = om_oracle.sigmoid(Z)[..., None], om_oracle.sigmoid(-Z)[..., None]
+        # the fused gate takes the unrounded core result, the two-kernel gate the rounded one
+        Y = yref if st["fused"] else f64(st["y"])
+        SY = S if st["fused"] else np.abs(Y)
+        S_g = (SY.reshape(N, H, W, G, Cg) * t + np.abs(V).reshape(N, H, W, G, Cg) * s).reshape(Y.shape)
+        s_ = tolerance.compare(f64(st["yg"]), om_oracle.gate_forward(Y, V, Z, G), S_g, 4 * P + 2, dt,
+                               store_roundings=0 if st["fused"] else 1)
+        assert s_["ok"], (name, "gate", s_)
+    # backward stages
+    check_projection(st["g_yg"], gout, layer.output_proj.weight.t(), None, dt, "output projection input grad")
+    check_param_grads(st["dWo"], st["dbo"], gout, st["yg"], dt, "output projection")
+    if cfs:
+        Y, GO = f64(st["y"]), f64(st["g_yg"])
+        gy, gv, gz = om_oracle.gate_backward(Y, V, Z, GO, G)
+        go5 = np.abs(GO).reshape(N, H, W, G, Cg)
+        s_ = tolerance.compare(f64(st["g_y"]), gy, np.abs(gy), 1, dt)
+        assert s_["ok"], (name, "gate backward: grad of y", s_)
+        s_ = tolerance.compare(f64(st["gv_gate"]), gv, np.abs(gv), 1, dt)
+        assert s_["ok"], (name, "gate backward: grad of v", s_)
+        Sz = (go5 * (np.abs(V) + np.abs(Y)).reshape(go5.shape)).sum(-1) * (s[..., 0] * t[..., 0])
+        s_ = tolerance.compare(f64(st["gz"]), gz, Sz, Cg + 4, dt)
+        assert s_["ok"], (name, "gate backward: grad of the logits", s_)
+    r = oracle.backward(f64(st["v"]), f64(off), f64(mask), f64(st["g_y"]), **core_kw)
+    s_ = tolerance.compare(f64(st["gi"]).reshape(r["grad_input"].shape), r["grad_input"], r["gi_abs"], r["gi_cnt"], dt)
+    assert s_["ok"], (name, "core backward: grad of v", s_)
+    goff, gmask = inputs.unpack_offset_mask(st["gom"].cpu(), G, P)
+    s_ = tolerance.compare(f64(goff).reshape(r["grad_offset"].shape), r["grad_offset"], r["goff_abs"], 4 * Cg, dt)
+    assert s_["ok"], (name, "core backward: grad of the offsets", s_)
+    s_ = tolerance.compare(f64(gmask).reshape(r["grad_mask"].shape), r["grad_mask"], r["gmask_abs"], 4 * Cg, dt)
+    assert s_["ok"], (name, "core backward: grad of the mask", s_)
+    if cfs:
+        s_ = tolerance.compare(f64(st["gv"]), f64(st["gi"]) + f64(st["gv_gate"]),
+                               np.abs(f64(st["gi"])) + np.abs(f64(st["gv_gate"])), 2, dt)
+        assert s_["ok"], (name, "grad of v: core + gate", s_)
+    for g, lin, a, what in ((st["gv"], layer.value_proj, x, "value"), (st["gom"], layer.offset_mask, x, "offset+mask")) \
+            + (((st["gz"], layer.center_feature_scale_proj, x, "gate"),) if cfs else ()):
+        gx = {"value": st["gx_v"], "offset+mask": st["gx_om"], "gate": st.get("gx_z")}[what]
+        check_projection(gx, g, lin.weight.t(), None, dt, what + " projection input grad")
+        dW, db = {"value": (st["dWv"], st["dbv"]), "offset+mask": (st["dWom"], st["dbom"]),
+                  "gate": (st.get("dWc"), st.get("dbc"))}[what]
+        check_param_grads(dW, db, g, a, dt, what + " projection")
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
-def test_layer_half_stagewise(dt):
-    """Half precision: the layer's output equals its stages composed by hand
-    (bit for bit; the core and the gate as the one fused call the layer
-    makes), and the projections, the HIP core and the gate match the float64
-    definitions on the layer's own intermediates."""
-    N, H, W, G, Cg, K = 2, 14, 14, 4, 16, 3
-    layer, x, gout = make_layer(N, H, W, G, Cg, K, False, True, 1.0, dt, 6400)
-    out = layer(x)
-    v = dcn.linear(x, layer.value_proj.weight, layer.value_proj.bias)
-    om = dcn.linear(x, layer.offset_mask.weight, layer.offset_mask.bias)
-    z = dcn.linear(x, layer.center_feature_scale_proj.weight, layer.center_feature_scale_proj.bias)
-    yg, y = dcn.forward_packed_gated(v, om, z, kernel_size=K, group=G, keep_core_output=True)
-    want = dcn.linear(yg, layer.output_proj.weight, layer.output_proj.bias)
-    torch.cuda.synchronize()
-    assert torch.equal(out, want)
-    # the projections against the float64 product of the same (half-precision) operands
-    for got, a, lin in ((v, x, layer.value_proj), (om, x, layer.offset_mask),
-                        (z, x, layer.center_feature_scale_proj), (want, yg, layer.output_proj)):
-        A, Wt, B = f64(a).reshape(-1, a.shape[-1]), f64(lin.weight), f64(lin.bias)
-        ref = A @ Wt.T + B
-        S = np.abs(A) @ np.abs(Wt).T + np.abs(B)
-        st = tolerance.compare(f64(got).reshape(ref.shape), ref, S, A.shape[1] + 1, dt)
-        assert st["ok"], ("projection", st)
-    P = K * K
-    off, mask = inputs.unpack_offset_mask(om.cpu(), G, P)
-    ref, S = oracle.forward(f64(v), f64(off), f64(mask), K=K, stride=1, pad=1, dilation=1, offset_scale=1.0,
-                            softmax=False, group=G)
-    st = tolerance.compare(f64(y), ref, S, 4 * P, dt)
-    assert st["ok"], ("core", st)
-    # the fused gate takes the unrounded y: against the gate of the oracle's y
-    V, Z = f64(v), f64(z)
-    s, t = om_oracle.sigmoid(Z)[..., None], om_oracle.sigmoid(-Z)[..., None]
-    S_g = (S.reshape(N, H, W, G, Cg) * t + np.abs(V).reshape(N, H, W, G, Cg) * s).reshape(ref.shape)
-    st = tolerance.compare(f64(yg), om_oracle.gate_forward(ref, V, Z, G), S_g, 4 * P + 2, dt)
-    assert st["ok"], ("gate", st)
-    # the backward runs end to end in half precision
-    xi = x.clone().requires_grad_(True)
-    layer(xi).backward(gout)
-    torch.cuda.synchronize()
-    assert torch.isfinite(xi.grad.float()).all()
+@pytest.mark.parametrize("case", [(2, 14, 14, 4, 16, 3, False, True, 1.0), (1, 12, 11, 4, 16, 3, True, False, 0.8),
+                                  (1, 9, 10, 3, 8, 3, False, True, 1.0)],
+                         ids=["gated", "rc_nogate", "two_kernel_gate"])
+def test_layer_half_stagewise(case, dt):
+    """Half precision, forward and backward, every stage element by element
+    on the layer's own intermediates (C = 24 runs the core and the gate as
+    two kernels)."""
+    check_layer_stages(case, dt, 6400 + case[1])
