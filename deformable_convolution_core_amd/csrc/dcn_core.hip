@@ -309,29 +309,33 @@ int forward_typed(const FwdArgs& a, const Call& c, hipStream_t st)
 #ifndef DCN_OWNER_FORCE_TH
 #define DCN_OWNER_FORCE_TH 0
 #endif
-#ifndef DCN_OWNER_FORCE_NT
-#define DCN_OWNER_FORCE_NT 0
+#ifndef DCN_OWNER_FORCE_R
+#define DCN_OWNER_FORCE_R 0   // nonzero: ... and this many output rows per chunk
+#endif
+#ifndef DCN_OWNER_CHUNK_CLK
+#define DCN_OWNER_CHUNK_CLK 1500   // modelled fixed cost of one chunk (barriers, scan), in lane-sample units
 #endif
 constexpr int64_t kMaxOwnerLds = 160 * 1024;
+constexpr int kOwnerMaxTile = 32;
+constexpr int kOwnerVgprs = 124;   // registers of the owner kernel per lane, at most (for the occupancy model)
 
 struct OwnerPlan {
-    OwnerGeo og;
+    BinGeo bg;
     int threads;
+    int cpl;
     uint32_t lds_bytes;
     uint64_t blocks;
 };
 
-// The owner kernel applies where a lane's 8 channels stay inside one group
-// (Cg a multiple of 8) and slabs of 32 channels tile the channel row (C a
-// multiple of 32), with 16-byte aligned grad_output and grad_input.  Among tiles that fit the LDS it picks the one with the
-// shortest makespan: blocks per CU (256 CUs) times a block's lane slots
-// issued over its visited output pixels (idle lanes of the last pass count)
-// plus its own zero fill and store, among tiles whose visited area stays
-// within 8x the output.
+// The owner kernel applies where a group's channels split into lanes of 16
+// or 8 (Cg a multiple of 8), with 16-byte aligned grad_output and grad_input.
+// Among tiles up to 32 x 32 it picks the one with the least modelled work per
+// CU (256 CUs): the samples its lanes bin, the records its items gather and a
+// fixed cost per chunk, with a discount where two or more workgroups fit a
+// CU (the measured effect of overlapping one's barriers with another's work).
 bool plan_owner(const Call& c, const void* gout, const void* gin, OwnerPlan& pl)
 {
-    const int C = c.G * c.Cg;
-    if (c.Cg % 8 != 0 || C % 32 != 0) return false;
+    if (c.Cg % 8 != 0) return false;
     if (!aligned(gout, 16) || !aligned(gin, 16)) return false;
     const float a = c.alpha < 0 ? -c.alpha : c.alpha;
     const int c0 = c.dil * (c.K - 1) / 2;
@@ -339,63 +343,85 @@ bool plan_owner(const Call& c, const void* gout, const void* gin, OwnerPlan& pl)
     const float mf = ceilf(a * ((float)span + (float)DCN_OWNER_REACH)) + 1.0f;
     if (!(mf <= 1024.0f)) return false;
     const int M = (int)mf;
-    const uint32_t slabs = (uint32_t)(C / 32);
+    const int cpl = c.Cg % 16 == 0 ? 16 : 8;
+    const int LP = c.Cg / cpl;
     double best = -1.0;
-    for (int nt = 256; nt <= 1024; nt *= 2) {
-        for (int tw = 1; tw <= 64 && tw <= c.W; ++tw)
-            for (int th = 1; th <= 64 && th <= c.H; ++th) {
-                if (DCN_OWNER_FORCE_TW && (tw != DCN_OWNER_FORCE_TW || th != DCN_OWNER_FORCE_TH ||
-                                           nt != DCN_OWNER_FORCE_NT))
-                    continue;
-                const int64_t lds = (int64_t)th * tw * kOwnerStride * 4;
-                if (lds > kMaxOwnerLds) continue;
-                const int per_cu = (int)(160 * 1024 / lds) < 2048 / nt ? (int)(160 * 1024 / lds) : 2048 / nt;
-                const int waves = per_cu * nt / 64;
-                if (waves < 8) continue;
-                const int64_t tx = (c.W + tw - 1) / tw, ty = (c.H + th - 1) / th;
-                int64_t ew = (tw - 1 + 2 * M) / c.stride + 1, eh = (th - 1 + 2 * M) / c.stride + 1;
-                if (ew > c.Wo) ew = c.Wo;
-                if (eh > c.Ho) eh = c.Ho;
-                // visited output pixels over output pixels: beyond 8x the
-                // atomic scatter is cheaper (a very large offset_scale makes
-                // every output pixel near every tile)
-                if ((double)(tx * ty) * (double)(ew * eh) > 8.0 * (double)c.Ho * c.Wo) continue;
-                const int64_t passes = (ew * eh * 4 + nt - 1) / nt;
-                const double occ = waves >= 16 ? 1.0 : 16.0 / (double)waves;
-                // makespan: the busiest CU runs ceil(blocks / CUs) blocks
-                const int64_t blocks = tx * ty * (int64_t)slabs * c.N;
-                const double rounds = (double)((blocks + 255) / 256);
-                const double cost = rounds * ((double)passes * nt * 10.0 + (double)th * tw * 16.0) * occ;
+    for (int tw = 1; tw <= kOwnerMaxTile && tw <= c.W; ++tw)
+        for (int th = 1; th <= kOwnerMaxTile && th <= c.H; ++th) {
+            if (DCN_OWNER_FORCE_TW && (tw != DCN_OWNER_FORCE_TW || th != DCN_OWNER_FORCE_TH)) continue;
+            const int items = th * tw * LP;
+            const int64_t tx = (c.W + tw - 1) / tw, ty = (c.H + th - 1) / th;
+            int64_t ew = (tw - 1 + 2 * M) / c.stride + 1, eh = (th - 1 + 2 * M) / c.stride + 1;
+            if (ew > c.Wo) ew = c.Wo;
+            if (eh > c.Ho) eh = c.Ho;
+            // visited output pixels over output pixels: beyond 8x the atomic
+            // scatter is cheaper (a very large offset_scale makes every
+            // output pixel near every tile)
+            if ((double)(tx * ty) * (double)(ew * eh) > 8.0 * (double)c.Ho * c.Wo) continue;
+            const int64_t blocks = tx * ty * (int64_t)c.G * c.N;
+            if (blocks >= (1ll << 31)) continue;
+            // one item per lane
+            const int nt = (items + 63) / 64 * 64;
+            if (nt > 1024) continue;
+            for (int R = 1; R <= eh; ++R) {
+                if (DCN_OWNER_FORCE_R && R != DCN_OWNER_FORCE_R) continue;
+                BinGeo bg{th, tw, M, c.Cg, R, (int)ew, (int)(R * ew * c.P), (th + 1) * (tw + 1), 0u, 0u, 0u, 0u, 0u};
+                // a lane holds at most kBinSamples samples of a chunk and
+                // kBinPrefetch 16-byte pieces of its gradient rows
+                if (R * ew * c.P > kBinSamples * nt || R * ew * (c.Cg * c.ebytes / 16) > kBinPrefetch * nt) break;
+                const int64_t lds = bin_lds_bytes(bg);
+                if (lds > kMaxOwnerLds) break;
+                const int waves = nt / 64;
+                int bpc = (int)(kMaxOwnerLds / lds);
+                const int by_waves = 32 / waves, by_regs = (512 / kOwnerVgprs) * 4 / waves;
+                if (bpc > by_waves) bpc = by_waves;
+                if (bpc > by_regs) bpc = by_regs;
+                if (bpc < 1) continue;
+                const int64_t chunks = (eh + R - 1) / R;
+                // per CU: every lane bins kBinSamples samples per chunk, every
+                // item gathers about 4P records, and each chunk pays a fixed
+                // latency (barriers, scan); two or more resident workgroups
+                // overlap one's barriers with another's work
+                const double per_cu = (double)((blocks + 255) / 256);
+                const double work = (double)chunks * nt * kBinSamples + (double)items * 4.0 * c.P * 0.8 +
+                                    (double)chunks * DCN_OWNER_CHUNK_CLK;
+                const double cost = per_cu * work / (bpc >= 2 ? 1.3 : 1.0);
                 if (best < 0 || cost < best) {
                     best = cost;
-                    pl.og = OwnerGeo{th, tw, M, c.Cg, (uint32_t)tx, (uint32_t)ty, slabs, 0u, 0u};
+                    pl.bg = bg;
+                    pl.bg.tiles_x = (uint32_t)tx;
+                    pl.bg.tiles_y = (uint32_t)ty;
                     pl.threads = nt;
+                    pl.cpl = cpl;
                     pl.lds_bytes = (uint32_t)lds;
-                    pl.blocks = (uint64_t)(tx * ty) * slabs * (uint64_t)c.N;
+                    pl.blocks = (uint64_t)blocks;
                 }
             }
-    }
-    if (best < 0 || pl.blocks >= (1ull << 31)) return false;
+        }
+    if (best < 0) return false;
     const int64_t off_img = (int64_t)c.Ho * c.Wo * c.G * c.off_stride * c.ebytes;
     const int64_t mask_img = (int64_t)c.Ho * c.Wo * c.G * c.mask_stride * c.ebytes;
-    if (off_img >= (1ll << 31) || mask_img >= (1ll << 31)) return false;
-    pl.og.off_image_bytes = (uint32_t)off_img;
-    pl.og.mask_image_bytes = (uint32_t)mask_img;
+    const int64_t gout_img = (int64_t)c.Ho * c.Wo * c.G * c.Cg * c.ebytes;
+    if (off_img >= (1ll << 31) || mask_img >= (1ll << 31) || gout_img >= (1ll << 31)) return false;
+    // the kernel's 24-bit index products
+    if ((int64_t)c.Ho * c.Wo * c.G >= (1 << 24) || (int64_t)c.G * c.Cg * c.ebytes >= (1 << 24) ||
+        (int64_t)c.off_stride * c.ebytes >= (1 << 24))
+        return false;
+    pl.bg.off_image_bytes = (uint32_t)off_img;
+    pl.bg.mask_image_bytes = (uint32_t)mask_img;
+    pl.bg.gout_image_bytes = (uint32_t)gout_img;
     return true;
 }
 
 template <typename T, int KT>
 int launch_owner(const BwdArgs& a, const OwnerPlan& pl, hipStream_t st)
 {
-    if (pl.threads == 1024)
-        hipLaunchKernelGGL((dcn_backward_input_owner<T, KT, 1024>), dim3((uint32_t)pl.blocks), dim3(1024),
-                           pl.lds_bytes, st, a, pl.og);
-    else if (pl.threads == 512)
-        hipLaunchKernelGGL((dcn_backward_input_owner<T, KT, 512>), dim3((uint32_t)pl.blocks), dim3(512), pl.lds_bytes,
-                           st, a, pl.og);
+    if (pl.cpl == 16)
+        hipLaunchKernelGGL((dcn_backward_input_binned<T, KT, 16>), dim3((uint32_t)pl.blocks), dim3(pl.threads),
+                           pl.lds_bytes, st, a, pl.bg);
     else
-        hipLaunchKernelGGL((dcn_backward_input_owner<T, KT, 256>), dim3((uint32_t)pl.blocks), dim3(256), pl.lds_bytes,
-                           st, a, pl.og);
+        hipLaunchKernelGGL((dcn_backward_input_binned<T, KT, 8>), dim3((uint32_t)pl.blocks), dim3(pl.threads),
+                           pl.lds_bytes, st, a, pl.bg);
     return launch_status();
 }
 
@@ -444,7 +470,7 @@ int backward_half(BwdArgs a, const Call& c, float* ws, hipStream_t st)
         return DCN_ERR_UNSUPPORTED;
     int rc = zero_fill(ws, (int64_t)c.N * c.H * c.W * c.G * c.Cg, st);
     if (rc != DCN_OK) return rc;
-    a.near_m = op.og.M;
+    a.near_m = op.bg.M;
     a.far_ws = ws;
     rc = backward_grad_tiled<T>(a, c, tp, st);
     if (rc != DCN_OK) return rc;
@@ -676,7 +702,7 @@ int backward_call(const Call& c, const void* input, const void* offset_in, const
         // then adds the corners that are not near with atomics
         a.geo = make_geometry(c, 8);
         rc = c.k3() ? launch_owner<float, 3>(a, op, st) : launch_owner<float, 0>(a, op, st);
-        a.near_m = op.og.M;
+        a.near_m = op.bg.M;
     } else {
         rc = zero_fill((float*)grad_input, (int64_t)N * H * W * G * Cg, st);
     }

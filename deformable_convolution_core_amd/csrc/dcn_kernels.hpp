@@ -1190,6 +1190,10 @@ __global__ __launch_bounds__(kBlock) void dcn_backward_kernel(BwdArgs a)
             const float wb[4] = {hy * hx, hy * s.lx, s.ly * hx, s.ly * s.lx};
             const float dwx[4] = {-hy, hy, -s.ly, s.ly};
             const float dwy[4] = {-hx, -s.lx, hx, s.lx};
+            // the owner kernel added the corners of samples whose four
+            // corners lie within near_m of the sampling base
+            const bool near = a.near_m >= 0 && (uint32_t)(s.x0 - bxi + a.near_m) < 2u * (uint32_t)a.near_m &&
+                              (uint32_t)(s.y0 - byi + a.near_m) < 2u * (uint32_t)a.near_m;
             float gm = 0.f, gdx = 0.f, gdy = 0.f;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -1201,10 +1205,6 @@ __global__ __launch_bounds__(kBlock) void dcn_backward_kernel(BwdArgs a)
                 gm = fmaf(wb[k], sk, gm);
                 gdx = fmaf(dwx[k], sk, gdx);
                 gdy = fmaf(dwy[k], sk, gdy);
-                // corners near the sampling base were added by the owner kernel
-                const bool near = a.near_m >= 0 &&
-                                  (uint32_t)(s.x0 + (k & 1) - bxi + a.near_m) <= 2u * (uint32_t)a.near_m &&
-                                  (uint32_t)(s.y0 + (k >> 1) - byi + a.near_m) <= 2u * (uint32_t)a.near_m;
                 if (s.v[k] && !near) {
                     const float mw = m * wb[k];
                     float* dst = (float*)(gin + s.off[k]);
@@ -1422,22 +1422,20 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
             const float am = pt.inmap ? G.alpha * m : 0.f;
             store_pair<T>(goff + 2 * q, am * gdx, am * gdy);
         }
-        // corners beyond the owners' reach: x0 and x0 + 1 both lie within
-        // M of the base exactly when x0 - base + M is in [0, 2M) (likewise
-        // y), which one test per axis settles for all four corners
-        // (unsigned arithmetic: off-map samples carry saturated floors and
-        // are excluded below)
+        // samples beyond the owners' reach: the owners took the corners of
+        // every sample whose x0 and x0 + 1 both lie within M of the base,
+        // that is x0 - base + M in [0, 2M) (likewise y); the corners of the
+        // others are added here (unsigned arithmetic: off-map samples carry
+        // saturated floors and are excluded below)
         const uint32_t nm = (uint32_t)a.near_m;
-        const bool all_near = a.near_m >= 0 && (uint32_t)pt.x0 - (uint32_t)bxi + nm < M2 &&
-                              (uint32_t)pt.y0 - (uint32_t)byi + nm < M2;
-        if (active && pt.inmap && !all_near) {
+        const bool near = a.near_m >= 0 && (uint32_t)pt.x0 - (uint32_t)bxi + nm < M2 &&
+                          (uint32_t)pt.y0 - (uint32_t)byi + nm < M2;
+        if (active && pt.inmap && !near) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int qx = pt.x0 + (k & 1), qy = pt.y0 + (k >> 1);
                 const bool valid = (uint32_t)qx < (uint32_t)G.W && (uint32_t)qy < (uint32_t)G.H;
-                const bool near = a.near_m >= 0 && (uint32_t)(qx - bxi + a.near_m) <= M2 &&
-                                  (uint32_t)(qy - byi + a.near_m) <= M2;
-                if (valid && !near) {
+                if (valid) {
                     const float mw = m * wb[k];
                     const size_t pix_el = (size_t)qy * G.W * G.C + (size_t)qx * G.C;   // elements
                     if constexpr (EB == 4) {
@@ -1521,79 +1519,40 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
 }
 
 // ---------------------------------------------------------------------------
-// grad_input by owner.  A workgroup owns a TH x TW tile of input pixels and
-// one slab of 32 of their channels (four lanes of eight channels per pixel).
-// A corner q of a sample of output pixel o is "near" when |q - b(o)| <= M on
-// both axes, b(o) = o*stride - pad + c0 being the sample's integer base.  The
-// owner visits exactly the output pixels whose base lies within M of its
-// tile, recomputes their samples, adds m*w*g of every near corner that falls
-// in its tile into an LDS copy of the tile (binary32), and writes the tile
-// once, rounded to the dtype.  Each near (sample, corner) pair lies in one
-// tile, so grad_input needs neither a zero fill nor global atomics; the rare
-// corners that are not near (offsets beyond the reach M was sized for) are
-// added afterwards, with atomics, by the gradient kernel.
+// grad_input by owner.  A workgroup owns a TH x TW tile of input pixels of one
+// image and one group.  A sample of output pixel o is "near" when its four
+// corners lie within M of b(o) = o*stride - pad + c0, the sample's integer
+// base, on both axes (x0 - b in [-M, M - 1], likewise y0).  The owner visits
+// exactly the output pixels whose base lies within M of its tile, recomputes
+// their samples, and sums m*w*g over the corners of near samples that fall in
+// its tile, in binary32, each tile element in one lane's registers; it
+// writes the tile once, rounded to the dtype.  Each corner of a near sample
+// lies in one tile, so grad_input needs neither a zero fill nor global
+// atomics; the corners of the rare samples that are not near (offsets beyond
+// the reach M was sized for) are added afterwards, with atomics, by the
+// gradient kernel.
 //
-// LDS keeps the tile pixel by pixel, 32 floats each in channel order, at a
-// stride of 34 floats: the pixels a wave's lanes add into then start on
-// different banks, and a lane's eight channels sit at fixed offsets from one
-// 8-byte aligned address.  Lane chunk `sub` adds into floats [8*sub, 8*sub + 8)
-// of a pixel.
-
-// Float adds into LDS through compare-and-swap.  On gfx950 an LDS float
-// atomic add (ds_add_f32) retires about one lane every few cycles per CU,
-// while integer LDS atomics run at the rate of plain LDS accesses; a CAS loop
-// uses the latter, on 64-bit words holding two floats each.  The eight adds
-// of one lane (consecutive floats) go out together as four swaps of
-// old + v; a lane whose swap found another value (another lane added in
-// between) repeats the round for its unfinished words, and finished words
-// then swap a value for itself, which never changes memory.  Each failed
-// swap follows some lane's successful one, so the loop ends.
-__device__ __forceinline__ uint64_t add_pair(uint64_t w, float a, float b)
-{
-    const uint32_t lo = __float_as_uint(__uint_as_float((uint32_t)w) + a);
-    const uint32_t hi = __float_as_uint(__uint_as_float((uint32_t)(w >> 32)) + b);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ void lds_add8(uint64_t* p, const float (&v)[8])
-{
-    uint64_t cur[4], des[4], got[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) cur[j] = __hip_atomic_load(p + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        des[j] = add_pair(cur[j], v[2 * j], v[2 * j + 1]);
-        got[j] = cur[j];
-        __hip_atomic_compare_exchange_strong(p + j, &got[j], des[j], __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    uint32_t pend = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pend |= (got[j] != cur[j] ? 1u : 0u) << j;
-    while (pend) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bool retry = (pend >> j) & 1u;
-            cur[j] = retry ? got[j] : des[j];
-            des[j] = retry ? add_pair(got[j], v[2 * j], v[2 * j + 1]) : des[j];
-            got[j] = cur[j];
-            __hip_atomic_compare_exchange_strong(p + j, &got[j], des[j], __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
-        uint32_t again = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) again |= (((pend >> j) & 1u) && got[j] != cur[j] ? 1u : 0u) << j;
-        pend = again;
-    }
-}
-
-constexpr int kOwnerStride = 34;   // floats per pixel in the LDS tile (even: 8-byte words)
-
-struct OwnerGeo {
-    int TH, TW, M, Cg;
-    uint32_t tiles_x, tiles_y, slabs;
-    uint32_t off_image_bytes, mask_image_bytes;   // one image of offset / mask
-};
+// The sums are gathers, not scatters: the visited output pixels are taken in
+// chunks of interleaved rows, and within a chunk every near sample whose 2x2
+// neighbourhood touches the tile is sorted by its top-left corner (x0, y0)
+// into bins, one per position in [qx0 - 1, qx0 + tw - 1] x
+// [qy0 - 1, qy0 + th - 1], with a counting sort: integer LDS atomics count
+// the bins, a block scan turns the counts into bin starts, and a second visit
+// places each sample's record (where its output pixel's gradient row sits in
+// LDS, m, the fractions lx, ly) at the next free slot of its bin.  The pixel
+// at tile position (cx, cy) is the (dx, dy) corner of exactly the samples in
+// the 2x2 bins (cx + 1 - dx, cy + 1 - dy); those are two runs of consecutive
+// records (bins are numbered row by row), which its lane walks, weighting
+// each record's upstream-gradient row (staged in LDS, binary32) by m times
+// the bilinear weight of that corner.  LDS float atomics, which gfx950
+// retires far slower than integer ones, are not used.
+//
+// While a chunk's records are gathered, every lane already holds the loads
+// of the next chunk (its output pixel's offset and mask record and its share
+// of the gradient rows), so the global-memory latency of a chunk hides behind
+// the previous chunk's gather.  A chunk takes at most one record slot per
+// sample (rows * window width * P), which the planner sizes the chunk for, so
+// one sort always holds the whole chunk.
 
 // Output indices o in [0, limit) whose base o*stride - pad + c0 lies in
 // [q0 - M, q0 + len - 1 + M].
@@ -1605,203 +1564,405 @@ __device__ __forceinline__ void owner_range(const Geometry& G, int M, int q0, in
     hi = hi < limit - 1 ? hi : limit - 1;
 }
 
-template <typename T, int KT, int NT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
-void dcn_backward_input_owner(BwdArgs a, OwnerGeo og)
+constexpr int kBinPrefetch = 4;   // 16-byte gradient pieces a lane holds for the next chunk, at most
+constexpr int kBinSamples = 6;    // samples a lane holds for the next chunk, at most
+
+struct BinGeo {
+    int TH, TW, M;               // tile of input pixels; reach
+    int Cg;                      // channels per group
+    int R;                       // visited output rows per chunk
+    int ew_max;                  // visited output columns, at most
+    int cap;                     // record slots: R * ew_max * P
+    int nb_max;                  // bins: (TH + 1) * (TW + 1)
+    uint32_t tiles_x, tiles_y;
+    uint32_t off_image_bytes, mask_image_bytes;   // one image of offset / mask
+    uint32_t gout_image_bytes;                    // one image of grad_output (< 2^31)
+};
+
+// Floats per staged gradient row: Cg plus 4, so that rows start on 16
+// different 16-byte bank groups and random rows read together rarely collide.
+__host__ __device__ inline int bin_row_floats(int Cg) { return Cg + 4; }
+
+// LDS of one workgroup, in this order: bin counts and bin starts (nb_max + 1,
+// the last one the total), one total per wave for the scan, the records (16
+// bytes each), the staged upstream gradient, and the softmax maximum and
+// reciprocal sum of each output pixel of the chunk.
+__host__ __device__ inline uint32_t bin_lds_words(const BinGeo& b)
+{
+    return ((uint32_t)(2 * b.nb_max + 1 + 16) + 3u) & ~3u;
+}
+__host__ __device__ inline uint32_t bin_lds_bytes(const BinGeo& b)
+{
+    return bin_lds_words(b) * 4u + (uint32_t)b.cap * 16u +
+           (uint32_t)(b.R * b.ew_max * (bin_row_floats(b.Cg) + 2)) * 4u;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele steps
+// within each row of 16 lanes (DPP row shifts by 1, 2, 4, 8; lanes shifted in
+// from outside the row add 0), then the running total of row 0 broadcast
+// into rows 1 and 3 and that of row 1 into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v)
+{
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return v;
+}
+
+// Exclusive prefix sums of cnt[0, nb) into start[0, nb] (start[nb] is the
+// total), by the whole workgroup (NT threads, a multiple of 64).  Every
+// thread takes a run of consecutive bins; the runs' sums are scanned within
+// each wave and across waves through wsum.  Starts and ends with a barrier.
+__device__ __forceinline__ void bin_scan(const uint32_t* cnt, uint32_t* start, uint32_t* wsum, int nb, int t, int NT)
+{
+    __syncthreads();
+    const int per = (nb + NT - 1) / NT;
+    const int b0 = t * per, b1 = b0 + per < nb ? b0 + per : nb;
+    uint32_t local = 0;
+    for (int b = b0; b < b1; ++b) local += cnt[b];
+    const int lane = t & 63, wave = t >> 6;
+    const uint32_t v = wave_inclusive_scan(local);
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    uint32_t base = 0;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+    uint32_t run = base + v - local;
+    for (int b = b0; b < b1; ++b) {
+        start[b] = run;
+        run += cnt[b];
+    }
+    if (t == NT - 1) start[nb] = base + v;
+    __syncthreads();
+}
+
+// Adds the records [e0, e2) of a run of two bins into acc: the records of the
+// first bin [e0, e1) have this pixel as their right-hand corner (dx = 1), the
+// others as their left-hand one; lower: the pixel is the lower corner
+// (dy = 1) of all the run's records.  Two records per step, their gradient
+// rows read together; the next two records are read meanwhile.
+template <int CPL>
+__device__ __forceinline__ void bin_run(const uint4* rec_lds, const char* gp, int e0, int e1, int e2,
+                                        bool lower, float (&acc)[CPL])
+{
+    if (e0 >= e2) return;
+    const int last = e2 - 1;
+    uint4 n0 = rec_lds[e0], n1 = rec_lds[e0 + 1 < last ? e0 + 1 : last];
+#pragma unroll 1
+    for (int e = e0; e < e2; e += 2) {
+        const uint4 r0 = n0, r1 = n1;
+        const bool two = e + 1 < e2;
+        n0 = rec_lds[e + 2 < last ? e + 2 : last];
+        n1 = rec_lds[e + 3 < last ? e + 3 : last];
+        const float wx0 = e < e1 ? __uint_as_float(r0.z) : 1.0f - __uint_as_float(r0.z);
+        const float wx1 = e + 1 < e1 ? __uint_as_float(r1.z) : 1.0f - __uint_as_float(r1.z);
+        const float wy0 = lower ? __uint_as_float(r0.w) : 1.0f - __uint_as_float(r0.w);
+        const float wy1 = lower ? __uint_as_float(r1.w) : 1.0f - __uint_as_float(r1.w);
+        const float w0 = __uint_as_float(r0.y) * (wy0 * wx0);
+        const float w1 = __uint_as_float(r1.y) * (wy1 * wx1);
+        const float* g0 = (const float*)(gp + r0.x);
+        const float* g1 = (const float*)(gp + r1.x);
+        float4 v0[CPL / 4], v1[CPL / 4];
+#pragma unroll
+        for (int c = 0; c < CPL / 4; ++c) {
+            v0[c] = *(const float4*)(g0 + 4 * c);
+            v1[c] = *(const float4*)(g1 + 4 * c);
+        }
+#pragma unroll
+        for (int c = 0; c < CPL / 4; ++c) {
+            acc[4 * c] = fmaf(w0, v0[c].x, acc[4 * c]);
+            acc[4 * c + 1] = fmaf(w0, v0[c].y, acc[4 * c + 1]);
+            acc[4 * c + 2] = fmaf(w0, v0[c].z, acc[4 * c + 2]);
+            acc[4 * c + 3] = fmaf(w0, v0[c].w, acc[4 * c + 3]);
+        }
+        if (two) {
+#pragma unroll
+            for (int c = 0; c < CPL / 4; ++c) {
+                acc[4 * c] = fmaf(w1, v1[c].x, acc[4 * c]);
+                acc[4 * c + 1] = fmaf(w1, v1[c].y, acc[4 * c + 1]);
+                acc[4 * c + 2] = fmaf(w1, v1[c].z, acc[4 * c + 2]);
+                acc[4 * c + 3] = fmaf(w1, v1[c].w, acc[4 * c + 3]);
+            }
+        }
+    }
+}
+
+// T: element type; KT: K, or 0 for a runtime K; CPL: channels per gather
+// lane (8 or 16, dividing Cg).  NT threads (a multiple of 64): every lane
+// takes at most one (pixel, channel part) item of the tile, at most
+// kBinSamples samples of a chunk and at most kBinPrefetch pieces of its
+// gradient rows.
+template <typename T, int KT, int CPL>
+__global__ __launch_bounds__(1024) void dcn_backward_input_binned(BwdArgs a, BinGeo bg)
 {
     constexpr int EB = Elem<T>::bytes;
-    extern __shared__ float owner_tile[];
+    extern __shared__ uint4 bin_lds[];
     const Geometry& G = a.geo;
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, NT = blockDim.x;
     uint32_t rest = xcd_remap(blockIdx.x, gridDim.x);
-    const uint32_t tx = rest % og.tiles_x;
-    rest /= og.tiles_x;
-    const uint32_t ty = rest % og.tiles_y;
-    rest /= og.tiles_y;
-    const uint32_t slab = rest % og.slabs;
-    const uint32_t n = rest / og.slabs;
-    const int qx0 = (int)tx * og.TW, qy0 = (int)ty * og.TH;
-    const int tw = og.TW < G.W - qx0 ? og.TW : G.W - qx0;     // ragged last column / row of tiles
-    const int th = og.TH < G.H - qy0 ? og.TH : G.H - qy0;
+    const uint32_t tx = rest % bg.tiles_x;
+    rest /= bg.tiles_x;
+    const uint32_t ty = rest % bg.tiles_y;
+    rest /= bg.tiles_y;
+    const uint32_t g = rest % (uint32_t)G.groups;
+    const uint32_t n = rest / (uint32_t)G.groups;
+    const int qx0 = (int)tx * bg.TW, qy0 = (int)ty * bg.TH;
+    const int tw = bg.TW < G.W - qx0 ? bg.TW : G.W - qx0;     // ragged last column / row of tiles
+    const int th = bg.TH < G.H - qy0 ? bg.TH : G.H - qy0;
+    const int nbx = tw + 1, nb = nbx * (th + 1);
+    const int RF = bin_row_floats(bg.Cg);
 
-    if (a.gi_init) {
-        // start from the binary32 partial sums already in the workspace (the
-        // corners beyond the owners' reach), 4 floats per lane and step
-        const float* src = a.gi_init + (size_t)n * G.H * G.W * G.C + slab * 32u;
-        for (int i = t; i < og.TH * og.TW * 8; i += NT) {
-            const int px = i >> 3, q4 = i & 7;
-            const int cy = px / og.TW, cx = px - cy * og.TW;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (cy < th && cx < tw)
-                v = *(const float4*)(src + ((size_t)(qy0 + cy) * G.W + (qx0 + cx)) * G.C + q4 * 4);
-            float* dst = owner_tile + px * kOwnerStride + q4 * 4;
-            *(float2*)dst = make_float2(v.x, v.y);
-            *(float2*)(dst + 2) = make_float2(v.z, v.w);
-        }
-    } else {
-        for (int i = t; i < og.TH * og.TW * kOwnerStride; i += NT) owner_tile[i] = 0.f;
-    }
-    __syncthreads();
+    uint32_t* cnt = (uint32_t*)bin_lds;
+    uint32_t* start = cnt + bg.nb_max;
+    uint32_t* wsum = start + bg.nb_max + 1;
+    uint4* rec_lds = bin_lds + bin_lds_words(bg) / 4;
+    float* gst = (float*)(rec_lds + bg.cap);
+    float2* smx = (float2*)(gst + bg.R * bg.ew_max * RF);
+
+    // this lane's gather item: tile pixel (cx, cy), channels [part*CPL, +CPL)
+    const int LP = bg.Cg / CPL;
+    const bool has_item = t < th * tw * LP;
+    const int ipx = t / LP, ipart = t - ipx * LP;
+    const int icy = ipx / tw, icx = ipx - icy * tw;
+    float acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
 
     int wlo, whi, hlo, hhi;
-    owner_range(G, og.M, qx0, tw, G.Wo, wlo, whi);
-    owner_range(G, og.M, qy0, th, G.Ho, hlo, hhi);
+    owner_range(G, bg.M, qx0, tw, G.Wo, wlo, whi);
+    owner_range(G, bg.M, qy0, th, G.Ho, hlo, hhi);
     const int EW = whi - wlo + 1;
-    const int E = (EW > 0 && hhi >= hlo) ? EW * (hhi - hlo + 1) : 0;
-
-    const int sub = t & 3;
-    const int ch0 = (int)slab * 32 + sub * 8;
-    const int g = ch0 / og.Cg;
+    // Chunks interleave the visited rows (chunk k takes rows hlo + k,
+    // hlo + k + nch, ...), so every chunk's samples spread over the whole tile
+    // and each lane gathers a share of its records in every chunk, rather
+    // than all of them in the one or two chunks whose rows lie over it.
+    const int EH = EW > 0 && hhi >= hlo ? hhi - hlo + 1 : 0;
+    const int nch = (EH + bg.R - 1) / bg.R;
     const int K = KT > 0 ? KT : G.K;
-    const uint32_t M2 = 2u * (uint32_t)og.M;
-    const RecordRsrc ro = record_rsrc((const char*)a.offset + (size_t)n * og.off_image_bytes, og.off_image_bytes);
-    const __amdgpu_buffer_rsrc_t roff = ro.r;
+    const int P = KT > 0 ? KT * KT : G.P;
+    const int centre = G.rc ? (K * K - 1) >> 1 : 1 << 30;     // the left-out tap, if any
+    // Quotients of non-negative integers v by EW, P and K as
+    // floor((v + 0.5) * (1/d)) in binary32: the true quotient is at least
+    // 0.5/d away from an integer and the two roundings move it by less than
+    // (v + 0.5)/d * 2^-23, which is smaller for v < 2^22 (here v < 2^13).
+    const float inv_ew = EW > 0 ? 1.0f / (float)EW : 0.f, inv_p = 1.0f / (float)P, inv_k = 1.0f / (float)K;
+    const uint32_t M2 = 2u * (uint32_t)bg.M;
+    const RecordRsrc ro = record_rsrc((const char*)a.offset + (size_t)n * bg.off_image_bytes, bg.off_image_bytes);
+    const RecordRsrc rm = record_rsrc((const char*)a.mask + (size_t)n * bg.mask_image_bytes, bg.mask_image_bytes);
     const bool odd = EB == 2 && (G.off_stride & 1);   // records on 2-byte boundaries
-    const RecordRsrc rm = record_rsrc((const char*)a.mask + (size_t)n * og.mask_image_bytes, og.mask_image_bytes);
-    const __amdgpu_buffer_rsrc_t rmk = rm.r;
-
-    // one sample point of output pixel (ho, wo): m*w*g of each near corner in the tile
-    auto point = [&](int i, int j, int bxi, int byi, float2 d, float m, const float* go) {
-        // the coordinates, skip rule and floor of make_sample
-        const float x = fmaf(G.alpha, d.x, fmaf(G.alpha, (float)(i * G.dil - G.c0), (float)bxi));
-        const float y = fmaf(G.alpha, d.y, fmaf(G.alpha, (float)(j * G.dil - G.c0), (float)byi));
-        if (!(x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H)) return;
-        const float fx = floorf(x), fy = floorf(y);
-        const int x0 = (int)fx, y0 = (int)fy;
-        const int rx = x0 - qx0, ry = y0 - qy0;
-        if (rx < -1 || rx >= tw || ry < -1 || ry >= th) return;   // no corner in the tile
-        const float lx = x - fx, ly = y - fy;
-        const float hy = 1.0f - ly, hx = 1.0f - lx;
-        const float wb[4] = {hy * hx, hy * lx, ly * hx, ly * lx};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int cx = rx + (k & 1), cy = ry + (k >> 1);
-            const int qx = x0 + (k & 1), qy = y0 + (k >> 1);
-            const bool mine = (uint32_t)cx < (uint32_t)tw && (uint32_t)cy < (uint32_t)th &&
-                              (uint32_t)(qx - bxi + og.M) <= M2 && (uint32_t)(qy - byi + og.M) <= M2;
-            if (mine) {
-                const float mw = m * wb[k];
-                // 24-bit multiply: a 64-bit multiply-add here reads a register
-                // pair whose upper half may be a load still in flight
-                const uint32_t base = (__umul24((uint32_t)cy, (uint32_t)og.TW) + (uint32_t)cx) * (uint32_t)kOwnerStride +
-                                      (uint32_t)sub * 8u;
-                float v[8];
-#pragma unroll
-                for (int c = 0; c < 8; ++c) v[c] = mw * go[c];
-                lds_add8((uint64_t*)(owner_tile + base), v);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    const char* gout_img = (const char*)a.grad_out + (size_t)n * G.Ho * G.Wo * G.C * EB + g * bg.Cg * EB;
+    const int pieces = bg.Cg * EB / 16;             // 16-byte pieces of a group's gradient row
+    auto mval = [&](uint32_t raw) { return EB == 4 ? __uint_as_float(raw) : Elem<T>::widen(raw); };
+    // (24-bit multiplies: the planner keeps Ho*Wo*G and the record and
+    // pixel strides below 2^24)
+    auto record_offset = [&](int kc, int e, uint32_t stride_bytes) {
+        const int r = (int)(((float)e + 0.5f) * inv_ew), c = e - __mul24(r, EW);
+        const uint32_t row = (uint32_t)(hlo + kc + __mul24(nch, r));
+        const uint32_t pg_img = __umul24(__umul24(row, (uint32_t)G.Wo) + (uint32_t)(wlo + c), (uint32_t)G.groups) + g;
+        return __umul24(pg_img, stride_bytes);
     };
 
-    // Each lane walks the visited output pixels in steps of NT/4, fetching a
-    // pixel's upstream gradient and whole records at once.  (Holding
-    // the next pixel's fetch in registers as well spills at this register
-    // budget and measured slower.)
-    struct Pending {
-        uint32_t gw[2 * EB];                  // the lane's 8 upstream-gradient elements
-        PointRecord<T, (KT > 0 ? KT * KT : 1)> rec;
-    };
-    auto fetch = [&](int ho, int wo, Pending& pd) {
-        const size_t pix = ((size_t)n * G.Ho + ho) * G.Wo + wo;
-        const uint4* gp = (const uint4*)((const char*)a.grad_out + (pix * G.C + ch0) * EB);
+    // The loads of a chunk: samples s = t + k*NT (output pixel e = s / P,
+    // point q = s mod P) and gradient pieces j = t + k*NT.  Every lane issues
+    // every load; those past the chunk get an out-of-range offset and read
+    // zeros, so no branch separates a load from the code that uses it.
+    const __amdgpu_buffer_rsrc_t rg = image_rsrc(gout_img - g * bg.Cg * EB, bg.gout_image_bytes);
+    const uint32_t gcol = g * (uint32_t)(bg.Cg * EB);
+    const float inv_pieces = 1.0f / (float)pieces;
+    uint32_t pd[kBinSamples][EB == 4 ? 2 : 1];
+    uint32_t pm[kBinSamples];
+    uint4 gpre[kBinPrefetch];
+    auto prefetch = [&](int kc) {
+        const int rows = kc < nch ? (EH - kc + nch - 1) / nch : 0;
+        const int CP = rows * EW, NS = CP * P;
 #pragma unroll
-        for (int h = 0; h < EB / 2; ++h) {
-            const uint4 v = gp[h];
-            pd.gw[4 * h] = v.x; pd.gw[4 * h + 1] = v.y; pd.gw[4 * h + 2] = v.z; pd.gw[4 * h + 3] = v.w;
-        }
-        if constexpr (KT > 0) {
-            const uint32_t pg_img = ((uint32_t)ho * (uint32_t)G.Wo + (uint32_t)wo) * (uint32_t)G.groups + (uint32_t)g;
-            load_record<T, KT * KT>(pd.rec, roff, pg_img * (uint32_t)(G.off_stride * EB) + ro.lead, rmk,
-                                    pg_img * (uint32_t)(G.mask_stride * EB) + rm.lead, odd);
-        }
-    };
-    auto mval = [&](uint32_t raw) {
-        return EB == 4 ? __uint_as_float(raw) : Elem<T>::widen(raw);
-    };
-
-    // Visit order: the rows of the visited window split into four phases
-    // (row mod 4); within a phase, column by column.  A wave's 16 pixel
-    // slots are consecutive in this order, so they share a column: the
-    // window's margin columns, whose samples rarely reach the tile, fill
-    // waves of their own that skip most corners together (mixing them into
-    // every wave cost 16% more time on the 56x56 fp32 stage).  The slots sit
-    // 4 rows apart, so two lanes of one LDS instruction rarely add into one
-    // address.
-    const int EH = E > 0 ? E / EW : 0;
-    int cum[5];
-    cum[0] = 0;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) cum[p + 1] = cum[p] + EW * ((EH - p + 3) >> 2);
-    const int e0 = t >> 2;
-    for (int e = e0; e < E; e += NT / 4) {
-        const int ph = (e >= cum[1]) + (e >= cum[2]) + (e >= cum[3]);   // cum[ph] <= e < cum[ph + 1]
-        const int cnt = (EH - ph + 3) >> 2, local = e - cum[ph];
-        const int col = local / cnt, k = local - col * cnt;
-        const int ho = hlo + ph + 4 * k, wo = wlo + col;
-        Pending cur;
-        fetch(ho, wo, cur);
-        const int bxi = wo * G.stride - G.pad + G.c0, byi = ho * G.stride - G.pad + G.c0;
-        float go[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            if constexpr (EB == 4) go[c] = __uint_as_float(cur.gw[c]);
-            else go[c] = Elem<T>::widen((c & 1) ? cur.gw[c >> 1] >> 16 : cur.gw[c >> 1] & 0xffffu);
-        }
-        if constexpr (KT > 0) {
-            constexpr int PK = KT * KT;
-            float mx = 0.f, inv = 1.f;
-            if (G.softmax) {
-                mx = mval(cur.rec.mask[0]);
-#pragma unroll
-                for (int q = 1; q < PK; ++q) mx = fmaxf(mx, mval(cur.rec.mask[q]));
-                float sum = 0.f;
-#pragma unroll
-                for (int q = 0; q < PK; ++q) sum += __expf(mval(cur.rec.mask[q]) - mx);
-                inv = 1.0f / sum;
-            }
-#pragma unroll
-            for (int i = 0; i < KT; ++i)
-#pragma unroll
-                for (int j = 0; j < KT; ++j) {
-                    const int q = i * KT + j;
-                    float m = mval(cur.rec.mask[q]);
-                    if (G.softmax) m = __expf(m - mx) * inv;
-                    point(i, j, bxi, byi, record_pair<T, PK>(cur.rec, q), m, go);
+        for (int k = 0; k < kBinSamples; ++k) {
+            int s = t + k * NT;
+            asm volatile("" : "+v"(s));     // decoded afresh each chunk (not held across the loop)
+            const bool ok = s < NS;
+            const int e = (int)(((float)s + 0.5f) * inv_p), q = s - __mul24(e, P);
+            const uint32_t vo = ok ? record_offset(kc, e, (uint32_t)(G.off_stride * EB)) + ro.lead : kOOB;
+            const uint32_t vm = ok ? record_offset(kc, e, (uint32_t)(G.mask_stride * EB)) + rm.lead : kOOB;
+            if constexpr (EB == 4) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(ro.r, vo + 8u * (uint32_t)q, 0, 0);
+                pd[k][0] = v[0];
+                pd[k][1] = v[1];
+                pm[k] = __builtin_amdgcn_raw_buffer_load_b32(rm.r, vm + 4u * (uint32_t)q, 0, 0);
+            } else {
+                if (odd) {
+                    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(ro.r, vo + 4u * (uint32_t)q, 0, 0);
+                    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(ro.r, vo + 4u * (uint32_t)q + 2u, 0, 0);
+                    pd[k][0] = lo | (hi << 16);
+                } else {
+                    pd[k][0] = __builtin_amdgcn_raw_buffer_load_b32(ro.r, vo + 4u * (uint32_t)q, 0, 0);
                 }
-        } else {
-            const size_t pg = (((size_t)n * G.Ho + ho) * G.Wo + wo) * G.groups + g;
-            const T* off = (const T*)a.offset + pg * G.off_stride;
-            const T* mk = (const T*)a.mask + pg * G.mask_stride;
-            float mx = 0.f, inv = 1.f;
-            if (G.softmax) {
-                mx = ld1(mk);
-                for (int q = 1; q < G.P; ++q) mx = fmaxf(mx, ld1(mk + q));
-                float sum = 0.f;
-                for (int q = 0; q < G.P; ++q) sum += __expf(ld1(mk + q) - mx);
-                inv = 1.0f / sum;
+                pm[k] = __builtin_amdgcn_raw_buffer_load_b16(rm.r, vm + 2u * (uint32_t)q, 0, 0);
             }
-            for (int i = 0; i < K; ++i)
-                for (int j = 0; j < K; ++j) {
-                    const int q = point_of(G, i, j);
-                    if (q < 0) continue;
-                    float m = ld1(mk + q);
-                    if (G.softmax) m = __expf(m - mx) * inv;
-                    point(i, j, bxi, byi, ld2(off + 2 * q), m, go);
-                }
         }
-    }
+#pragma unroll
+        for (int k = 0; k < kBinPrefetch; ++k) {
+            int j = t + k * NT;
+            asm volatile("" : "+v"(j));
+            const int e = (int)(((float)j + 0.5f) * inv_pieces), pc = j - __mul24(e, pieces);
+            const int r = (int)(((float)e + 0.5f) * inv_ew), c = e - __mul24(r, EW);
+            const uint32_t row = (uint32_t)(hlo + kc + __mul24(nch, r));
+            const uint32_t off = j < CP * pieces
+                                     ? __umul24(__umul24(row, (uint32_t)G.Wo) + (uint32_t)(wlo + c), (uint32_t)(G.C * EB)) +
+                                           gcol + (uint32_t)pc * 16u
+                                     : kOOB;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0);
+            gpre[k] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+    };
+
+    for (int b = t; b < nb; b += NT) cnt[b] = 0u;
+    prefetch(0);
     __syncthreads();
 
-    // write the tile, 4 channels per lane, rounded once to the dtype
-    char* gin = (char*)a.grad_input + (size_t)n * G.in_image_bytes + slab * (32u * EB);
-    for (int i = t; i < th * tw * 8; i += NT) {
-        const int px = i >> 3, q4 = i & 7;
-        const int cy = px / tw, cx = px - cy * tw;
-        const int qx = qx0 + cx, qy = qy0 + cy;
-        const float* src = owner_tile + (cy * og.TW + cx) * kOwnerStride + q4 * 4;
-        const float v[4] = {src[0], src[1], src[2], src[3]};
-        store<T, 4 * EB>(gin + (size_t)qy * G.in_line_bytes + (size_t)qx * G.in_row_bytes + q4 * (4 * EB), v);
+    for (int kc = 0; kc < nch; ++kc) {
+        const int rows = (EH - kc + nch - 1) / nch;
+        const int CP = rows * EW, NS = CP * P;
+
+        // the chunk's upstream-gradient rows of this group, in binary32
+#pragma unroll
+        for (int k = 0; k < kBinPrefetch; ++k) {
+            const int j = t + k * NT;
+            if (j < CP * pieces) {
+                const int e = (int)(((float)j + 0.5f) * inv_pieces), pc = j - e * pieces;
+                float* dst = gst + e * RF + pc * (16 / EB);
+                const uint4 v = gpre[k];
+                if constexpr (EB == 4) {
+                    *(uint4*)dst = v;
+                } else {
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                    float f[8];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        f[2 * q] = Elem<T>::widen(w[q] & 0xffffu);
+                        f[2 * q + 1] = Elem<T>::widen(w[q] >> 16);
+                    }
+                    *(float4*)dst = make_float4(f[0], f[1], f[2], f[3]);
+                    *(float4*)(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
+                }
+            }
+        }
+        if (G.softmax) {
+            // the softmax of each output pixel's mask row, once per chunk
+            for (int e = t; e < CP; e += NT) {
+                const uint32_t vm = record_offset(kc, e, (uint32_t)(G.mask_stride * EB)) + rm.lead;
+                float mx = load_mask_value<T>(rm.r, vm, 0);
+                for (int q = 1; q < P; ++q) mx = fmaxf(mx, load_mask_value<T>(rm.r, vm, q));
+                float sum = 0.f;
+                for (int q = 0; q < P; ++q) sum += __expf(load_mask_value<T>(rm.r, vm, q) - mx);
+                smx[e] = make_float2(mx, 1.0f / sum);
+            }
+            __syncthreads();
+        }
+
+        // Bin this lane's samples: an LDS atomic on the bin's count returns
+        // the sample's slot in its bin, and after the scan its record goes to
+        // the bin's start plus that slot.
+        // (The slots are first used after the scan, so the atomics' returns
+        // are waited for once, not one by one.)
+        uint32_t sbin[kBinSamples], sslot[kBinSamples];   // bin (~0: no record) and slot
+        float sw[kBinSamples][3];                         // m, lx, ly
+        const int base_off = G.c0 - G.pad;
+#pragma unroll
+        for (int k = 0; k < kBinSamples; ++k) {
+            int s = t + k * NT;
+            asm volatile("" : "+v"(s));
+            // every step computed for every lane, one predicate at the end
+            const int e = (int)(((float)s + 0.5f) * inv_p), q = s - __mul24(e, P);
+            const int r = (int)(((float)e + 0.5f) * inv_ew), c = e - __mul24(r, EW);
+            const int bxi = __mul24(wlo + c, G.stride) + base_off;
+            const int byi = __mul24(hlo + kc + __mul24(nch, r), G.stride) + base_off;
+            const int tap = q + (q >= centre ? 1 : 0);
+            // tap / 3 for tap < 9 is (tap * 11) >> 5
+            const int i = KT == 3 ? (tap * 11) >> 5 : (int)(((float)tap + 0.5f) * inv_k);
+            const int j = tap - __mul24(i, K);
+            float2 d;
+            if constexpr (EB == 4) d = make_float2(__uint_as_float(pd[k][0]), __uint_as_float(pd[k][1]));
+            else d = make_float2(Elem<T>::widen(pd[k][0] & 0xffffu), Elem<T>::widen(pd[k][0] >> 16));
+            float m = mval(pm[k]);
+            if (G.softmax) {
+                const float2 sm = smx[s < NS ? e : 0];
+                m = __expf(m - sm.x) * sm.y;
+            }
+            const float x = fmaf(G.alpha, d.x, fmaf(G.alpha, (float)(__mul24(i, G.dil) - G.c0), (float)bxi));
+            const float y = fmaf(G.alpha, d.y, fmaf(G.alpha, (float)(__mul24(j, G.dil) - G.c0), (float)byi));
+            // the skip rule of the definition (false for NaN)
+            const bool inmap = x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H;
+            const float fx = floorf(inmap ? x : -2.0f), fy = floorf(inmap ? y : -2.0f);
+            const int x0 = (int)fx, y0 = (int)fy;
+            // near: both corners of each axis within M of the base
+            const bool near = (uint32_t)(x0 - bxi + bg.M) < M2 && (uint32_t)(y0 - byi + bg.M) < M2;
+            const int bx = x0 - qx0 + 1, by = y0 - qy0 + 1;      // bin coordinates
+            const bool valid = s < NS && inmap && near && (uint32_t)bx <= (uint32_t)tw && (uint32_t)by <= (uint32_t)th;
+            const uint32_t bin = (uint32_t)(__mul24(by, nbx) + bx);
+            sbin[k] = valid ? bin : ~0u;
+            sslot[k] = 0u;
+            if (valid) sslot[k] = atomicAdd(cnt + bin, 1u);
+            sw[k][0] = m;
+            sw[k][1] = x - fx;
+            sw[k][2] = y - fy;
+        }
+        bin_scan(cnt, start, wsum, nb, t, NT);
+        // the counts are not read again in this chunk: clear them for the
+        // next one (past the barriers below)
+        for (int b = t; b < nb; b += NT) cnt[b] = 0u;
+        uint32_t pos[kBinSamples];
+#pragma unroll
+        for (int k = 0; k < kBinSamples; ++k) pos[k] = start[sbin[k] == ~0u ? 0u : sbin[k]] + sslot[k];
+#pragma unroll
+        for (int k = 0; k < kBinSamples; ++k) {
+            int s = t + k * NT;
+            asm volatile("" : "+v"(s));
+            const int e = (int)(((float)s + 0.5f) * inv_p);
+            if (sbin[k] != ~0u && pos[k] < (uint32_t)bg.cap)
+                rec_lds[pos[k]] = make_uint4((uint32_t)(e * RF * 4), __float_as_uint(sw[k][0]),
+                                             __float_as_uint(sw[k][1]), __float_as_uint(sw[k][2]));
+        }
+        __syncthreads();
+        prefetch(kc + 1);
+
+        // gather: the two runs of records of the item's 2x2 bins
+        if (has_item) {
+            const int bU = icy * nbx + icx, bL = bU + nbx;
+            const char* gp = (const char*)(gst + ipart * CPL);
+            // (every start is at most the chunk's record count, which is
+            // at most cap; the clamp keeps the reads inside the records
+            // whatever the counts)
+            const int cap = bg.cap;
+            auto st = [&](int b) { const int v = (int)start[b]; return v < cap ? v : cap; };
+            bin_run<CPL>(rec_lds, gp, st(bU), st(bU + 1), st(bU + 2), true, acc);
+            bin_run<CPL>(rec_lds, gp, st(bL), st(bL + 1), st(bL + 2), false, acc);
+        }
+        __syncthreads();
+    }
+
+    // write the tile, rounded once to the dtype
+    if (has_item) {
+        if (a.gi_init) {
+            // add the binary32 partial sums already in the workspace (the
+            // corners of samples that are not near)
+            const float4* src = (const float4*)(a.gi_init + (size_t)n * G.H * G.W * G.C +
+                                                ((size_t)(qy0 + icy) * G.W + (qx0 + icx)) * G.C + g * bg.Cg +
+                                                ipart * CPL);
+#pragma unroll
+            for (int c = 0; c < CPL / 4; ++c) {
+                const float4 v = src[c];
+                acc[4 * c] = v.x + acc[4 * c];
+                acc[4 * c + 1] = v.y + acc[4 * c + 1];
+                acc[4 * c + 2] = v.z + acc[4 * c + 2];
+                acc[4 * c + 3] = v.w + acc[4 * c + 3];
+            }
+        }
+        char* dst = (char*)a.grad_input + (size_t)n * G.in_image_bytes + g * (bg.Cg * EB) +
+                    (size_t)(qy0 + icy) * G.in_line_bytes + (size_t)(qx0 + icx) * G.in_row_bytes + ipart * (CPL * EB);
+#pragma unroll
+        for (int c = 0; c < CPL; c += 16 / EB) store<T, 16>(dst + c * EB, &acc[c]);
     }
 }
 
