@@ -1470,22 +1470,30 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
             for (int q = 0; q < PK; ++q) sum += __expf(mval(rec.mask[q]) - mx);
             inv = 1.0f / sum;
         }
-        float gms[PK];
+        // the softmax Jacobian needs every point's mask gradient first; a raw
+        // mask's gradient is stored as soon as it is known
+        float gms[SOFTMAX ? PK : 1];
         float dot = 0.f;
 #pragma unroll
         for (int q = 0; q < PK; ++q) {
             float m = mval(rec.mask[q]);
             if constexpr (SOFTMAX) m = __expf(m - mx) * inv;
-            gms[q] = point(q, record_pair<T, PK>(rec, q), m);
-            dot = fmaf(m, gms[q], dot);
+            const float gq = point(q, record_pair<T, PK>(rec, q), m);
+            if constexpr (SOFTMAX) {
+                gms[q] = gq;
+                dot = fmaf(m, gq, dot);
+            } else if (active && leader) {
+                store<T, EB>(gmk + q, &gq);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (active && leader) {
+        if constexpr (SOFTMAX) {
+            if (active && leader) {
 #pragma unroll
-            for (int q = 0; q < PK; ++q) {
-                float v = gms[q];
-                if constexpr (SOFTMAX) v = __expf(mval(rec.mask[q]) - mx) * inv * (v - dot);
-                store<T, EB>(gmk + q, &v);
+                for (int q = 0; q < PK; ++q) {
+                    const float v = __expf(mval(rec.mask[q]) - mx) * inv * (gms[q] - dot);
+                    store<T, EB>(gmk + q, &v);
+                }
             }
         }
     } else {
@@ -1585,8 +1593,8 @@ __host__ __device__ inline int bin_row_floats(int Cg) { return Cg + 4; }
 
 // LDS of one workgroup, in this order: bin counts and bin starts (nb_max + 1,
 // the last one the total), one total per wave for the scan, the records (16
-// bytes each), the staged upstream gradient, and the softmax maximum and
-// reciprocal sum of each output pixel of the chunk.
+// bytes each), the staged upstream gradient, a row of zeros, and the softmax
+// maximum and reciprocal sum of each output pixel of the chunk.
 __host__ __device__ inline uint32_t bin_lds_words(const BinGeo& b)
 {
     return ((uint32_t)(2 * b.nb_max + 1 + 16) + 3u) & ~3u;
@@ -1594,7 +1602,7 @@ __host__ __device__ inline uint32_t bin_lds_words(const BinGeo& b)
 __host__ __device__ inline uint32_t bin_lds_bytes(const BinGeo& b)
 {
     return bin_lds_words(b) * 4u + (uint32_t)b.cap * 16u +
-           (uint32_t)(b.R * b.ew_max * (bin_row_floats(b.Cg) + 2)) * 4u;
+           (uint32_t)((b.R * b.ew_max + 1) * bin_row_floats(b.Cg) + 2 * b.R * b.ew_max) * 4u;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele steps
@@ -1641,35 +1649,33 @@ __device__ __forceinline__ void bin_scan(const uint32_t* cnt, uint32_t* start, u
 // Adds the records [e0, e2) of a run of two bins into acc: the records of the
 // first bin [e0, e1) have this pixel as their right-hand corner (dx = 1), the
 // others as their left-hand one; lower: the pixel is the lower corner
-// (dy = 1) of all the run's records.  Two records per step, their gradient
-// rows read together; the next two records are read meanwhile.
+// (dy = 1) of all the run's records.  Two records per step, both gradient
+// rows read before either is used; a run of odd length ends on a step whose
+// second record has weight 0 and reads the zero row zr (a record's own row
+// could hold an Inf, and 0 * Inf is not 0).
 template <int CPL>
-__device__ __forceinline__ void bin_run(const uint4* rec_lds, const char* gp, int e0, int e1, int e2,
-                                        bool lower, float (&acc)[CPL])
+__device__ __forceinline__ void bin_run(const uint4* rec_lds, const char* gp, const float* zr, int e0, int e1,
+                                        int e2, bool lower, float (&acc)[CPL])
 {
-    if (e0 >= e2) return;
-    const int last = e2 - 1;
-    uint4 n0 = rec_lds[e0], n1 = rec_lds[e0 + 1 < last ? e0 + 1 : last];
 #pragma unroll 1
     for (int e = e0; e < e2; e += 2) {
-        const uint4 r0 = n0, r1 = n1;
         const bool two = e + 1 < e2;
-        n0 = rec_lds[e + 2 < last ? e + 2 : last];
-        n1 = rec_lds[e + 3 < last ? e + 3 : last];
-        const float wx0 = e < e1 ? __uint_as_float(r0.z) : 1.0f - __uint_as_float(r0.z);
-        const float wx1 = e + 1 < e1 ? __uint_as_float(r1.z) : 1.0f - __uint_as_float(r1.z);
-        const float wy0 = lower ? __uint_as_float(r0.w) : 1.0f - __uint_as_float(r0.w);
-        const float wy1 = lower ? __uint_as_float(r1.w) : 1.0f - __uint_as_float(r1.w);
-        const float w0 = __uint_as_float(r0.y) * (wy0 * wx0);
-        const float w1 = __uint_as_float(r1.y) * (wy1 * wx1);
+        const uint4 r0 = rec_lds[e];
+        const uint4 r1 = rec_lds[two ? e + 1 : e];
         const float* g0 = (const float*)(gp + r0.x);
-        const float* g1 = (const float*)(gp + r1.x);
+        const float* g1 = two ? (const float*)(gp + r1.x) : zr;
         float4 v0[CPL / 4], v1[CPL / 4];
 #pragma unroll
         for (int c = 0; c < CPL / 4; ++c) {
             v0[c] = *(const float4*)(g0 + 4 * c);
             v1[c] = *(const float4*)(g1 + 4 * c);
         }
+        const float wx0 = e < e1 ? __uint_as_float(r0.z) : 1.0f - __uint_as_float(r0.z);
+        const float wx1 = e + 1 < e1 ? __uint_as_float(r1.z) : 1.0f - __uint_as_float(r1.z);
+        const float wy0 = lower ? __uint_as_float(r0.w) : 1.0f - __uint_as_float(r0.w);
+        const float wy1 = lower ? __uint_as_float(r1.w) : 1.0f - __uint_as_float(r1.w);
+        const float w0 = __uint_as_float(r0.y) * (wy0 * wx0);
+        const float w1 = two ? __uint_as_float(r1.y) * (wy1 * wx1) : 0.f;
 #pragma unroll
         for (int c = 0; c < CPL / 4; ++c) {
             acc[4 * c] = fmaf(w0, v0[c].x, acc[4 * c]);
@@ -1677,14 +1683,12 @@ __device__ __forceinline__ void bin_run(const uint4* rec_lds, const char* gp, in
             acc[4 * c + 2] = fmaf(w0, v0[c].z, acc[4 * c + 2]);
             acc[4 * c + 3] = fmaf(w0, v0[c].w, acc[4 * c + 3]);
         }
-        if (two) {
 #pragma unroll
-            for (int c = 0; c < CPL / 4; ++c) {
-                acc[4 * c] = fmaf(w1, v1[c].x, acc[4 * c]);
-                acc[4 * c + 1] = fmaf(w1, v1[c].y, acc[4 * c + 1]);
-                acc[4 * c + 2] = fmaf(w1, v1[c].z, acc[4 * c + 2]);
-                acc[4 * c + 3] = fmaf(w1, v1[c].w, acc[4 * c + 3]);
-            }
+        for (int c = 0; c < CPL / 4; ++c) {
+            acc[4 * c] = fmaf(w1, v1[c].x, acc[4 * c]);
+            acc[4 * c + 1] = fmaf(w1, v1[c].y, acc[4 * c + 1]);
+            acc[4 * c + 2] = fmaf(w1, v1[c].z, acc[4 * c + 2]);
+            acc[4 * c + 3] = fmaf(w1, v1[c].w, acc[4 * c + 3]);
         }
     }
 }
@@ -1719,7 +1723,8 @@ __global__ __launch_bounds__(1024) void dcn_backward_input_binned(BwdArgs a, Bin
     uint32_t* wsum = start + bg.nb_max + 1;
     uint4* rec_lds = bin_lds + bin_lds_words(bg) / 4;
     float* gst = (float*)(rec_lds + bg.cap);
-    float2* smx = (float2*)(gst + bg.R * bg.ew_max * RF);
+    float* zrow = gst + bg.R * bg.ew_max * RF;
+    float2* smx = (float2*)(zrow + RF);
 
     // this lane's gather item: tile pixel (cx, cy), channels [part*CPL, +CPL)
     const int LP = bg.Cg / CPL;
@@ -1764,47 +1769,86 @@ __global__ __launch_bounds__(1024) void dcn_backward_input_binned(BwdArgs a, Bin
         return __umul24(pg_img, stride_bytes);
     };
 
-    // The loads of a chunk: samples s = t + k*NT (output pixel e = s / P,
-    // point q = s mod P) and gradient pieces j = t + k*NT.  Every lane issues
-    // every load; those past the chunk get an out-of-range offset and read
-    // zeros, so no branch separates a load from the code that uses it.
+    // A unit is NJ consecutive points of one output pixel: a row of the 3 x 3
+    // taps (i fixed, j = 0, 1, 2) in the K = 3 specialisation, which shares
+    // the pixel's decoding and loads its three offset pairs and mask values
+    // with wide loads; a single point otherwise.  Lanes take units
+    // u = t + k*NT, k < NUL (kBinSamples samples per lane either way).
+    constexpr int NJ = KT > 0 ? KT : 1;
+    constexpr int NUL = kBinSamples / NJ;
+    static_assert(NUL * NJ == kBinSamples, "units per lane");
+    const int UPP = P / NJ;                          // units per output pixel
+    const float inv_upp = 1.0f / (float)UPP;
+
+    // The loads of a chunk: units (their offset pairs and mask values) and
+    // gradient pieces j = t + k*NT.  Every lane issues every load; those past
+    // the chunk get an out-of-range offset and read zeros, so no branch
+    // separates a load from the code that uses it.
     const __amdgpu_buffer_rsrc_t rg = image_rsrc(gout_img - g * bg.Cg * EB, bg.gout_image_bytes);
     const uint32_t gcol = g * (uint32_t)(bg.Cg * EB);
     const float inv_pieces = 1.0f / (float)pieces;
-    uint32_t pd[kBinSamples][EB == 4 ? 2 : 1];
-    uint32_t pm[kBinSamples];
+    uint32_t pd[NUL][NJ][EB == 4 ? 2 : 1];
+    uint32_t pm[NUL][NJ];
     uint4 gpre[kBinPrefetch];
     auto prefetch = [&](int kc) {
         const int rows = kc < nch ? (EH - kc + nch - 1) / nch : 0;
-        const int CP = rows * EW, NS = CP * P;
+        const int NU = rows * EW * UPP;
 #pragma unroll
-        for (int k = 0; k < kBinSamples; ++k) {
-            int s = t + k * NT;
-            asm volatile("" : "+v"(s));     // decoded afresh each chunk (not held across the loop)
-            const bool ok = s < NS;
-            const int e = (int)(((float)s + 0.5f) * inv_p), q = s - __mul24(e, P);
+        for (int k = 0; k < NUL; ++k) {
+            int u = t + k * NT;
+            asm volatile("" : "+v"(u));     // decoded afresh each chunk (not held across the loop)
+            const bool ok = u < NU;
+            const int e = (int)(((float)u + 0.5f) * inv_upp), q0 = (u - __mul24(e, UPP)) * NJ;
             const uint32_t vo = ok ? record_offset(kc, e, (uint32_t)(G.off_stride * EB)) + ro.lead : kOOB;
             const uint32_t vm = ok ? record_offset(kc, e, (uint32_t)(G.mask_stride * EB)) + rm.lead : kOOB;
             if constexpr (EB == 4) {
-                const auto v = __builtin_amdgcn_raw_buffer_load_b64(ro.r, vo + 8u * (uint32_t)q, 0, 0);
-                pd[k][0] = v[0];
-                pd[k][1] = v[1];
-                pm[k] = __builtin_amdgcn_raw_buffer_load_b32(rm.r, vm + 4u * (uint32_t)q, 0, 0);
-            } else {
-                if (odd) {
-                    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(ro.r, vo + 4u * (uint32_t)q, 0, 0);
-                    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(ro.r, vo + 4u * (uint32_t)q + 2u, 0, 0);
-                    pd[k][0] = lo | (hi << 16);
+                if constexpr (NJ == 3) {
+                    const auto a4 = __builtin_amdgcn_raw_buffer_load_b128(ro.r, vo + 8u * (uint32_t)q0, 0, 0);
+                    const auto a2 = __builtin_amdgcn_raw_buffer_load_b64(ro.r, vo + 8u * (uint32_t)q0 + 16u, 0, 0);
+                    const auto m3 = __builtin_amdgcn_raw_buffer_load_b96(rm.r, vm + 4u * (uint32_t)q0, 0, 0);
+                    pd[k][0][0] = a4[0]; pd[k][0][1] = a4[1];
+                    pd[k][1][0] = a4[2]; pd[k][1][1] = a4[3];
+                    pd[k][2][0] = a2[0]; pd[k][2][1] = a2[1];
+                    pm[k][0] = m3[0]; pm[k][1] = m3[1]; pm[k][2] = m3[2];
                 } else {
-                    pd[k][0] = __builtin_amdgcn_raw_buffer_load_b32(ro.r, vo + 4u * (uint32_t)q, 0, 0);
+#pragma unroll
+                    for (int jj = 0; jj < NJ; ++jj) {
+                        const uint32_t qq = (uint32_t)(q0 + jj);
+                        const auto v = __builtin_amdgcn_raw_buffer_load_b64(ro.r, vo + 8u * qq, 0, 0);
+                        pd[k][jj][0] = v[0];
+                        pd[k][jj][1] = v[1];
+                        pm[k][jj] = __builtin_amdgcn_raw_buffer_load_b32(rm.r, vm + 4u * qq, 0, 0);
+                    }
                 }
-                pm[k] = __builtin_amdgcn_raw_buffer_load_b16(rm.r, vm + 2u * (uint32_t)q, 0, 0);
+            } else {
+                if (NJ == 3 && !odd) {
+                    // three offset pairs on a 4-byte boundary
+                    const auto a3 = __builtin_amdgcn_raw_buffer_load_b96(ro.r, vo + 4u * (uint32_t)q0, 0, 0);
+#pragma unroll
+                    for (int jj = 0; jj < NJ; ++jj) pd[k][jj][0] = a3[jj < 3 ? jj : 0];
+                } else {
+#pragma unroll
+                    for (int jj = 0; jj < NJ; ++jj) {
+                        const uint32_t o = vo + 4u * (uint32_t)(q0 + jj);
+                        if (odd) {
+                            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(ro.r, o, 0, 0);
+                            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(ro.r, o + 2u, 0, 0);
+                            pd[k][jj][0] = lo | (hi << 16);
+                        } else {
+                            pd[k][jj][0] = __builtin_amdgcn_raw_buffer_load_b32(ro.r, o, 0, 0);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int jj = 0; jj < NJ; ++jj)
+                    pm[k][jj] = __builtin_amdgcn_raw_buffer_load_b16(rm.r, vm + 2u * (uint32_t)(q0 + jj), 0, 0);
             }
         }
 #pragma unroll
         for (int k = 0; k < kBinPrefetch; ++k) {
             int j = t + k * NT;
             asm volatile("" : "+v"(j));
+            const int CP = rows * EW;
             const int e = (int)(((float)j + 0.5f) * inv_pieces), pc = j - __mul24(e, pieces);
             const int r = (int)(((float)e + 0.5f) * inv_ew), c = e - __mul24(r, EW);
             const uint32_t row = (uint32_t)(hlo + kc + __mul24(nch, r));
@@ -1818,12 +1862,13 @@ __global__ __launch_bounds__(1024) void dcn_backward_input_binned(BwdArgs a, Bin
     };
 
     for (int b = t; b < nb; b += NT) cnt[b] = 0u;
+    for (int c = t; c < RF; c += NT) zrow[c] = 0.f;
     prefetch(0);
     __syncthreads();
 
     for (int kc = 0; kc < nch; ++kc) {
         const int rows = (EH - kc + nch - 1) / nch;
-        const int CP = rows * EW, NS = CP * P;
+        const int CP = rows * EW;
 
         // the chunk's upstream-gradient rows of this group, in binary32
 #pragma unroll
@@ -1863,66 +1908,86 @@ __global__ __launch_bounds__(1024) void dcn_backward_input_binned(BwdArgs a, Bin
 
         // Bin this lane's samples: an LDS atomic on the bin's count returns
         // the sample's slot in its bin, and after the scan its record goes to
-        // the bin's start plus that slot.
-        // (The slots are first used after the scan, so the atomics' returns
-        // are waited for once, not one by one.)
-        uint32_t sbin[kBinSamples], sslot[kBinSamples];   // bin (~0: no record) and slot
-        float sw[kBinSamples][3];                         // m, lx, ly
+        // the bin's start plus that slot.  (The slots are first used after
+        // the scan, so the atomics' returns are waited for once, not one by
+        // one.)
+        const int NU = rows * EW * UPP;
+        uint32_t sbin[NUL][NJ], sslot[NUL][NJ];   // bin (~0: no record) and slot
+        float sw[NUL][NJ][3];                     // m, lx, ly
         const int base_off = G.c0 - G.pad;
 #pragma unroll
-        for (int k = 0; k < kBinSamples; ++k) {
-            int s = t + k * NT;
-            asm volatile("" : "+v"(s));
-            // every step computed for every lane, one predicate at the end
-            const int e = (int)(((float)s + 0.5f) * inv_p), q = s - __mul24(e, P);
+        for (int k = 0; k < NUL; ++k) {
+            int u = t + k * NT;
+            asm volatile("" : "+v"(u));
+            // every step computed for every lane, one predicate per sample
+            const int e = (int)(((float)u + 0.5f) * inv_upp), iu = u - __mul24(e, UPP);
             const int r = (int)(((float)e + 0.5f) * inv_ew), c = e - __mul24(r, EW);
             const int bxi = __mul24(wlo + c, G.stride) + base_off;
+            const float bxf = (float)bxi;
             const int byi = __mul24(hlo + kc + __mul24(nch, r), G.stride) + base_off;
-            const int tap = q + (q >= centre ? 1 : 0);
-            // tap / 3 for tap < 9 is (tap * 11) >> 5
-            const int i = KT == 3 ? (tap * 11) >> 5 : (int)(((float)tap + 0.5f) * inv_k);
-            const int j = tap - __mul24(i, K);
-            float2 d;
-            if constexpr (EB == 4) d = make_float2(__uint_as_float(pd[k][0]), __uint_as_float(pd[k][1]));
-            else d = make_float2(Elem<T>::widen(pd[k][0] & 0xffffu), Elem<T>::widen(pd[k][0] >> 16));
-            float m = mval(pm[k]);
+            const float byf = (float)byi;
+            float smx_m = 0.f, smx_inv = 1.f;
             if (G.softmax) {
-                const float2 sm = smx[s < NS ? e : 0];
-                m = __expf(m - sm.x) * sm.y;
+                const float2 sm = smx[u < NU ? e : 0];
+                smx_m = sm.x;
+                smx_inv = sm.y;
             }
-            const float x = fmaf(G.alpha, d.x, fmaf(G.alpha, (float)(__mul24(i, G.dil) - G.c0), (float)bxi));
-            const float y = fmaf(G.alpha, d.y, fmaf(G.alpha, (float)(__mul24(j, G.dil) - G.c0), (float)byi));
-            // the skip rule of the definition (false for NaN)
-            const bool inmap = x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H;
-            const float fx = floorf(inmap ? x : -2.0f), fy = floorf(inmap ? y : -2.0f);
-            const int x0 = (int)fx, y0 = (int)fy;
-            // near: both corners of each axis within M of the base
-            const bool near = (uint32_t)(x0 - bxi + bg.M) < M2 && (uint32_t)(y0 - byi + bg.M) < M2;
-            const int bx = x0 - qx0 + 1, by = y0 - qy0 + 1;      // bin coordinates
-            const bool valid = s < NS && inmap && near && (uint32_t)bx <= (uint32_t)tw && (uint32_t)by <= (uint32_t)th;
-            const uint32_t bin = (uint32_t)(__mul24(by, nbx) + bx);
-            sbin[k] = valid ? bin : ~0u;
-            sslot[k] = 0u;
-            if (valid) sslot[k] = atomicAdd(cnt + bin, 1u);
-            sw[k][0] = m;
-            sw[k][1] = x - fx;
-            sw[k][2] = y - fy;
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj) {
+                int i, j;
+                if constexpr (KT > 0) {
+                    i = iu;
+                    j = jj;
+                } else {
+                    const int tap = iu + (iu >= centre ? 1 : 0);
+                    i = (int)(((float)tap + 0.5f) * inv_k);
+                    j = tap - __mul24(i, K);
+                }
+                float2 d;
+                if constexpr (EB == 4) d = make_float2(__uint_as_float(pd[k][jj][0]), __uint_as_float(pd[k][jj][1]));
+                else d = make_float2(Elem<T>::widen(pd[k][jj][0] & 0xffffu), Elem<T>::widen(pd[k][jj][0] >> 16));
+                float m = mval(pm[k][jj]);
+                if (G.softmax) m = __expf(m - smx_m) * smx_inv;
+                const float x = fmaf(G.alpha, d.x, fmaf(G.alpha, (float)(__mul24(i, G.dil) - G.c0), bxf));
+                const float y = fmaf(G.alpha, d.y, fmaf(G.alpha, (float)(__mul24(j, G.dil) - G.c0), byf));
+                // the skip rule of the definition (false for NaN)
+                const bool inmap = x > -1.0f && x < (float)G.W && y > -1.0f && y < (float)G.H;
+                const float fx = floorf(inmap ? x : -2.0f), fy = floorf(inmap ? y : -2.0f);
+                const int x0 = (int)fx, y0 = (int)fy;
+                // near: both corners of each axis within M of the base
+                const bool near = (uint32_t)(x0 - bxi + bg.M) < M2 && (uint32_t)(y0 - byi + bg.M) < M2;
+                const int bx = x0 - qx0 + 1, by = y0 - qy0 + 1;      // bin coordinates
+                const bool valid =
+                    u < NU && inmap && near && (uint32_t)bx <= (uint32_t)tw && (uint32_t)by <= (uint32_t)th;
+                const uint32_t bin = (uint32_t)(__mul24(by, nbx) + bx);
+                sbin[k][jj] = valid ? bin : ~0u;
+                sslot[k][jj] = 0u;
+                if (valid) sslot[k][jj] = atomicAdd(cnt + bin, 1u);
+                sw[k][jj][0] = m;
+                sw[k][jj][1] = x - fx;
+                sw[k][jj][2] = y - fy;
+            }
         }
         bin_scan(cnt, start, wsum, nb, t, NT);
         // the counts are not read again in this chunk: clear them for the
         // next one (past the barriers below)
         for (int b = t; b < nb; b += NT) cnt[b] = 0u;
-        uint32_t pos[kBinSamples];
+        uint32_t pos[NUL][NJ];
 #pragma unroll
-        for (int k = 0; k < kBinSamples; ++k) pos[k] = start[sbin[k] == ~0u ? 0u : sbin[k]] + sslot[k];
+        for (int k = 0; k < NUL; ++k)
 #pragma unroll
-        for (int k = 0; k < kBinSamples; ++k) {
-            int s = t + k * NT;
-            asm volatile("" : "+v"(s));
-            const int e = (int)(((float)s + 0.5f) * inv_p);
-            if (sbin[k] != ~0u && pos[k] < (uint32_t)bg.cap)
-                rec_lds[pos[k]] = make_uint4((uint32_t)(e * RF * 4), __float_as_uint(sw[k][0]),
-                                             __float_as_uint(sw[k][1]), __float_as_uint(sw[k][2]));
+            for (int jj = 0; jj < NJ; ++jj)
+                pos[k][jj] = start[sbin[k][jj] == ~0u ? 0u : sbin[k][jj]] + sslot[k][jj];
+#pragma unroll
+        for (int k = 0; k < NUL; ++k) {
+            int u = t + k * NT;
+            asm volatile("" : "+v"(u));
+            const uint32_t goff = (uint32_t)((int)(((float)u + 0.5f) * inv_upp) * RF * 4);
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj)
+                if (sbin[k][jj] != ~0u && pos[k][jj] < (uint32_t)bg.cap)
+                    rec_lds[pos[k][jj]] = make_uint4(goff, __float_as_uint(sw[k][jj][0]), __float_as_uint(sw[k][jj][1]),
+                                                     __float_as_uint(sw[k][jj][2]));
         }
         __syncthreads();
         prefetch(kc + 1);
@@ -1936,8 +2001,9 @@ __global__ __launch_bounds__(1024) void dcn_backward_input_binned(BwdArgs a, Bin
             // whatever the counts)
             const int cap = bg.cap;
             auto st = [&](int b) { const int v = (int)start[b]; return v < cap ? v : cap; };
-            bin_run<CPL>(rec_lds, gp, st(bU), st(bU + 1), st(bU + 2), true, acc);
-            bin_run<CPL>(rec_lds, gp, st(bL), st(bL + 1), st(bL + 2), false, acc);
+            const float* zr = zrow + ipart * CPL;
+            bin_run<CPL>(rec_lds, gp, zr, st(bU), st(bU + 1), st(bU + 2), true, acc);
+            bin_run<CPL>(rec_lds, gp, zr, st(bL), st(bL + 1), st(bL + 2), false, acc);
         }
         __syncthreads();
     }
