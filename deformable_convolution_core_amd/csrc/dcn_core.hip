@@ -166,9 +166,10 @@ struct TilePlan {
 // waves per CU) plus region chunks staged.  min_waves and max_lds are the
 // caller's limits (the forward's are kMinFwdTileWaves and kMaxFwdTileLds);
 // zero_block reserves the forward's 2x2 block of zero pixels after a
-// partial region.
+// partial region; reach is how far (pixels, before offset_scale) offsets may
+// go and stay inside the staged region.
 bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan, int min_waves = 12,
-                int64_t max_lds = kMaxTileLds, bool zero_block = false)
+                int64_t max_lds = kMaxTileLds, bool zero_block = false, int reach = DCN_TILE_REACH)
 {
     const int eb = c.ebytes, rowg = c.Cg * eb, rowc = c.G * c.Cg * eb;
     if (!(rowg == 32 || rowg == 64 || rowg == 128) || rowc % 128 != 0) return false;
@@ -180,7 +181,7 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan, 
     const float a = c.alpha < 0 ? -c.alpha : c.alpha;
     const int c0 = c.dil * (c.K - 1) / 2;
     const int span = c0 > c.dil * (c.K - 1) - c0 ? c0 : c.dil * (c.K - 1) - c0;
-    const int ml = (int)ceilf(a * (float)span + a * (float)DCN_TILE_REACH);
+    const int ml = (int)ceilf(a * (float)span + a * (float)reach);
     const uint32_t slabs = (uint32_t)(rowc / 128);
     double best = -1.0;
     for (int nt = 256; nt <= 512; nt *= 2) {
@@ -365,7 +366,8 @@ bool plan_owner(const Call& c, const void* gout, const void* gin, OwnerPlan& pl)
             if (nt > 1024) continue;
             for (int R = 1; R <= eh; ++R) {
                 if (DCN_OWNER_FORCE_R && R != DCN_OWNER_FORCE_R) continue;
-                BinGeo bg{th, tw, M, c.Cg, R, (int)ew, (int)(R * ew * c.P), (th + 1) * (tw + 1), 0u, 0u, 0u, 0u, 0u};
+                BinGeo bg{th, tw, M, c.Cg, R, (int)ew, (int)(R * ew * c.P), (th + 1) * (tw + 1), 0u, 0u, 0u, 0u, 0u,
+                          c.ebytes};
                 // a lane holds at most kBinSamples samples of a chunk and
                 // kBinPrefetch 16-byte pieces of its gradient rows
                 if (R * ew * c.P > kBinSamples * nt || R * ew * (c.Cg * c.ebytes / 16) > kBinPrefetch * nt) break;
@@ -428,6 +430,15 @@ int launch_owner(const BwdArgs& a, const OwnerPlan& pl, hipStream_t st)
 #ifndef DCN_USE_GRAD_TILES
 #define DCN_USE_GRAD_TILES 1  // grad_offset / grad_mask from staged input tiles where the shape allows
 #endif
+#ifndef DCN_GRAD_TILE_REACH
+#define DCN_GRAD_TILE_REACH 3 // the gradient kernel's region reach (its samples beyond it read global memory)
+#endif
+
+bool plan_grad_tiles(const Call& c, const void* in, const void* gout, TilePlan& tp, int min_waves = 12,
+                     int64_t max_lds = kMaxTileLds)
+{
+    return plan_tiles(c, in, gout, tp, min_waves, max_lds, false, DCN_GRAD_TILE_REACH);
+}
 
 template <typename T, int KT, int NT>
 int launch_grad_tiled(const BwdArgs& a, const Call& c, const TilePlan& pl, hipStream_t st)
@@ -466,7 +477,7 @@ int backward_half(BwdArgs a, const Call& c, float* ws, hipStream_t st)
     TilePlan tp;
     // there is no untiled half-precision gradient kernel to fall back on, so
     // any tile that fits the LDS will do
-    if (!plan_owner(c, a.grad_out, a.grad_input, op) || !plan_tiles(c, a.input, a.grad_out, tp, 1, 160 * 1024))
+    if (!plan_owner(c, a.grad_out, a.grad_input, op) || !plan_grad_tiles(c, a.input, a.grad_out, tp, 1, 160 * 1024))
         return DCN_ERR_UNSUPPORTED;
     int rc = zero_fill(ws, (int64_t)c.N * c.H * c.W * c.G * c.Cg, st);
     if (rc != DCN_OK) return rc;
@@ -485,7 +496,7 @@ bool half_tiled_ok(const Call& c, const void* input, const void* gout, const voi
 {
     OwnerPlan op;
     TilePlan tp;
-    return plan_owner(c, gout, gin, op) && plan_tiles(c, input, gout, tp, 1, 160 * 1024);
+    return plan_owner(c, gout, gin, op) && plan_grad_tiles(c, input, gout, tp, 1, 160 * 1024);
 }
 
 // Half-precision backward on any shape whose group splits into a power of
@@ -708,7 +719,7 @@ int backward_call(const Call& c, const void* input, const void* offset_in, const
     }
     if (rc != DCN_OK) return rc;
     TilePlan tp;
-    if (DCN_USE_GRAD_TILES && plan_tiles(c, input, grad_output, tp)) return backward_grad_tiled<float>(a, c, tp, st);
+    if (DCN_USE_GRAD_TILES && plan_grad_tiles(c, input, grad_output, tp)) return backward_grad_tiled<float>(a, c, tp, st);
     return LB == 16 ? backward_lanes<16>(a, c, st, L) : backward_lanes<4>(a, c, st, L);
 }
 }  // namespace

@@ -1585,16 +1585,19 @@ struct BinGeo {
     uint32_t tiles_x, tiles_y;
     uint32_t off_image_bytes, mask_image_bytes;   // one image of offset / mask
     uint32_t gout_image_bytes;                    // one image of grad_output (< 2^31)
+    int eb;                                       // element bytes
 };
 
-// Floats per staged gradient row: Cg plus 4, so that rows start on 16
-// different 16-byte bank groups and random rows read together rarely collide.
-__host__ __device__ inline int bin_row_floats(int Cg) { return Cg + 4; }
+// Bytes per staged gradient row (the group's Cg elements in the call's
+// dtype) plus 16, so that rows start on different 16-byte bank groups and
+// random rows read together rarely collide.
+__host__ __device__ inline int bin_row_bytes(int Cg, int eb) { return Cg * eb + 16; }
 
 // LDS of one workgroup, in this order: bin counts and bin starts (nb_max + 1,
 // the last one the total), one total per wave for the scan, the records (16
-// bytes each), the staged upstream gradient, a row of zeros, and the softmax
-// maximum and reciprocal sum of each output pixel of the chunk.
+// bytes each), the staged upstream gradient (in the call's dtype), a row of
+// zeros, and the softmax maximum and reciprocal sum of each output pixel of
+// the chunk.
 __host__ __device__ inline uint32_t bin_lds_words(const BinGeo& b)
 {
     return ((uint32_t)(2 * b.nb_max + 1 + 16) + 3u) & ~3u;
@@ -1602,7 +1605,7 @@ __host__ __device__ inline uint32_t bin_lds_words(const BinGeo& b)
 __host__ __device__ inline uint32_t bin_lds_bytes(const BinGeo& b)
 {
     return bin_lds_words(b) * 4u + (uint32_t)b.cap * 16u +
-           (uint32_t)((b.R * b.ew_max + 1) * bin_row_floats(b.Cg) + 2 * b.R * b.ew_max) * 4u;
+           (uint32_t)((b.R * b.ew_max + 1) * bin_row_bytes(b.Cg, b.eb) + 8 * b.R * b.ew_max);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele steps
@@ -1646,6 +1649,30 @@ __device__ __forceinline__ void bin_scan(const uint32_t* cnt, uint32_t* start, u
     __syncthreads();
 }
 
+// CPL gradient elements of a staged row, widened to binary32 (exactly).
+template <typename T, int CPL>
+__device__ __forceinline__ void load_grad_row(const char* p, float (&v)[CPL])
+{
+    if constexpr (Elem<T>::bytes == 4) {
+#pragma unroll
+        for (int c = 0; c < CPL / 4; ++c) {
+            const float4 f = *(const float4*)(p + 16 * c);
+            v[4 * c] = f.x; v[4 * c + 1] = f.y; v[4 * c + 2] = f.z; v[4 * c + 3] = f.w;
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPL / 8; ++c) {
+            const uint4 h = *(const uint4*)(p + 16 * c);
+            const uint32_t w[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v[8 * c + 2 * q] = Elem<T>::widen(w[q] & 0xffffu);
+                v[8 * c + 2 * q + 1] = Elem<T>::widen(w[q] >> 16);
+            }
+        }
+    }
+}
+
 // Adds the records [e0, e2) of a run of two bins into acc: the records of the
 // first bin [e0, e1) have this pixel as their right-hand corner (dx = 1), the
 // others as their left-hand one; lower: the pixel is the lower corner
@@ -1653,8 +1680,8 @@ __device__ __forceinline__ void bin_scan(const uint32_t* cnt, uint32_t* start, u
 // rows read before either is used; a run of odd length ends on a step whose
 // second record has weight 0 and reads the zero row zr (a record's own row
 // could hold an Inf, and 0 * Inf is not 0).
-template <int CPL>
-__device__ __forceinline__ void bin_run(const uint4* rec_lds, const char* gp, const float* zr, int e0, int e1,
+template <typename T, int CPL>
+__device__ __forceinline__ void bin_run(const uint4* rec_lds, const char* gp, const char* zr, int e0, int e1,
                                         int e2, bool lower, float (&acc)[CPL])
 {
 #pragma unroll 1
@@ -1662,14 +1689,9 @@ __device__ __forceinline__ void bin_run(const uint4* rec_lds, const char* gp, co
         const bool two = e + 1 < e2;
         const uint4 r0 = rec_lds[e];
         const uint4 r1 = rec_lds[two ? e + 1 : e];
-        const float* g0 = (const float*)(gp + r0.x);
-        const float* g1 = two ? (const float*)(gp + r1.x) : zr;
-        float4 v0[CPL / 4], v1[CPL / 4];
-#pragma unroll
-        for (int c = 0; c < CPL / 4; ++c) {
-            v0[c] = *(const float4*)(g0 + 4 * c);
-            v1[c] = *(const float4*)(g1 + 4 * c);
-        }
+        float v0[CPL], v1[CPL];
+        load_grad_row<T, CPL>(gp + r0.x, v0);
+        load_grad_row<T, CPL>(two ? gp + r1.x : zr, v1);
         const float wx0 = e < e1 ? __uint_as_float(r0.z) : 1.0f - __uint_as_float(r0.z);
         const float wx1 = e + 1 < e1 ? __uint_as_float(r1.z) : 1.0f - __uint_as_float(r1.z);
         const float wy0 = lower ? __uint_as_float(r0.w) : 1.0f - __uint_as_float(r0.w);
@@ -1677,19 +1699,9 @@ __device__ __forceinline__ void bin_run(const uint4* rec_lds, const char* gp, co
         const float w0 = __uint_as_float(r0.y) * (wy0 * wx0);
         const float w1 = two ? __uint_as_float(r1.y) * (wy1 * wx1) : 0.f;
 #pragma unroll
-        for (int c = 0; c < CPL / 4; ++c) {
-            acc[4 * c] = fmaf(w0, v0[c].x, acc[4 * c]);
-            acc[4 * c + 1] = fmaf(w0, v0[c].y, acc[4 * c + 1]);
-            acc[4 * c + 2] = fmaf(w0, v0[c].z, acc[4 * c + 2]);
-            acc[4 * c + 3] = fmaf(w0, v0[c].w, acc[4 * c + 3]);
-        }
+        for (int c = 0; c < CPL; ++c) acc[c] = fmaf(w0, v0[c], acc[c]);
 #pragma unroll
-        for (int c = 0; c < CPL / 4; ++c) {
-            acc[4 * c] = fmaf(w1, v1[c].x, acc[4 * c]);
-            acc[4 * c + 1] = fmaf(w1, v1[c].y, acc[4 * c + 1]);
-            acc[4 * c + 2] = fmaf(w1, v1[c].z, acc[4 * c + 2]);
-            acc[4 * c + 3] = fmaf(w1, v1[c].w, acc[4 * c + 3]);
-        }
+        for (int c = 0; c < CPL; ++c) acc[c] = fmaf(w1, v1[c], acc[c]);
     }
 }
 
@@ -1716,15 +1728,15 @@ __global__ __launch_bounds__(1024) void dcn_backward_input_binned(BwdArgs a, Bin
     const int tw = bg.TW < G.W - qx0 ? bg.TW : G.W - qx0;     // ragged last column / row of tiles
     const int th = bg.TH < G.H - qy0 ? bg.TH : G.H - qy0;
     const int nbx = tw + 1, nb = nbx * (th + 1);
-    const int RF = bin_row_floats(bg.Cg);
+    const int RB = bin_row_bytes(bg.Cg, EB);
 
     uint32_t* cnt = (uint32_t*)bin_lds;
     uint32_t* start = cnt + bg.nb_max;
     uint32_t* wsum = start + bg.nb_max + 1;
     uint4* rec_lds = bin_lds + bin_lds_words(bg) / 4;
-    float* gst = (float*)(rec_lds + bg.cap);
-    float* zrow = gst + bg.R * bg.ew_max * RF;
-    float2* smx = (float2*)(zrow + RF);
+    char* gst = (char*)(rec_lds + bg.cap);
+    char* zrow = gst + bg.R * bg.ew_max * RB;
+    float2* smx = (float2*)(zrow + RB);
 
     // this lane's gather item: tile pixel (cx, cy), channels [part*CPL, +CPL)
     const int LP = bg.Cg / CPL;
@@ -1862,7 +1874,7 @@ __global__ __launch_bounds__(1024) void dcn_backward_input_binned(BwdArgs a, Bin
     };
 
     for (int b = t; b < nb; b += NT) cnt[b] = 0u;
-    for (int c = t; c < RF; c += NT) zrow[c] = 0.f;
+    for (int c = t; c < RB / 4; c += NT) ((uint32_t*)zrow)[c] = 0u;
     prefetch(0);
     __syncthreads();
 
@@ -1870,27 +1882,13 @@ __global__ __launch_bounds__(1024) void dcn_backward_input_binned(BwdArgs a, Bin
         const int rows = (EH - kc + nch - 1) / nch;
         const int CP = rows * EW;
 
-        // the chunk's upstream-gradient rows of this group, in binary32
+        // the chunk's upstream-gradient rows of this group, as they are
 #pragma unroll
         for (int k = 0; k < kBinPrefetch; ++k) {
             const int j = t + k * NT;
             if (j < CP * pieces) {
                 const int e = (int)(((float)j + 0.5f) * inv_pieces), pc = j - e * pieces;
-                float* dst = gst + e * RF + pc * (16 / EB);
-                const uint4 v = gpre[k];
-                if constexpr (EB == 4) {
-                    *(uint4*)dst = v;
-                } else {
-                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-                    float f[8];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        f[2 * q] = Elem<T>::widen(w[q] & 0xffffu);
-                        f[2 * q + 1] = Elem<T>::widen(w[q] >> 16);
-                    }
-                    *(float4*)dst = make_float4(f[0], f[1], f[2], f[3]);
-                    *(float4*)(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
-                }
+                *(uint4*)(gst + e * RB + pc * 16) = gpre[k];
             }
         }
         if (G.softmax) {
@@ -1982,7 +1980,7 @@ __global__ __launch_bounds__(1024) void dcn_backward_input_binned(BwdArgs a, Bin
         for (int k = 0; k < NUL; ++k) {
             int u = t + k * NT;
             asm volatile("" : "+v"(u));
-            const uint32_t goff = (uint32_t)((int)(((float)u + 0.5f) * inv_upp) * RF * 4);
+            const uint32_t goff = (uint32_t)((int)(((float)u + 0.5f) * inv_upp) * RB);
 #pragma unroll
             for (int jj = 0; jj < NJ; ++jj)
                 if (sbin[k][jj] != ~0u && pos[k][jj] < (uint32_t)bg.cap)
@@ -1995,15 +1993,15 @@ __global__ __launch_bounds__(1024) void dcn_backward_input_binned(BwdArgs a, Bin
         // gather: the two runs of records of the item's 2x2 bins
         if (has_item) {
             const int bU = icy * nbx + icx, bL = bU + nbx;
-            const char* gp = (const char*)(gst + ipart * CPL);
+            const char* gp = gst + ipart * CPL * EB;
             // (every start is at most the chunk's record count, which is
             // at most cap; the clamp keeps the reads inside the records
             // whatever the counts)
             const int cap = bg.cap;
             auto st = [&](int b) { const int v = (int)start[b]; return v < cap ? v : cap; };
-            const float* zr = zrow + ipart * CPL;
-            bin_run<CPL>(rec_lds, gp, zr, st(bU), st(bU + 1), st(bU + 2), true, acc);
-            bin_run<CPL>(rec_lds, gp, zr, st(bL), st(bL + 1), st(bL + 2), false, acc);
+            const char* zr = zrow + ipart * CPL * EB;
+            bin_run<T, CPL>(rec_lds, gp, zr, st(bU), st(bU + 1), st(bU + 2), true, acc);
+            bin_run<T, CPL>(rec_lds, gp, zr, st(bL), st(bL + 1), st(bL + 2), false, acc);
         }
         __syncthreads();
     }
