@@ -407,6 +407,54 @@ def cpu_baseline(w):
                             bound="|gpu - ref| <= 2e-2 |ref| + (n_terms + 32) 2^-24 S per element"))
 
 
+def parity_per_config(names):
+    """Part of the CPU leg: each forward workload (and the backward of the
+    56x56 DCNv4 shape in every dtype) runs through the HIP path on its whole
+    batch, in the launch configuration timed above, and image 0 of the result
+    is compared element by element with the oracle on image 0 (binary32
+    coordinates, the kernels' contract)."""
+    import oracle   # test infrastructure, used here only within the CPU leg
+    from tests import tolerance
+    res = {}
+
+    def comp(got, ref, S, n, dtype):
+        st = tolerance.compare(got, ref, S, n, dtype)
+        return dict(ok=st["ok"], max_ratio=round(st["max_ratio"], 4), norm_rel=st["norm_rel"], n_bad=st["n_bad"],
+                    n=st["n"])
+
+    for name in names:
+        w = inputs.WORKLOADS[name]
+        t = inputs.make(w, with_grad=False)
+        d = {k: v.to("cuda") for k, v in t.items()}
+        out = dcn.forward(d["input"], d["offset"], d["mask"], kernel_size=w.K, stride=w.stride, pad=w.pad,
+                          dilation=w.dilation, offset_scale=w.offset_scale, softmax=w.softmax, group=w.G)
+        torch.cuda.synchronize()
+        f64 = {k: inputs.to_f64(v[:1]) for k, v in t.items()}
+        ref, S = oracle.forward(f64["input"], f64["offset"], f64["mask"], K=w.K, stride=w.stride, pad=w.pad,
+                                dilation=w.dilation, offset_scale=w.offset_scale, softmax=w.softmax, group=w.G,
+                                coord_mode=oracle.COORD_BINARY32)
+        res[name] = comp(out[:1].float().cpu().numpy(), ref, S, 4 * w.P, w.dtype)
+    w5 = inputs.WORKLOADS["c5_dcnv4_f32_56_fwdbwd"]
+    for dt in ("f32", "f16", "bf16"):
+        w = w5 if dt == "f32" else inputs.scaled(w5, dtype=dt)
+        t = inputs.make(w, with_grad=True)
+        d = {k: v.to("cuda") for k, v in t.items()}
+        gi, goff, gm = dcn.backward(d["input"], d["offset"], d["mask"], d["grad_out"], kernel_size=w.K,
+                                    stride=w.stride, pad=w.pad, dilation=w.dilation, offset_scale=w.offset_scale,
+                                    softmax=w.softmax, group=w.G)
+        torch.cuda.synchronize()
+        f64 = {k: inputs.to_f64(v[:1]) for k, v in t.items()}
+        r = oracle.backward(f64["input"], f64["offset"], f64["mask"], f64["grad_out"], K=w.K, stride=w.stride,
+                            pad=w.pad, dilation=w.dilation, offset_scale=w.offset_scale, softmax=w.softmax,
+                            group=w.G, coord_mode=oracle.COORD_BINARY32)
+        res[f"{w5.name}@{dt} backward"] = {
+            key: comp(got[:1].float().cpu().numpy().reshape(r[key].shape), r[key], S, n, dt)
+            for key, got, S, n in (("grad_input", gi, r["gi_abs"], r["gi_cnt"]),
+                                   ("grad_offset", goff, r["goff_abs"], 4 * w.Cg),
+                                   ("grad_mask", gm, r["gmask_abs"], 4 * w.Cg))}
+    return res
+
+
 def _counters(name):
     """The committed rocprofv3 counter record of a workload, if it was taken
     on the current kernel sources."""
@@ -537,6 +585,8 @@ def main():
     ap.add_argument("--backward", action="store_true", help="with --profile: launch the backward")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="with --profile: also run plain device copies of this many MB (counter calibration)")
+    ap.add_argument("--dtype", choices=("f32", "f16", "bf16"), default=None,
+                    help="with --profile: run the workload's shape in this dtype")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -550,8 +600,9 @@ def main():
     torch.cuda.set_device(0)
 
     w = inputs.WORKLOADS[args.workload]
+    w5 = inputs.WORKLOADS["c5_dcnv4_f32_56_fwdbwd"]
     if args.profile:
-        profile_mode(w, args)
+        profile_mode(w if args.dtype is None else inputs.scaled(w, dtype=args.dtype), args)
         return
     log(f"headline {w.name}: steps={args.steps} warmup={args.warmup}")
     head = forward_record(w, args.steps, args.warmup)
@@ -588,7 +639,6 @@ def main():
             log(f"{name} packed: {r['us']} us, {r['GBps']} GB/s")
             packed.append(r)
         extra["packed_forward"] = packed
-        w5 = inputs.WORKLOADS["c5_dcnv4_f32_56_fwdbwd"]
         bwd = []
         for dt in ("f32", "f16", "bf16"):
             wb = w5 if dt == "f32" else inputs.scaled(w5, dtype=dt)
@@ -619,6 +669,15 @@ def main():
     if not args.quick and not args.no_cpu_baseline:
         cpu = cpu_baseline(w)
         log(f"cpu oracle {cpu['value']} GB/s on {cpu['cores']} threads; headline parity {cpu.get('parity')}")
+        names = [r["workload"] for r in extra["bf16_sweep"] + extra["other_forward"]]
+        par = parity_per_config(names)
+        for r in extra["bf16_sweep"] + extra["other_forward"]:
+            r["parity"] = par.get(r["workload"])
+        for r in [extra["backward"]] + extra["backward_half"]:
+            r["parity"] = par.get(f"{w5.name}@{r['dtype']} backward")
+        bad = [k for k, v in par.items() if not all(x["ok"] for x in (v.values() if "ok" not in v else [v]))]
+        log(f"per-config parity (image 0 vs the oracle): {len(par) - len(bad)} of {len(par)} within bound"
+            + (f"; outside: {bad}" if bad else ""))
 
     agg = extra.get("bf16_sweep_aggregate")
     line = {
