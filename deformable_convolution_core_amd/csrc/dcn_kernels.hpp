@@ -892,10 +892,10 @@ __device__ __forceinline__ TileCoord tile_coord(const Geometry& G, const TileGeo
 // 16*l).  Off-image pixels get an out-of-range offset and are written as
 // zeros, which is the zero padding of the definition.  Rows above and below
 // the image (a range every lane shares) use that offset outright; on image
-// rows a lane steps its offset by one image row.
-template <int NT>
+// rows a lane steps its offset by one image row.  NT: the block's lanes, a
+// multiple of 64.
 __device__ __forceinline__ void stage_rows(const Geometry& G, const TileGeo& tg, const void* input,
-                                           const TileCoord& c, uint4* buf, int r0, int r1, int t)
+                                           const TileCoord& c, uint4* buf, int r0, int r1, int t, int NT)
 {
     const int RW8 = tg.RW * 8;
     const __amdgpu_buffer_rsrc_t rin =
@@ -945,7 +945,7 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
     const int t = threadIdx.x;
 
     const TileCoord cur = tile_coord(G, tg, xcd_remap(blockIdx.x, gridDim.x));
-    stage_rows<NT>(G, tg, a.input, cur, region, 0, tg.RH, t);
+    stage_rows(G, tg, a.input, cur, region, 0, tg.RH, t, (int)blockDim.x);
     if constexpr (!WHOLE) {
         // the 2x2 block of zero pixels after the region (rows RH and RH + 1,
         // columns 0 and 1 at the region's row stride): 32 lanes, 16 bytes each
@@ -1313,7 +1313,7 @@ void dcn_backward_grad_tiled(BwdArgs a, TileGeo tg)
     const Geometry& G = a.geo;
     const int t = threadIdx.x;
     const TileCoord cur = tile_coord(G, tg, xcd_remap(blockIdx.x, gridDim.x));
-    stage_rows<NT>(G, tg, a.input, cur, region, 0, tg.RH, t);
+    stage_rows(G, tg, a.input, cur, region, 0, tg.RH, t, (int)blockDim.x);
 
     const int p = t >> 2, sub = t & 3;
     const int py = p / tg.TW, px = p - py * tg.TW;
