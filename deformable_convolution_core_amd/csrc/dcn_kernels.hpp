@@ -867,13 +867,17 @@ struct TileCoord {
 __device__ __forceinline__ TileCoord tile_coord(const Geometry& G, const TileGeo& tg, uint32_t tile)
 {
     TileCoord c;
+    // the slab varies fastest: the slabs of one tile run as neighbouring
+    // tiles of one XCD, so the cache lines of a pixel's offset and mask
+    // records that two slabs' groups share meet in that XCD's L2 (read once,
+    // and written back once by the gradient kernel)
     uint32_t rest = tile;
+    c.slab = rest % tg.slabs;
+    rest /= tg.slabs;
     const uint32_t tx = rest % tg.tiles_x;
     rest /= tg.tiles_x;
     const uint32_t ty = rest % tg.tiles_y;
-    rest /= tg.tiles_y;
-    c.slab = rest % tg.slabs;
-    c.n = rest / tg.slabs;
+    c.n = rest / tg.tiles_y;
     c.ho0 = (int)ty * tg.TH;
     c.wo0 = (int)tx * tg.TW;
     // A region cut down to the map and a one-pixel border starts no earlier
