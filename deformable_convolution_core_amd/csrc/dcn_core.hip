@@ -143,6 +143,7 @@ int forward_variant(const FwdArgs& base, const Call& c, hipStream_t st)
 #define DCN_TILE_FORCE_TH 0
 #endif
 constexpr int64_t kMaxTileLds = 96 * 1024;
+constexpr int kMaxTilePixels = 128;   // 512 lanes
 // The forward planner may take a region of all of LDS with as few as 4
 // resident waves per CU: measured on a stride-2 stage (bf16, 128x128 input,
 // 512 channels), a 154 KB region with one block of 512 lanes per CU beats
@@ -163,18 +164,16 @@ struct TilePlan {
 // multiple of 128, 16-byte aligned input and output.  Among tile shapes with
 // at most 128 pixels it picks the cheapest by a simple cost model: lane slots
 // issued (idle lanes of ragged tiles count, weighted up below 16 resident
-// waves per CU) plus region chunks staged.  min_waves and max_lds are the
-// caller's limits (the forward's are kMinFwdTileWaves and kMaxFwdTileLds);
-// zero_block reserves the forward's 2x2 block of zero pixels after a
-// partial region; reach is how far (pixels, before offset_scale) offsets may
-// go and stay inside the staged region.  exact_lanes (the forward): a block
-// has as many lanes as its tile needs, rounded up to whole waves, so tiles
-// shorter than 128 (64) pixels are candidates too and no wave of a block
-// runs without a pixel; otherwise every block has 512 (256) lanes and a tile
-// is as tall as that allows.
+// waves per CU) plus region chunks staged; on equal cost the wider tile (a
+// wave's pixels then span fewer tile rows; measured 1-3% faster at 56x56,
+// 8x14 against 14x8).  A block has the lanes its tile needs (4 per pixel),
+// rounded up to whole waves, so no wave runs without a pixel.  min_waves and
+// max_lds are the caller's limits (the forward's are kMinFwdTileWaves and
+// kMaxFwdTileLds); zero_block reserves the forward's 2x2 block of zero pixels
+// after a partial region; reach is how far (pixels, before offset_scale)
+// offsets may go and stay inside the staged region.
 bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan, int min_waves = 12,
-                int64_t max_lds = kMaxTileLds, bool zero_block = false, int reach = DCN_TILE_REACH,
-                bool exact_lanes = false)
+                int64_t max_lds = kMaxTileLds, bool zero_block = false, int reach = DCN_TILE_REACH)
 {
     const int eb = c.ebytes, rowg = c.Cg * eb, rowc = c.G * c.Cg * eb;
     if (!(rowg == 32 || rowg == 64 || rowg == 128) || rowc % 128 != 0) return false;
@@ -189,12 +188,8 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan, 
     const int ml = (int)ceilf(a * (float)span + a * (float)reach);
     const uint32_t slabs = (uint32_t)(rowc / 128);
     double best = -1.0;
-    for (int nt = 256; nt <= 512; nt *= 2) {
-        const int maxpx = nt / 4;
-        for (int tw = 1; tw <= 32 && tw <= c.Wo; ++tw)
-        for (int th = exact_lanes ? 1 : maxpx / tw; th <= maxpx / tw; ++th) {
-            if (th > c.Ho || th < 1) continue;
-            if (exact_lanes && nt == 512 && th * tw <= 64) continue;   // the 256-lane pass has it
+    for (int tw = 1; tw <= 32 && tw <= c.Wo; ++tw) {
+        for (int th = 1; th <= kMaxTilePixels / tw && th <= c.Ho; ++th) {
             if (DCN_TILE_FORCE_TW && (tw != DCN_TILE_FORCE_TW || th != DCN_TILE_FORCE_TH)) continue;
             // A region never needs more than the map and a one-pixel border
             // (tile_coord starts it no earlier than -1).  When that is all of
@@ -213,20 +208,17 @@ bool plan_tiles(const Call& c, const void* in, const void* out, TilePlan& plan, 
             const uint64_t tx = (uint64_t)((c.Wo + tw - 1) / tw), ty = (uint64_t)((c.Ho + th - 1) / th);
             const uint64_t tiles = tx * ty * slabs * (uint64_t)c.N;
             const int lanes = ((th * tw * 4 + 63) / 64) * 64;
-            const int threads = exact_lanes ? lanes : nt;
             // LDS per block bounds the blocks a CU holds; below 16 resident
             // waves per CU the latency of the corner reads shows
-            const int per_cu = (int)(160 * 1024 / lds) < 2048 / threads ? (int)(160 * 1024 / lds) : 2048 / threads;
-            const int waves = per_cu * threads / 64;
+            const int per_cu = (int)(160 * 1024 / lds) < 2048 / lanes ? (int)(160 * 1024 / lds) : 2048 / lanes;
+            const int waves = per_cu * lanes / 64;
             if (waves < min_waves) continue;   // too few resident waves for this caller's kernel
             const double occ_penalty = waves >= 16 ? 1.0 : 16.0 / (double)waves;
             const double cost = (double)tiles * ((double)lanes * 900.0 * occ_penalty + (double)rh * rw * 8 * 3.0);
-            // equal costs: the wider tile (a wave's pixels then span fewer
-            // tile rows; measured 1-3% faster at 56x56, 8x14 against 14x8)
-            if (best < 0 || cost < best || (exact_lanes && cost == best && tw > plan.tg.TW)) {
+            if (best < 0 || cost < best || (cost == best && tw > plan.tg.TW)) {
                 best = cost;
                 plan.tg = TileGeo{th, tw, rh, rw, ml, 0, whole ? 1 : 0, (uint32_t)tx, (uint32_t)ty, slabs};
-                plan.threads = threads;
+                plan.threads = lanes;
                 plan.lds_bytes = (uint32_t)lds;
                 plan.blocks = tiles;
             }
@@ -289,7 +281,7 @@ template <typename T>
 int forward_typed(const FwdArgs& a, const Call& c, hipStream_t st)
 {
     TilePlan pl;
-    if (DCN_USE_TILES && plan_tiles(c, a.input, a.output, pl, kMinFwdTileWaves, kMaxFwdTileLds, true, DCN_TILE_REACH, true))
+    if (DCN_USE_TILES && plan_tiles(c, a.input, a.output, pl, kMinFwdTileWaves, kMaxFwdTileLds, true))
         return forward_tiled<T>(a, c, pl, st);
     if (a.gate) return DCN_ERR_UNSUPPORTED;   // the gate is fused into the tiled kernel only
     const int row = c.Cg * (int)sizeof(T);
@@ -446,7 +438,7 @@ int launch_owner(const BwdArgs& a, const OwnerPlan& pl, hipStream_t st)
 bool plan_grad_tiles(const Call& c, const void* in, const void* gout, TilePlan& tp, int min_waves = 12,
                      int64_t max_lds = kMaxTileLds)
 {
-    return plan_tiles(c, in, gout, tp, min_waves, max_lds, false, DCN_GRAD_TILE_REACH, true);
+    return plan_tiles(c, in, gout, tp, min_waves, max_lds, false, DCN_GRAD_TILE_REACH);
 }
 
 template <typename T, int KT, int NT>
