@@ -368,7 +368,7 @@ bool plan_owner(const Call& c, const void* gout, const void* gin, OwnerPlan& pl)
             for (int R = 1; R <= eh; ++R) {
                 if (DCN_OWNER_FORCE_R && R != DCN_OWNER_FORCE_R) continue;
                 BinGeo bg{th, tw, M, c.Cg, R, (int)ew, (int)(R * ew * c.P), (th + 1) * (tw + 1), 0u, 0u, 0u, 0u, 0u,
-                          c.ebytes};
+                          c.dtype == DCN_F16 ? 2 : 4};   // staged gradient rows: fp16, else binary32
                 // a lane holds at most kBinSamples samples of a chunk and
                 // kBinPrefetch 16-byte pieces of its gradient rows
                 if (R * ew * c.P > kBinSamples * nt || R * ew * (c.Cg * c.ebytes / 16) > kBinPrefetch * nt) break;
