@@ -953,6 +953,11 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
     const Geometry& G = a.geo;
     const int t = threadIdx.x;
 
+    // The staging and record loads are issued at a raised wave priority, so
+    // that a workgroup arriving on a CU gets its memory requests out ahead of
+    // the point loop of the workgroup already there; the priority drops back
+    // before the wait.  (Measured: 2-5% off the large-shape launches.)
+    __builtin_amdgcn_s_setprio(1);
     const TileCoord cur = tile_coord(G, tg, xcd_remap(blockIdx.x, gridDim.x));
     stage_rows(G, tg, a.input, cur, region, 0, tg.RH, t, (int)blockDim.x);
     if constexpr (!WHOLE) {
@@ -1031,6 +1036,7 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
         constexpr int PK = KT * KT;
         PointRecord<T, PK> rec;
         load_record<T, PK>(rec, roff, voff, rmk, vmk, odd);
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_s_waitcnt(0);   // the region (and the record) have landed
         __syncthreads();
         // the modulation: raw, or the softmax over the PK points (each
@@ -1065,6 +1071,7 @@ void dcn_forward_tiled(FwdArgs a, TileGeo tg)
             point_fence<CPL>(acc);
         }
     } else {
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_s_waitcnt(0);   // the region has landed
         __syncthreads();
         float mx = 0.f, inv = 1.f;
